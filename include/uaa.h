@@ -1,0 +1,209 @@
+/*
+ * uaa.h -- C ABI of libuaa.so: one rank's share of context-parallel
+ * attention (Ulysses, Ulysses Anything, Ring, Unified) on one AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Pages whose statement of the problem these calls follow:
+ *   [CP]  "Context parallelism" (diffusers documentation), sections
+ *         "Ring Attention", "Ulysses Attention", "Unified Attention",
+ *         "Ulysses Anything Attention", "Ring Anything Attention".
+ *   [USP] "Add Unified Sequence Parallel attention" (diffusers pull request
+ *         #12693), review thread: each Ring step's attention returns
+ *         (out, lse); the running pair is merged in fp32 and cast back to the
+ *         query dtype once; the LSE travels as (B, S, H_LOCAL).
+ *   [UAA] "UAA: Ulysses Anything Attention" (diffusers issue #12706): any
+ *         sequence length, no padding, only per-rank seq_len is exchanged;
+ *         forced host/device syncs are what costs time.
+ *   [YC]  USP / yunchang project summary (sourcepulse), "How It Works",
+ *         "Highlighted Details": zigzag / stripe / basic ring layouts.
+ *
+ * Conventions shared by every call
+ *   - Tensors are dense, row-major, BSHD: [batch, sequence, heads, feature].
+ *     "bf16" is IEEE bfloat16 storage; all arithmetic inside is fp32.
+ *   - Pointers named "device" are HIP device pointers; host arrays (offsets,
+ *     the arrays of device pointers, the mask descriptor) are read during the
+ *     call only and never retained.
+ *   - The caller owns every buffer.  No call allocates or frees memory.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = the
+ *     null stream) and the call returns without waiting for it.  No call
+ *     synchronises the device or copies device data to the host ([UAA]: such
+ *     forced syncs are the cost to avoid).
+ *   - Every argument is validated on the host before anything is enqueued.
+ *     A failing check returns a negative status and leaves the stream
+ *     untouched; uaa_last_error() then describes it.
+ *   - Calls on different streams may run concurrently if their outputs do
+ *     not overlap each other or any input.
+ */
+#ifndef UAA_H
+#define UAA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define UAA_OK 0
+#define UAA_ERR_INVALID_ARG (-1) /* malformed arguments (null, negative, inconsistent) */
+#define UAA_ERR_UNSUPPORTED (-2) /* well-formed but outside what the kernels handle */
+#define UAA_ERR_HIP (-3)         /* the HIP runtime reported an error on launch */
+
+/* Element types. */
+#define UAA_BF16 0
+#define UAA_FP32 1
+
+/* Permute directions. */
+#define UAA_SEQ2HEAD 0
+#define UAA_HEAD2SEQ 1
+
+/* Largest Ulysses degree a permute accepts, largest N a merge accepts. */
+#define UAA_MAX_WORLD 64
+#define USP_MAX_PARTS 16
+
+/* Mask kinds ([YC] ring layouts; "basic" contiguous shards are CAUSAL). */
+#define USP_MASK_FULL 0
+#define USP_MASK_CAUSAL 1
+#define USP_MASK_ZIGZAG 2
+#define USP_MASK_STRIPE 3
+
+/*
+ * Global token positions of the query rows and key columns of one attention
+ * call.  Under every kind but FULL, key j is allowed for query i iff
+ * kpos(j) <= qpos(i) (causal by global position).
+ *   CAUSAL: qpos(i) = q_off + i,  kpos(j) = k_off + j   (contiguous shards)
+ *   ZIGZAG: the sequence is cut into chunks of `chunk` tokens; the query rows
+ *           are chunk q_chunks[0] followed by chunk q_chunks[1] (or only
+ *           q_chunks[0] when q_chunks[1] < 0), so
+ *           qpos(i) = q_chunks[i / chunk] * chunk + i % chunk; keys likewise
+ *           with k_chunks.  Rank r of an R-rank zigzag ring holds chunks r
+ *           and 2R-1-r.
+ *   STRIPE: qpos(i) = q_rank + world * i,  kpos(j) = k_rank + world * j.
+ * Unused fields are ignored.
+ */
+typedef struct usp_mask {
+    int32_t kind;
+    int32_t world;
+    int64_t q_off;
+    int64_t k_off;
+    int64_t chunk;
+    int32_t q_chunks[2];
+    int32_t k_chunks[2];
+    int32_t q_rank;
+    int32_t k_rank;
+} usp_mask;
+
+/*
+ * uaa_seq2head_permute -- the local data movement of the Ulysses all-to-all
+ * for one rank, run as a gather ([CP] "Ulysses Attention": the first
+ * exchange leaves every GPU all tokens of a subset of heads, the second
+ * regroups by token; [CP] "Ulysses Anything Attention" / [UAA]: the token
+ * and head counts per rank are arbitrary and nothing is padded).
+ *
+ * seq_off[0..world]  host, exclusive prefix sums of the per-rank token
+ *                    counts: rank p holds tokens [seq_off[p], seq_off[p+1]).
+ *                    Must start at 0 and never decrease (empty ranks allowed).
+ * head_off[0..world] host, the same for heads; must start at 0, strictly
+ *                    increase and end at H (so world <= H).  NULL = split H
+ *                    with the first H mod world ranks taking one extra head.
+ * S = seq_off[world], S_p = seq_off[p+1]-seq_off[p], H_r likewise.
+ *
+ * dir = UAA_SEQ2HEAD, `rank` = the head rank r being assembled:
+ *   src[p] (p < world): device [B, S_p, H, D]   (rank p's token shard)
+ *   dst:                device [B, S, H_r, D]
+ *   dst[b, s, h, d] = src[p][b, s - seq_off[p], head_off[r] + h, d]
+ *   with p the rank whose token range contains s.
+ * dir = UAA_HEAD2SEQ, `rank` = the token rank p being assembled:
+ *   src[r] (r < world): device [B, S, H_r, D]   (rank r's head shard)
+ *   dst:                device [B, S_p, H, D]
+ *   dst[b, t, h, d] = src[r][b, seq_off[p] + t, h - head_off[r], d]
+ *   with r the rank whose head range contains h.
+ * The LSE of the Unified path ([USP], (B, S, H_LOCAL)) moves with D = 1,
+ * elem_bytes = 4.
+ *
+ * elem_bytes: 1, 2, 4 or 8; elements are copied as opaque bit patterns
+ * (bit-exact).  Every pointer must be aligned to elem_bytes; the widest
+ * access that alignment and the row sizes allow is chosen internally.
+ * src and dst must not overlap.  B, H, D >= 1 (B = 0 or S = 0: no work).
+ * Returns UAA_OK, UAA_ERR_INVALID_ARG, or UAA_ERR_HIP.
+ */
+int uaa_seq2head_permute(int dir, int rank, int world,
+                         const int64_t* seq_off, const int64_t* head_off,
+                         int64_t B, int64_t H, int64_t D, int elem_bytes,
+                         const void* const* src, void* dst, void* stream);
+
+/*
+ * usp_attn_fwd_lse -- softmax attention of one rank's query rows against
+ * one block of keys/values, returning both the output and the per-row
+ * log-sum-exp: the (out, lse) pair each Ring step produces ([USP]; [CP]
+ * "Ring Attention": each GPU computes attention against the K/V block it
+ * holds; "Ring Anything Attention": blocks of any length).
+ *
+ *   q  device [B, Sq, H, D]  dtype
+ *   k  device [B, Sk, H, D]  dtype
+ *   v  device [B, Sk, H, D]  dtype
+ *   o  device [B, Sq, H, D]  o_dtype (bf16 rounded to nearest even)
+ *   lse device [B, Sq, H]    fp32, natural log
+ * For every (b, i, h), with J the allowed keys of row i (all j < Sk under
+ * USP_MASK_FULL or mask == NULL; kpos(j) <= qpos(i) otherwise):
+ *   s_j = scale * <q_i, k_j>,  lse = log(sum_{j in J} exp(s_j)),
+ *   o   = sum_{j in J} exp(s_j - lse) * v_j,
+ * and o = 0, lse = -inf when J is empty (a row with no allowed key, or
+ * Sk = 0), so that such a partial drops out of usp_lse_merge.
+ *
+ * dtype: UAA_BF16 (bf16 matrix-core products, fp32 accumulation and
+ * softmax) or UAA_FP32 (fp32 throughout).  o_dtype: UAA_BF16 or UAA_FP32 for
+ * bf16 input, UAA_FP32 for fp32 input.  D: 64 or 128 (else
+ * UAA_ERR_UNSUPPORTED).  scale: finite, > 0.  q, k, v, o: 16-byte aligned;
+ * lse: 4-byte aligned.  Outputs must not overlap inputs.  Sq = 0, B = 0 or
+ * H = 0: no work.
+ * Returns UAA_OK, UAA_ERR_INVALID_ARG, UAA_ERR_UNSUPPORTED or UAA_ERR_HIP.
+ */
+int usp_attn_fwd_lse(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                     const void* q, const void* k, const void* v,
+                     void* o, int o_dtype, float* lse,
+                     float scale, const usp_mask* mask, void* stream);
+
+/*
+ * usp_lse_merge -- merge N partial (O, LSE) pairs of the same query rows,
+ * each over a disjoint set of keys, into the pair over their union ([USP]:
+ * the Ring loop's fp32 update of the running (out, lse), cast to the output
+ * dtype once at the end).  Per row, computed in fp32:
+ *   M   = max_n lse_n
+ *   lse = M + log(sum_n exp(lse_n - M))
+ *   o   = sum_n exp(lse_n - lse) * o_n
+ * and (o, lse) = (0, -inf) when every lse_n is -inf.  On finite inputs this
+ * is the pages' pairwise sigmoid / log-sigmoid update folded over n; the
+ * max-shifted form also accepts -inf partials, which the pairwise form
+ * turns into NaN.
+ *
+ *   o_parts   host array of n_parts device pointers, each [B, S, H, D]
+ *             part_dtype
+ *   lse_parts host array of n_parts device pointers, each [B, S, H] fp32
+ *   o_out     device [B, S, H, D] out_dtype (bf16 rounded to nearest even)
+ *   lse_out   device [B, S, H] fp32
+ * n_parts in [1, USP_MAX_PARTS].  D >= 1.  Pointers aligned to their
+ * element size.  lse_out may equal lse_parts[n], and o_out may equal
+ * o_parts[n] when part_dtype == out_dtype (in-place accumulation); no other
+ * overlap.  B, S or H = 0: no work.
+ * Returns UAA_OK, UAA_ERR_INVALID_ARG or UAA_ERR_HIP.
+ */
+int usp_lse_merge(int n_parts, int64_t B, int64_t S, int64_t H, int64_t D,
+                  const void* const* o_parts, int part_dtype, const float* const* lse_parts,
+                  void* o_out, int out_dtype, float* lse_out, void* stream);
+
+/*
+ * uaa_last_error -- text describing the last non-zero status returned on
+ * the calling thread ("" if none).  The pointer stays valid until the next
+ * call on that thread.
+ */
+const char* uaa_last_error(void);
+
+/* uaa_abi_version -- version of this header's contract (currently 1). */
+int uaa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UAA_H */

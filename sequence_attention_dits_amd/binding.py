@@ -1,0 +1,243 @@
+"""Python binding of libuaa.so: the three calls of include/uaa.h under the
+same names, taking torch tensors.
+
+Argument marshalling only: shapes, dtypes and device placement are checked
+so that the raw pointers handed to the library always cover what the call
+will touch, then the C entry point is called with ``data_ptr()`` values and
+the current HIP stream.  Every step of the computation runs in the HIP
+kernels; there is no fallback of any kind, and a missing library is an
+error.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libuaa.so")
+
+UAA_OK = 0
+UAA_ERR_INVALID_ARG = -1
+UAA_ERR_UNSUPPORTED = -2
+UAA_ERR_HIP = -3
+UAA_BF16 = 0
+UAA_FP32 = 1
+UAA_SEQ2HEAD = 0
+UAA_HEAD2SEQ = 1
+UAA_MAX_WORLD = 64
+USP_MAX_PARTS = 16
+USP_MASK_FULL = 0
+USP_MASK_CAUSAL = 1
+USP_MASK_ZIGZAG = 2
+USP_MASK_STRIPE = 3
+
+_c_i64 = ctypes.c_int64
+_c_p = ctypes.c_void_p
+
+
+class usp_mask(ctypes.Structure):
+    """Mirror of ``usp_mask`` in include/uaa.h."""
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("world", ctypes.c_int32),
+        ("q_off", ctypes.c_int64),
+        ("k_off", ctypes.c_int64),
+        ("chunk", ctypes.c_int64),
+        ("q_chunks", ctypes.c_int32 * 2),
+        ("k_chunks", ctypes.c_int32 * 2),
+        ("q_rank", ctypes.c_int32),
+        ("k_rank", ctypes.c_int32),
+    ]
+
+
+def mask_full() -> usp_mask:
+    return usp_mask(kind=USP_MASK_FULL)
+
+
+def mask_causal(q_off: int = 0, k_off: int = 0) -> usp_mask:
+    """Contiguous ("basic") shards: qpos = q_off + i, kpos = k_off + j."""
+    return usp_mask(kind=USP_MASK_CAUSAL, q_off=q_off, k_off=k_off)
+
+
+def mask_zigzag(chunk: int, q_chunks: Sequence[int], k_chunks: Sequence[int]) -> usp_mask:
+    """Rows are the listed global chunks (one or two) of length `chunk`."""
+    qc = list(q_chunks) + [-1] * (2 - len(q_chunks))
+    kc = list(k_chunks) + [-1] * (2 - len(k_chunks))
+    m = usp_mask(kind=USP_MASK_ZIGZAG, chunk=chunk)
+    m.q_chunks[0], m.q_chunks[1] = qc[0], qc[1]
+    m.k_chunks[0], m.k_chunks[1] = kc[0], kc[1]
+    return m
+
+
+def mask_stripe(world: int, q_rank: int, k_rank: int) -> usp_mask:
+    """qpos = q_rank + world * i, kpos = k_rank + world * j."""
+    return usp_mask(kind=USP_MASK_STRIPE, world=world, q_rank=q_rank, k_rank=k_rank)
+
+
+class UaaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("libuaa status %d: %s" % (status, message))
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libuaa.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libuaa.so is not built (%s); run "
+                               "`python -m sequence_attention_dits_amd.build`" % LIB_PATH)
+        l = ctypes.CDLL(LIB_PATH)
+        l.uaa_seq2head_permute.restype = ctypes.c_int
+        l.uaa_seq2head_permute.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_p, _c_p,
+                                           _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_p, _c_p, _c_p]
+        l.usp_attn_fwd_lse.restype = ctypes.c_int
+        l.usp_attn_fwd_lse.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                       _c_p, _c_p, _c_p, _c_p, ctypes.c_int, _c_p,
+                                       ctypes.c_float, ctypes.POINTER(usp_mask), _c_p]
+        l.usp_lse_merge.restype = ctypes.c_int
+        l.usp_lse_merge.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_int,
+                                    _c_p, _c_p, ctypes.c_int, _c_p, _c_p]
+        l.uaa_last_error.restype = ctypes.c_char_p
+        l.uaa_last_error.argtypes = []
+        l.uaa_abi_version.restype = ctypes.c_int
+        l.uaa_abi_version.argtypes = []
+        _lib = l
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != UAA_OK:
+        raise UaaError(status, lib().uaa_last_error().decode(errors="replace"))
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError("%s must be a CUDA (HIP) tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _code(dt: torch.dtype, name: str) -> int:
+    if dt == torch.bfloat16:
+        return UAA_BF16
+    if dt == torch.float32:
+        return UAA_FP32
+    raise ValueError("%s must be bfloat16 or float32, got %s" % (name, dt))
+
+
+def _i64_array(vals):
+    return (ctypes.c_int64 * len(vals))(*[int(x) for x in vals])
+
+
+def uaa_seq2head_permute(direction: int, rank: int, src: Sequence[torch.Tensor], dst: torch.Tensor,
+                         seq_off: Sequence[int], head_off: Optional[Sequence[int]] = None) -> None:
+    """Ulysses layout change for one rank (include/uaa.h).
+
+    SEQ2HEAD: src[p] [B,S_p,H,D] -> dst [B,S,H_r,D] for head rank `rank`.
+    HEAD2SEQ: src[r] [B,S,H_r,D] -> dst [B,S_p,H,D] for token rank `rank`.
+    Any element dtype; bits are copied unchanged.
+    """
+    world = len(src)
+    if len(seq_off) != world + 1:
+        raise ValueError("seq_off needs world+1 entries")
+    _dev(dst, "dst")
+    for x in src:
+        _dev(x, "src")
+        if x.dtype != dst.dtype or x.device != dst.device:
+            raise ValueError("src and dst must share dtype and device")
+    if dst.dim() != 4:
+        raise ValueError("tensors are [B, S, H, D]")
+    B, D = dst.shape[0], dst.shape[3]
+    S = int(seq_off[-1])
+    if direction == UAA_SEQ2HEAD:
+        H = src[0].shape[2]
+    elif direction == UAA_HEAD2SEQ:
+        H = dst.shape[2]
+    else:
+        raise ValueError("direction must be UAA_SEQ2HEAD or UAA_HEAD2SEQ")
+    if head_off is None:
+        base, extra = divmod(H, world)
+        hoff = [0]
+        for p in range(world):
+            hoff.append(hoff[-1] + base + (1 if p < extra else 0))
+    else:
+        hoff = [int(x) for x in head_off]
+    if len(hoff) != world + 1:
+        raise ValueError("head_off needs world+1 entries")
+    if direction == UAA_SEQ2HEAD:
+        for p, x in enumerate(src):
+            if tuple(x.shape) != (B, seq_off[p + 1] - seq_off[p], H, D):
+                raise ValueError("src[%d] shape %s does not match the offsets" % (p, tuple(x.shape)))
+        if tuple(dst.shape) != (B, S, hoff[rank + 1] - hoff[rank], D):
+            raise ValueError("dst shape %s does not match the offsets" % (tuple(dst.shape),))
+    else:
+        for r, x in enumerate(src):
+            if tuple(x.shape) != (B, S, hoff[r + 1] - hoff[r], D):
+                raise ValueError("src[%d] shape %s does not match the offsets" % (r, tuple(x.shape)))
+        if tuple(dst.shape) != (B, seq_off[rank + 1] - seq_off[rank], H, D):
+            raise ValueError("dst shape %s does not match the offsets" % (tuple(dst.shape),))
+    ptrs = (ctypes.c_void_p * world)(*[x.data_ptr() if x.numel() else 0 for x in src])
+    _check(lib().uaa_seq2head_permute(direction, rank, world, _i64_array(seq_off),
+                                      _i64_array(hoff), B, H, D, dst.element_size(), ptrs,
+                                      dst.data_ptr() if dst.numel() else 0, _stream(dst)))
+
+
+def usp_attn_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                     lse: torch.Tensor, scale: float, mask: Optional[usp_mask] = None) -> None:
+    """Attention forward with LSE into caller-owned o [B,Sq,H,D], lse [B,Sq,H] fp32."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse")):
+        _dev(t, n)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q, k, v are [B, S, H, D] and k, v share a shape")
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
+        raise ValueError("k/v shape %s does not match q %s" % (tuple(k.shape), tuple(q.shape)))
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    if tuple(o.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Sq, H) or lse.dtype != torch.float32:
+        raise ValueError("o must be shaped like q and lse [B, Sq, H] float32")
+    dt, odt = _code(q.dtype, "q"), _code(o.dtype, "o")
+    m = mask if mask is not None else mask_full()
+    _check(lib().usp_attn_fwd_lse(dt, B, H, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  o.data_ptr(), odt, lse.data_ptr(), float(scale), ctypes.byref(m),
+                                  _stream(q)))
+
+
+def usp_lse_merge(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor],
+                  o_out: torch.Tensor, lse_out: torch.Tensor) -> None:
+    """N-way LSE merge of partial (O, LSE) pairs into o_out, lse_out."""
+    n = len(o_parts)
+    if n != len(lse_parts) or n < 1:
+        raise ValueError("need matching, non-empty part lists")
+    _dev(o_out, "o_out")
+    _dev(lse_out, "lse_out")
+    if o_out.dim() != 4:
+        raise ValueError("o tensors are [B, S, H, D]")
+    B, S, H, D = o_out.shape
+    pdt = _code(o_parts[0].dtype, "o_parts")
+    for o, l in zip(o_parts, lse_parts):
+        _dev(o, "o_parts")
+        _dev(l, "lse_parts")
+        if tuple(o.shape) != (B, S, H, D) or o.dtype != o_parts[0].dtype:
+            raise ValueError("every o part must be [B, S, H, D] of one dtype")
+        if tuple(l.shape) != (B, S, H) or l.dtype != torch.float32:
+            raise ValueError("every lse part must be [B, S, H] float32")
+    if tuple(lse_out.shape) != (B, S, H) or lse_out.dtype != torch.float32:
+        raise ValueError("lse_out must be [B, S, H] float32")
+    optr = (ctypes.c_void_p * n)(*[o.data_ptr() for o in o_parts])
+    lptr = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lse_parts])
+    _check(lib().usp_lse_merge(n, B, S, H, D, optr, pdt, lptr, o_out.data_ptr(),
+                               _code(o_out.dtype, "o_out"), lse_out.data_ptr(), _stream(o_out)))

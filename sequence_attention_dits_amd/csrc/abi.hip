@@ -1,0 +1,277 @@
+// abi.hip -- the extern "C" entry points of libuaa.so: host-side validation
+// of every argument, conversion of the caller's description into kernel
+// arguments, and one asynchronous launch on the caller's stream.  Nothing
+// here synchronises the device or reads device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "internal.h"
+
+#define UAA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_status(hipError_t e, const char* what)
+{
+    if (e == hipSuccess) return UAA_OK;
+    return fail(UAA_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+constexpr int64_t kMaxElems = int64_t(1) << 46;   // far above any HBM, keeps products in int64
+constexpr int64_t kMaxIdx32 = int64_t(1) << 31;
+
+// Default head split: the first H mod world ranks take one extra head.
+void even_split(int64_t total, int parts, int64_t* off)
+{
+    const int64_t base = total / parts, extra = total % parts;
+    off[0] = 0;
+    for (int p = 0; p < parts; ++p) off[p + 1] = off[p] + base + (p < extra ? 1 : 0);
+}
+
+}  // namespace
+
+UAA_EXPORT const char* uaa_last_error(void) { return g_err; }
+
+UAA_EXPORT int uaa_abi_version(void) { return 1; }
+
+UAA_EXPORT int uaa_seq2head_permute(int dir, int rank, int world, const int64_t* seq_off,
+                                    const int64_t* head_off, int64_t B, int64_t H, int64_t D,
+                                    int elem_bytes, const void* const* src, void* dst, void* stream)
+{
+    if (dir != UAA_SEQ2HEAD && dir != UAA_HEAD2SEQ)
+        return fail(UAA_ERR_INVALID_ARG, "permute: dir must be UAA_SEQ2HEAD or UAA_HEAD2SEQ, got %d", dir);
+    if (world < 1 || world > UAA_MAX_WORLD)
+        return fail(UAA_ERR_INVALID_ARG, "permute: world must be in [1, %d], got %d", UAA_MAX_WORLD, world);
+    if (rank < 0 || rank >= world)
+        return fail(UAA_ERR_INVALID_ARG, "permute: rank %d outside [0, %d)", rank, world);
+    if (B < 0 || H < 1 || D < 1)
+        return fail(UAA_ERR_INVALID_ARG, "permute: need B >= 0, H >= 1, D >= 1 (got %lld, %lld, %lld)",
+                    (long long)B, (long long)H, (long long)D);
+    if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+        return fail(UAA_ERR_INVALID_ARG, "permute: elem_bytes must be 1, 2, 4 or 8, got %d", elem_bytes);
+    if (seq_off == nullptr) return fail(UAA_ERR_INVALID_ARG, "permute: seq_off is NULL");
+    if (seq_off[0] != 0) return fail(UAA_ERR_INVALID_ARG, "permute: seq_off[0] must be 0");
+    for (int p = 0; p < world; ++p)
+        if (seq_off[p + 1] < seq_off[p])
+            return fail(UAA_ERR_INVALID_ARG, "permute: seq_off decreases at rank %d", p);
+    int64_t hoff[UAA_MAX_WORLD + 1];
+    if (head_off == nullptr) {
+        even_split(H, world, hoff);
+    } else {
+        for (int p = 0; p <= world; ++p) hoff[p] = head_off[p];
+    }
+    if (hoff[0] != 0 || hoff[world] != H)
+        return fail(UAA_ERR_INVALID_ARG, "permute: head_off must run from 0 to H = %lld", (long long)H);
+    for (int p = 0; p < world; ++p)
+        if (hoff[p + 1] <= hoff[p])
+            return fail(UAA_ERR_INVALID_ARG,
+                        "permute: rank %d gets no heads (head_off must strictly increase; world <= H)", p);
+    const int64_t S = seq_off[world];
+    if (S > kMaxIdx32 || B * S >= kMaxIdx32 || (double)B * S * H * D * elem_bytes > (double)kMaxElems)
+        return fail(UAA_ERR_INVALID_ARG, "permute: tensor too large");
+    if (src == nullptr) return fail(UAA_ERR_INVALID_ARG, "permute: src array is NULL");
+
+    const int64_t Hr = hoff[rank + 1] - hoff[rank];
+    const int64_t Sp = seq_off[rank + 1] - seq_off[rank];
+    const int64_t out_tokens = dir == UAA_SEQ2HEAD ? S : Sp;
+    const int64_t n_rows = B * out_tokens;
+
+    if (n_rows == 0) return UAA_OK;
+
+    // Sources that hold data must be present; every pointer must be aligned.
+    const int64_t slice = D * elem_bytes;       // bytes of one head of one token
+    int vec = 16;
+    while (vec > 1 && slice % vec != 0) vec >>= 1;
+    for (int p = 0; p < world; ++p) {
+        // SEQ2HEAD reads every non-empty token shard; HEAD2SEQ every head shard
+        if (dir == UAA_SEQ2HEAD && seq_off[p + 1] == seq_off[p]) continue;
+        if (src[p] == nullptr) return fail(UAA_ERR_INVALID_ARG, "permute: src[%d] is NULL", p);
+        if (!aligned(src[p], elem_bytes))
+            return fail(UAA_ERR_INVALID_ARG, "permute: src[%d] not aligned to %d bytes", p, elem_bytes);
+        while (vec > elem_bytes && !aligned(src[p], vec)) vec >>= 1;
+    }
+    if (dst == nullptr) return fail(UAA_ERR_INVALID_ARG, "permute: dst is NULL");
+    if (!aligned(dst, elem_bytes))
+        return fail(UAA_ERR_INVALID_ARG, "permute: dst not aligned to %d bytes", elem_bytes);
+    while (vec > elem_bytes && !aligned(dst, vec)) vec >>= 1;
+
+    uaa::PermuteArgs a{};
+    for (int p = 0; p < world; ++p) a.src[p] = static_cast<const unsigned char*>(src[p]);
+    for (int p = 0; p <= world; ++p) {
+        a.seq_off[p] = seq_off[p];
+        a.head_off[p] = hoff[p];
+    }
+    a.dst = static_cast<unsigned char*>(dst);
+    a.B = B;
+    a.H = H;
+    a.n_rows = n_rows;
+    a.head_vecs = slice / vec;
+    a.world = world;
+    a.rank = rank;
+    const int64_t row_vecs = (dir == UAA_SEQ2HEAD ? Hr : H) * a.head_vecs;
+    if (row_vecs >= kMaxIdx32) return fail(UAA_ERR_INVALID_ARG, "permute: rows too long");
+    a.row_vecs = (int32_t)row_vecs;
+    int lg = 0;
+    while ((int64_t(1) << lg) < row_vecs && lg < 6) ++lg;
+    a.lanes_per_row_log2 = lg;
+    a.div_tokens = uaa::make_fastdiv((uint32_t)out_tokens);
+    a.div_head = uaa::make_fastdiv((uint32_t)a.head_vecs);
+    return hip_status(uaa::launch_permute(dir, vec, a, static_cast<hipStream_t>(stream)), "permute launch");
+}
+
+namespace {
+
+// Map one side of a usp_mask onto the two-piece affine position map.
+int side_map(const usp_mask& m, bool q_side, int64_t n, uaa::PosMap& out)
+{
+    const int64_t big = int64_t(1) << 62;
+    out = uaa::PosMap{0, 0, 1, big};
+    switch (m.kind) {
+    case USP_MASK_CAUSAL: {
+        const int64_t off = q_side ? m.q_off : m.k_off;
+        if (off < -(int64_t(1) << 60) || off > (int64_t(1) << 60))
+            return fail(UAA_ERR_INVALID_ARG, "attn: causal offset out of range");
+        out.base0 = off;
+        return UAA_OK;
+    }
+    case USP_MASK_ZIGZAG: {
+        const int32_t* ids = q_side ? m.q_chunks : m.k_chunks;
+        if (m.chunk < 1 || m.chunk > (int64_t(1) << 40))
+            return fail(UAA_ERR_INVALID_ARG, "attn: zigzag chunk length must be >= 1");
+        if (ids[0] < 0) return fail(UAA_ERR_INVALID_ARG, "attn: zigzag chunk id must be >= 0");
+        const int n_chunks = ids[1] >= 0 ? 2 : 1;
+        if (n > n_chunks * m.chunk)
+            return fail(UAA_ERR_INVALID_ARG, "attn: %s side has %lld rows but its chunks hold %lld",
+                        q_side ? "query" : "key", (long long)n, (long long)(n_chunks * m.chunk));
+        out.base0 = (int64_t)ids[0] * m.chunk;
+        if (n_chunks == 2) {
+            out.base1 = (int64_t)ids[1] * m.chunk;
+            out.seg_len = m.chunk;
+        }
+        return UAA_OK;
+    }
+    case USP_MASK_STRIPE: {
+        const int32_t r = q_side ? m.q_rank : m.k_rank;
+        if (m.world < 1 || r < 0 || r >= m.world)
+            return fail(UAA_ERR_INVALID_ARG, "attn: stripe needs world >= 1 and 0 <= rank < world");
+        out.base0 = r;
+        out.stride = m.world;
+        return UAA_OK;
+    }
+    default:
+        return fail(UAA_ERR_INVALID_ARG, "attn: unknown mask kind %d", m.kind);
+    }
+}
+
+}  // namespace
+
+UAA_EXPORT int usp_attn_fwd_lse(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                const void* q, const void* k, const void* v, void* o, int o_dtype,
+                                float* lse, float scale, const usp_mask* mask, void* stream)
+{
+    if (dtype != UAA_BF16 && dtype != UAA_FP32)
+        return fail(UAA_ERR_INVALID_ARG, "attn: dtype must be UAA_BF16 or UAA_FP32, got %d", dtype);
+    if (o_dtype != UAA_BF16 && o_dtype != UAA_FP32)
+        return fail(UAA_ERR_INVALID_ARG, "attn: o_dtype must be UAA_BF16 or UAA_FP32, got %d", o_dtype);
+    if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || D < 1)
+        return fail(UAA_ERR_INVALID_ARG, "attn: negative size");
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(UAA_ERR_INVALID_ARG, "attn: scale must be finite and > 0");
+    if (mask != nullptr && (mask->kind < USP_MASK_FULL || mask->kind > USP_MASK_STRIPE))
+        return fail(UAA_ERR_INVALID_ARG, "attn: unknown mask kind %d", mask->kind);
+    if (D != 64 && D != 128) return fail(UAA_ERR_UNSUPPORTED, "attn: D must be 64 or 128, got %lld", (long long)D);
+    if (dtype == UAA_FP32 && o_dtype != UAA_FP32)
+        return fail(UAA_ERR_UNSUPPORTED, "attn: fp32 input needs fp32 output");
+    if ((double)B * (Sq > Sk ? Sq : Sk) * H * D > (double)kMaxElems)
+        return fail(UAA_ERR_INVALID_ARG, "attn: tensor too large");
+    if (B == 0 || H == 0 || Sq == 0) return UAA_OK;
+    if (q == nullptr || o == nullptr || lse == nullptr)
+        return fail(UAA_ERR_INVALID_ARG, "attn: q, o and lse must not be NULL");
+    if (Sk > 0 && (k == nullptr || v == nullptr))
+        return fail(UAA_ERR_INVALID_ARG, "attn: k and v must not be NULL when Sk > 0");
+    if (!aligned(q, 16) || !aligned(o, 16) || (Sk > 0 && (!aligned(k, 16) || !aligned(v, 16))))
+        return fail(UAA_ERR_INVALID_ARG, "attn: q, k, v and o must be 16-byte aligned");
+    if (!aligned(lse, 4)) return fail(UAA_ERR_INVALID_ARG, "attn: lse must be 4-byte aligned");
+
+    uaa::AttnArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.B = B;
+    a.H = H;
+    a.Sq = Sq;
+    a.Sk = Sk;
+    a.scale = scale;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    a.masked = 0;
+    if (mask != nullptr && mask->kind != USP_MASK_FULL) {
+        a.masked = 1;
+        int rc = side_map(*mask, true, Sq, a.qmap);
+        if (rc != UAA_OK) return rc;
+        rc = side_map(*mask, false, Sk, a.kmap);
+        if (rc != UAA_OK) return rc;
+    }
+    const int64_t bm = dtype == UAA_BF16 ? 128 : 64;
+    const int64_t n_qtiles = (Sq + bm - 1) / bm;
+    if (n_qtiles * H * B >= kMaxIdx32) return fail(UAA_ERR_INVALID_ARG, "attn: grid too large");
+    a.n_qtiles = (int32_t)n_qtiles;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == UAA_BF16) return hip_status(uaa::launch_attn_bf16((int)D, o_dtype, a, s), "attn launch");
+    return hip_status(uaa::launch_attn_fp32((int)D, a, s), "attn launch");
+}
+
+UAA_EXPORT int usp_lse_merge(int n_parts, int64_t B, int64_t S, int64_t H, int64_t D,
+                             const void* const* o_parts, int part_dtype, const float* const* lse_parts,
+                             void* o_out, int out_dtype, float* lse_out, void* stream)
+{
+    if (n_parts < 1 || n_parts > USP_MAX_PARTS)
+        return fail(UAA_ERR_INVALID_ARG, "merge: n_parts must be in [1, %d], got %d", USP_MAX_PARTS, n_parts);
+    if (part_dtype != UAA_BF16 && part_dtype != UAA_FP32)
+        return fail(UAA_ERR_INVALID_ARG, "merge: part_dtype must be UAA_BF16 or UAA_FP32");
+    if (out_dtype != UAA_BF16 && out_dtype != UAA_FP32)
+        return fail(UAA_ERR_INVALID_ARG, "merge: out_dtype must be UAA_BF16 or UAA_FP32");
+    if (B < 0 || S < 0 || H < 0 || D < 1) return fail(UAA_ERR_INVALID_ARG, "merge: bad sizes");
+    if ((double)B * S * H * D > (double)kMaxElems) return fail(UAA_ERR_INVALID_ARG, "merge: tensor too large");
+    const int64_t rows = B * S * H;
+    if (rows == 0) return UAA_OK;
+    if (D > 65536) return fail(UAA_ERR_UNSUPPORTED, "merge: D above 65536");
+    if (o_parts == nullptr || lse_parts == nullptr || o_out == nullptr || lse_out == nullptr)
+        return fail(UAA_ERR_INVALID_ARG, "merge: NULL pointer");
+    const uintptr_t in_sz = part_dtype == UAA_BF16 ? 2 : 4, out_sz = out_dtype == UAA_BF16 ? 2 : 4;
+    uaa::MergeArgs a{};
+    for (int n = 0; n < n_parts; ++n) {
+        if (o_parts[n] == nullptr || lse_parts[n] == nullptr)
+            return fail(UAA_ERR_INVALID_ARG, "merge: part %d is NULL", n);
+        if (!aligned(o_parts[n], in_sz) || !aligned(lse_parts[n], 4))
+            return fail(UAA_ERR_INVALID_ARG, "merge: part %d misaligned", n);
+        if (o_parts[n] == o_out && part_dtype != out_dtype)
+            return fail(UAA_ERR_INVALID_ARG, "merge: o_out may alias a part only when the dtypes match");
+        a.o_parts[n] = o_parts[n];
+        a.lse_parts[n] = lse_parts[n];
+    }
+    if (!aligned(o_out, out_sz) || !aligned(lse_out, 4))
+        return fail(UAA_ERR_INVALID_ARG, "merge: output misaligned");
+    a.o_out = o_out;
+    a.lse_out = lse_out;
+    a.rows = rows;
+    a.D = (int32_t)D;
+    a.n_parts = n_parts;
+    return hip_status(uaa::launch_merge(part_dtype, out_dtype, a, static_cast<hipStream_t>(stream)),
+                      "merge launch");
+}

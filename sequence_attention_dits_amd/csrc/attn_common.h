@@ -1,0 +1,50 @@
+// attn_common.h -- position maps and tile classification shared by the two
+// attention kernels (fp32 and bf16).  Internal to libuaa.
+//
+// Positions: the USP / yunchang summary ("How It Works", "Highlighted
+// Details") names zigzag, stripe and basic ring layouts; every one of them
+// gives each side of an attention call a map from local row index to global
+// token position made of at most two increasing affine pieces (PosMap).  A
+// key is allowed for a query iff kpos <= qpos.
+#pragma once
+
+#include "internal.h"
+
+namespace uaa {
+
+__device__ __forceinline__ int64_t pos_of(const PosMap& m, int64_t idx)
+{
+    return idx < m.seg_len ? m.base0 + m.stride * idx : m.base1 + m.stride * (idx - m.seg_len);
+}
+
+// [min, max] of pos_of over idx in [lo, hi), hi > lo.  Each piece increases.
+__device__ __forceinline__ void pos_range(const PosMap& m, int64_t lo, int64_t hi, int64_t& pmin,
+                                          int64_t& pmax)
+{
+    if (hi <= m.seg_len || lo >= m.seg_len) {
+        pmin = pos_of(m, lo);
+        pmax = pos_of(m, hi - 1);
+    } else {
+        const int64_t a = pos_of(m, lo), b = pos_of(m, m.seg_len);
+        const int64_t c = pos_of(m, m.seg_len - 1), d = pos_of(m, hi - 1);
+        pmin = a < b ? a : b;
+        pmax = c > d ? c : d;
+    }
+}
+
+// Workgroup index -> (q tile, head, batch).  Workgroups are handed to the
+// 8 XCDs round-robin, and each XCD has its own L2: renumber so that each XCD
+// gets one contiguous run of logical tiles, i.e. the q tiles of the same head
+// share the L2 that holds that head's K and V.
+__device__ __forceinline__ void decode_tile(const AttnArgs& a, int64_t& qt, int64_t& h, int64_t& b)
+{
+    const uint32_t n = gridDim.x, L = blockIdx.x;
+    const uint32_t per = n / 8u;
+    const uint32_t logical = (L < per * 8u) ? (L % 8u) * per + L / 8u : L;
+    qt = logical % (uint32_t)a.n_qtiles;
+    const int64_t rest = logical / (uint32_t)a.n_qtiles;
+    h = rest % a.H;
+    b = rest / a.H;
+}
+
+}  // namespace uaa

@@ -1,0 +1,93 @@
+// internal.h -- declarations shared by the HIP translation units of libuaa.
+// Not part of the public ABI (include/uaa.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/uaa.h"
+
+namespace uaa {
+
+// Launch through hipLaunchKernel so the launch status is this launch's own
+// (a <<<>>> launch only reports through the sticky hipGetLastError state).
+template <typename Arg>
+inline hipError_t launch_kernel(void (*kern)(Arg), dim3 grid, dim3 block, size_t lds_bytes,
+                                hipStream_t stream, const Arg& arg)
+{
+    void* params[] = {const_cast<Arg*>(&arg)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, params, lds_bytes, stream);
+}
+
+// --------------------------------------------------------------------------
+// Permute: arguments after host validation.  Offsets are in tokens / heads;
+// `vec_bytes` is the access width chosen on the host (1, 2, 4, 8 or 16),
+// and every row, head slice and pointer is a multiple of it.
+// --------------------------------------------------------------------------
+struct FastDiv {  // n / d for 0 <= n < 2^31, d >= 1, via one mul-hi and a shift
+    uint32_t mul;
+    uint32_t shift;
+    uint32_t d;
+};
+FastDiv make_fastdiv(uint32_t d);
+
+struct PermuteArgs {
+    const unsigned char* src[UAA_MAX_WORLD];
+    int64_t seq_off[UAA_MAX_WORLD + 1];
+    int64_t head_off[UAA_MAX_WORLD + 1];
+    unsigned char* dst;
+    int64_t B, H;
+    int64_t n_rows;       // destination rows (b, token) to produce
+    int64_t head_vecs;    // vectors per head slice (D * elem_bytes / vec_bytes)
+    int32_t world, rank;
+    int32_t row_vecs;     // vectors per destination row
+    int32_t lanes_per_row_log2;
+    FastDiv div_tokens;   // destination tokens per batch (S or S_p)
+    FastDiv div_head;     // head_vecs, for HEAD2SEQ
+};
+
+hipError_t launch_permute(int dir, int vec_bytes, const PermuteArgs& a, hipStream_t s);
+
+// --------------------------------------------------------------------------
+// Merge.
+// --------------------------------------------------------------------------
+struct MergeArgs {
+    const void* o_parts[USP_MAX_PARTS];
+    const float* lse_parts[USP_MAX_PARTS];
+    void* o_out;
+    float* lse_out;
+    int64_t rows;         // B * S * H
+    int32_t D;
+    int32_t n_parts;
+};
+
+hipError_t launch_merge(int part_dtype, int out_dtype, const MergeArgs& a, hipStream_t s);
+
+// --------------------------------------------------------------------------
+// Attention.  Token positions of both sides as two affine segments:
+//   pos(idx) = base0 + stride * idx                    for idx <  seg_len
+//            = base1 + stride * (idx - seg_len)        for idx >= seg_len
+// Every mask kind of usp_mask maps onto this form on the host.
+// --------------------------------------------------------------------------
+struct PosMap {
+    int64_t base0, base1, stride, seg_len;
+};
+
+struct AttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int64_t B, H, Sq, Sk;
+    float scale;          // softmax scale as given
+    float scale_log2;     // scale * log2(e)
+    int32_t masked;       // 0: every key allowed; 1: kpos(j) <= qpos(i)
+    PosMap qmap, kmap;
+    int32_t n_qtiles;     // ceil(Sq / rows per workgroup)
+};
+
+hipError_t launch_attn_bf16(int D, int o_dtype, const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_fp32(int D, const AttnArgs& a, hipStream_t s);
+
+}  // namespace uaa

@@ -1,0 +1,198 @@
+// merge.hip -- N-way LSE-rescaled merge of partial attention results.
+//
+// "Add Unified Sequence Parallel attention" (diffusers PR #12693), review
+// thread: each Ring step's (out, lse) is folded into the running pair in
+// fp32 with a sigmoid-weighted update of out and a log-sigmoid update of
+// lse, and cast back to the query dtype once.  Folding N partials that way
+// is the softmax-weighted mean of the partials; this kernel computes it in
+// one pass with the maximum shifted out, which keeps rows whose partials are
+// -inf (no allowed key) finite instead of NaN:
+//   M = max_n lse_n,  lse = M + log(sum_n exp(lse_n - M)),
+//   o = sum_n exp(lse_n - lse) * o_n,   (0, -inf) if every lse_n is -inf.
+//
+// HBM-bound: each row is D contiguous elements per partial.  A row is split
+// over D / VEC lanes (VEC elements = 16 bytes each), so a wavefront covers
+// several rows with fully coalesced 16-byte accesses; every lane loads all
+// N partial slices before it does any arithmetic, and the few LSE loads per
+// row are shared by the row's lanes through the cache.
+#include "internal.h"
+
+namespace uaa {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short b)
+{
+    return __uint_as_float(((unsigned int)b) << 16);
+}
+
+// float -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ unsigned short f32_to_bf16(float f)
+{
+    const unsigned int u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (unsigned short)((u >> 16) | 0x40u);
+    return (unsigned short)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// VEC elements of type T at p, widened to fp32.
+template <typename T, int VEC> struct Slice;
+
+template <> struct Slice<unsigned short, 8> {     // bf16, 16 bytes
+    static __device__ __forceinline__ void load(const void* p, float* x)
+    {
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = __uint_as_float(w[e] << 16);
+            x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void store(void* p, const float* x)
+    {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = (unsigned int)f32_to_bf16(x[2 * e]) | ((unsigned int)f32_to_bf16(x[2 * e + 1]) << 16);
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+    }
+};
+
+template <> struct Slice<float, 4> {              // fp32, 16 bytes
+    static __device__ __forceinline__ void load(const void* p, float* x)
+    {
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e]);
+    }
+    static __device__ __forceinline__ void store(void* p, const float* x)
+    {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(x[e]);
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+    }
+};
+
+template <> struct Slice<unsigned short, 1> {     // bf16, any D
+    static __device__ __forceinline__ void load(const void* p, float* x)
+    {
+        x[0] = bf16_to_f32(*reinterpret_cast<const unsigned short*>(p));
+    }
+    static __device__ __forceinline__ void store(void* p, const float* x)
+    {
+        *reinterpret_cast<unsigned short*>(p) = f32_to_bf16(x[0]);
+    }
+};
+
+template <> struct Slice<float, 1> {              // fp32, any D
+    static __device__ __forceinline__ void load(const void* p, float* x)
+    {
+        x[0] = *reinterpret_cast<const float*>(p);
+    }
+    static __device__ __forceinline__ void store(void* p, const float* x)
+    {
+        *reinterpret_cast<float*>(p) = x[0];
+    }
+};
+
+// A row's D / VEC slices are spread over `lpr` lanes (a power of two, at most
+// 64; lanes loop when a row has more slices), so a wavefront covers 64 / lpr
+// rows and no lane index needs a division.
+template <typename TIn, typename TOut, int VEC, int NMAX>
+__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a, int lpr_log2)
+{
+    const int lane = threadIdx.x & 63;
+    const int lpr = 1 << lpr_log2;
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t row = wave * (64 >> lpr_log2) + (lane >> lpr_log2);
+    if (row >= a.rows) return;
+    const int N = a.n_parts;
+    const int slices = a.D / VEC;              // host guarantees divisibility
+
+    float lse[NMAX];
+    float M = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < NMAX; ++n) {
+        lse[n] = (n < N) ? a.lse_parts[n][row] : -INFINITY;
+        M = fmaxf(M, lse[n]);
+    }
+    float L = -INFINITY;
+    float w[NMAX];
+    if (M != -INFINITY) {
+        float sum = 0.f;
+#pragma unroll
+        for (int n = 0; n < NMAX; ++n)
+            if (n < N) sum += __expf(lse[n] - M);
+        L = M + __logf(sum);
+    }
+#pragma unroll
+    for (int n = 0; n < NMAX; ++n) w[n] = (n < N && M != -INFINITY) ? __expf(lse[n] - L) : 0.f;
+
+    for (int seg = lane & (lpr - 1); seg < slices; seg += lpr) {
+        const int64_t elem = row * a.D + (int64_t)seg * VEC;
+        float acc[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+        if (M != -INFINITY) {
+            // every partial slice is loaded before any arithmetic
+            float x[NMAX][VEC];
+#pragma unroll
+            for (int n = 0; n < NMAX; ++n)
+                if (n < N)
+                    Slice<TIn, VEC>::load(reinterpret_cast<const TIn*>(a.o_parts[n]) + elem, x[n]);
+#pragma unroll
+            for (int n = 0; n < NMAX; ++n)
+                if (n < N) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) acc[e] = fmaf(w[n], x[n][e], acc[e]);
+                }
+        }
+        Slice<TOut, VEC>::store(reinterpret_cast<TOut*>(a.o_out) + elem, acc);
+    }
+    if ((lane & (lpr - 1)) == 0) a.lse_out[row] = L;
+}
+
+template <typename TIn, typename TOut, int VEC>
+static hipError_t launch_vec(const MergeArgs& a, hipStream_t s)
+{
+    const int slices = a.D / VEC;
+    int lpr_log2 = 0;
+    while ((1 << lpr_log2) < slices && lpr_log2 < 6) ++lpr_log2;
+    const int64_t rows_per_block = 4 * (64 >> lpr_log2);
+    const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)blocks), block(256);
+    void* params[] = {const_cast<MergeArgs*>(&a), &lpr_log2};
+    const void* fn;
+    if (a.n_parts <= 2) fn = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, VEC, 2>);
+    else if (a.n_parts <= 4) fn = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, VEC, 4>);
+    else if (a.n_parts <= 8) fn = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, VEC, 8>);
+    else fn = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, VEC, 16>);
+    return hipLaunchKernel(fn, grid, block, params, 0, s);
+}
+
+// 16-byte slices need D * size to be a multiple of 16 on both sides and
+// 16-byte aligned base pointers; otherwise one element per lane.
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hipError_t launch_merge(int part_dtype, int out_dtype, const MergeArgs& a, hipStream_t s)
+{
+    bool wide = aligned16(a.o_out);
+    for (int n = 0; n < a.n_parts; ++n) wide = wide && aligned16(a.o_parts[n]);
+    const bool in_bf = part_dtype == UAA_BF16, out_bf = out_dtype == UAA_BF16;
+    if (in_bf && out_bf) {
+        if (wide && a.D % 8 == 0) return launch_vec<unsigned short, unsigned short, 8>(a, s);
+        return launch_vec<unsigned short, unsigned short, 1>(a, s);
+    }
+    if (!in_bf && !out_bf) {
+        if (wide && a.D % 4 == 0) return launch_vec<float, float, 4>(a, s);
+        return launch_vec<float, float, 1>(a, s);
+    }
+    // mixed dtypes: one element per lane keeps both sides simple
+    if (in_bf) return launch_vec<unsigned short, float, 1>(a, s);
+    return launch_vec<float, unsigned short, 1>(a, s);
+}
+
+}  // namespace uaa

@@ -1,0 +1,167 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/uaa.h declares, agrees with the binding on the mask
+struct layout, and rejects malformed arguments with the documented status
+before anything reaches the HIP runtime."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sequence_attention_dits_amd as uaa
+from sequence_attention_dits_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "uaa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert {"uaa_seq2head_permute", "usp_attn_fwd_lse", "usp_lse_merge", "uaa_last_error"} <= set(names)
+    lib = uaa.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+    assert lib.uaa_abi_version() == 1
+
+
+def test_mask_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "uaa.h"\n'
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(usp_mask),'
+                   'offsetof(usp_mask,kind),offsetof(usp_mask,world),offsetof(usp_mask,q_off),'
+                   'offsetof(usp_mask,k_off),offsetof(usp_mask,chunk),offsetof(usp_mask,q_chunks),'
+                   'offsetof(usp_mask,k_chunks),offsetof(usp_mask,q_rank),offsetof(usp_mask,k_rank));return 0;}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    c_vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
+    M = binding.usp_mask
+    py_vals = [ctypes.sizeof(M)] + [getattr(M, f).offset for f in
+                                    ("kind", "world", "q_off", "k_off", "chunk", "q_chunks", "k_chunks",
+                                     "q_rank", "k_rank")]
+    assert c_vals == py_vals
+
+
+def _perm(*args):
+    lib = uaa.lib()
+    return lib.uaa_seq2head_permute(*args), lib.uaa_last_error().decode()
+
+
+def _i64(*v):
+    return (ctypes.c_int64 * len(v))(*v)
+
+
+def _ptrs(*v):
+    return (ctypes.c_void_p * len(v))(*v)
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails validation first
+
+
+@pytest.mark.parametrize("args,code,text", [
+    ((7, 0, 2, _i64(0, 2, 4), None, 1, 2, 8, 2, _ptrs(FAKE, FAKE), FAKE, None), -1, "dir"),
+    ((0, 0, 0, _i64(0), None, 1, 2, 8, 2, _ptrs(FAKE), FAKE, None), -1, "world"),
+    ((0, 2, 2, _i64(0, 2, 4), None, 1, 2, 8, 2, _ptrs(FAKE, FAKE), FAKE, None), -1, "rank"),
+    ((0, 0, 2, _i64(0, 2, 4), None, 1, 2, 8, 3, _ptrs(FAKE, FAKE), FAKE, None), -1, "elem_bytes"),
+    ((0, 0, 2, _i64(1, 2, 4), None, 1, 2, 8, 2, _ptrs(FAKE, FAKE), FAKE, None), -1, "seq_off[0]"),
+    ((0, 0, 2, _i64(0, 3, 2), None, 1, 2, 8, 2, _ptrs(FAKE, FAKE), FAKE, None), -1, "decreases"),
+    ((0, 0, 3, _i64(0, 1, 2, 3), None, 1, 2, 8, 2, _ptrs(FAKE, FAKE, FAKE), FAKE, None), -1, "no heads"),
+    ((0, 0, 2, _i64(0, 2, 4), _i64(0, 1, 3), 1, 2, 8, 2, _ptrs(FAKE, FAKE), FAKE, None), -1, "head_off"),
+    ((0, 0, 2, _i64(0, 2, 4), None, 1, 2, 8, 2, _ptrs(FAKE, 0), FAKE, None), -1, "src[1]"),
+    ((0, 0, 2, _i64(0, 2, 4), None, 1, 2, 8, 2, _ptrs(FAKE, FAKE), 0, None), -1, "dst"),
+    ((0, 0, 2, _i64(0, 2, 4), None, 1, 2, 8, 4, _ptrs(FAKE + 2, FAKE), FAKE, None), -1, "aligned"),
+    ((0, 0, 2, _i64(0, 2, 4), None, -1, 2, 8, 2, _ptrs(FAKE, FAKE), FAKE, None), -1, "B >= 0"),
+])
+def test_permute_validation(args, code, text):
+    rc, msg = _perm(*args)
+    assert rc == code and text in msg, (rc, msg)
+
+
+def test_permute_empty_work_is_ok_without_pointers():
+    # B = 0 and an empty destination shard need no pointers and no GPU
+    assert _perm(0, 0, 2, _i64(0, 2, 4), None, 0, 2, 8, 2, _ptrs(0, 0), 0, None)[0] == 0
+    assert _perm(1, 1, 2, _i64(0, 4, 4), None, 1, 2, 8, 2, _ptrs(0, 0), 0, None)[0] == 0
+
+
+def _attn(dtype=0, B=1, H=1, Sq=4, Sk=4, D=128, q=FAKE, k=FAKE, v=FAKE, o=FAKE, odt=0, lse=FAKE,
+          scale=0.1, mask=None):
+    lib = uaa.lib()
+    m = mask if mask is not None else uaa.mask_full()
+    rc = lib.usp_attn_fwd_lse(dtype, B, H, Sq, Sk, D, q, k, v, o, odt, lse, scale, ctypes.byref(m), None)
+    return rc, lib.uaa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(dtype=5), -1, "dtype"),
+    (dict(odt=9), -1, "o_dtype"),
+    (dict(Sq=-1), -1, "negative"),
+    (dict(scale=0.0), -1, "scale"),
+    (dict(scale=float("inf")), -1, "scale"),
+    (dict(scale=float("nan")), -1, "scale"),
+    (dict(D=96), -2, "D must be"),
+    (dict(dtype=1, odt=0), -2, "fp32 input"),
+    (dict(q=0), -1, "NULL"),
+    (dict(k=0), -1, "NULL"),
+    (dict(o=FAKE + 8), -1, "16-byte"),
+    (dict(lse=FAKE + 2), -1, "4-byte"),
+    (dict(mask=binding.usp_mask(kind=9)), -1, "mask kind"),
+    (dict(mask=uaa.mask_zigzag(0, [1], [2])), -1, "chunk length"),
+    (dict(mask=uaa.mask_zigzag(2, [1], [2])), -1, "chunks hold"),
+    (dict(mask=uaa.mask_zigzag(4, [-3], [2])), -1, "chunk id"),
+    (dict(mask=uaa.mask_stripe(0, 0, 0)), -1, "stripe"),
+    (dict(mask=uaa.mask_stripe(4, 1, 4)), -1, "stripe"),
+])
+def test_attention_validation(kw, code, text):
+    rc, msg = _attn(**kw)
+    assert rc == code and text in msg, (rc, msg)
+
+
+def test_attention_empty_work_is_ok():
+    assert _attn(Sq=0, q=0, o=0, lse=0)[0] == 0
+    assert _attn(B=0)[0] == 0
+    assert _attn(H=0)[0] == 0
+
+
+def _merge(n=2, B=1, S=4, H=1, D=8, parts=None, pdt=0, lses=None, o=FAKE, odt=0, lse=FAKE):
+    lib = uaa.lib()
+    parts = parts if parts is not None else [FAKE] * max(n, 1)
+    lses = lses if lses is not None else [FAKE] * max(n, 1)
+    rc = lib.usp_lse_merge(n, B, S, H, D, _ptrs(*parts), pdt, _ptrs(*lses), o, odt, lse, None)
+    return rc, lib.uaa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(n=0), -1, "n_parts"),
+    (dict(n=17, parts=[FAKE] * 17, lses=[FAKE] * 17), -1, "n_parts"),
+    (dict(pdt=4), -1, "part_dtype"),
+    (dict(odt=4), -1, "out_dtype"),
+    (dict(D=0), -1, "sizes"),
+    (dict(parts=[FAKE, 0]), -1, "part 1"),
+    (dict(lses=[FAKE + 2, FAKE]), -1, "misaligned"),
+    (dict(o=0), -1, "NULL"),
+    (dict(parts=[FAKE, FAKE], o=FAKE, pdt=0, odt=1), -1, "alias"),
+])
+def test_merge_validation(kw, code, text):
+    rc, msg = _merge(**kw)
+    assert rc == code and text in msg, (rc, msg)
+
+
+def test_merge_empty_work_is_ok():
+    assert _merge(S=0, o=0, lse=0)[0] == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.lib()
