@@ -1,0 +1,358 @@
+"""Throughput of one rank's share of context-parallel attention on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input
+resident in HBM, for the FLUX.1-dev 1024x1024 rank share (B=1, S=4608 =
+512 text + 4096 image tokens, 24 heads of 128, bf16, Ulysses degree 2, this
+rank = head rank 0 / token rank 0):
+
+  1. Ulysses gather (SEQ2HEAD) of Q, K and V from the 2 token shards of 2304
+     tokens into this rank's 12 heads over all 4608 tokens      (3 launches)
+  2. attention with LSE of the 4608 queries against the keys/values, taken
+     as 2 Ring chunks of 2304                                   (2 launches)
+  3. LSE merge of the 2 partial (O, LSE) pairs                  (1 launch)
+  4. inverse gather (HEAD2SEQ) of O and of the LSE into this rank's token
+     shard; the other head rank's shard stands in for what the exchange
+     would deliver                                              (2 launches)
+
+value = attention FLOPs of the step (4*D*H*Sq*Sk = 130.46 GFLOP) / step time.
+Input sets rotate over more than 4x the 256 MB Infinity Cache so every
+step starts from cold HBM.  Each step is captured once per input set as a
+HIP graph and replayed (a replay is checked bit for bit against the eager
+step first).  Per-kernel times come from HIP events around each launch of
+the same steps launched eagerly, on the stream the kernels run on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_BF16_TFLOPS = 2516.6   # dense bf16 matrix (256 CU x 2.4 GHz x 4096 FLOP/clk)
+PEAK_HBM_GBPS = 8000.0      # HBM3E
+
+METRIC = "attention TFLOP/s + % bf16 MFMA peak on FLUX-shaped rank share; permute GB/s"
+
+WORKLOADS = {
+    # name: (synth config id, description)
+    "flux1024": (2, "FLUX.1-dev 1024x1024 Ulysses rank share: S=4608, 12 of 24 heads, D=128, bf16, "
+                    "K/V as 2 Ring chunks of 2304, LSE merge, inverse gather"),
+    "flux1008": (3, "FLUX.1-dev 1008x1008 UAA rank share: S=4481 (2241/2240), 12 of 24 heads, D=128, bf16, "
+                    "K/V as 2 Ring chunks of 2241/2240, LSE merge, inverse gather"),
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="flux1024", choices=sorted(WORKLOADS))
+    p.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough for 1 GiB)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+class Share:
+    """Device buffers of one workload and the launches of one step."""
+
+    def __init__(self, cfg_id: int, n_sets: int):
+        import numpy as np
+        import torch
+
+        import synth
+        import sequence_attention_dits_amd as uaa
+        self.uaa = uaa
+        self.torch = torch
+        c = synth.CONFIGS[cfg_id]
+        self.B, self.S, self.H, self.D = c["B"], c["S"], c["H"], c["D"]
+        self.P = 2
+        self.seq_off = [0, c["shards"][0], self.S]
+        base, extra = divmod(self.H, self.P)
+        self.head_off = [0, base + (1 if extra else 0), self.H]
+        self.Hr = self.head_off[1]
+        self.scale = float(np.float32(1.0 / math.sqrt(self.D)))
+        self.ring = [(0, self.seq_off[1]), (self.seq_off[1], self.S)]   # K/V chunks
+        self.host = {}
+        dev0 = {}
+        for t, name in enumerate("qkv"):
+            bits, vals = synth.tensor(cfg_id, t, (self.B, self.S, self.H, self.D), "bf16", rms_norm=(name != "v"))
+            self.host[name] = vals
+            dev0[name] = [torch.from_numpy(np.ascontiguousarray(bits[:, a:b]).view(np.int16)).cuda()
+                          .view(torch.bfloat16) for a, b in zip(self.seq_off[:-1], self.seq_off[1:])]
+        ob, _ = synth.tensor(cfg_id, 9, (self.B, self.S, self.H - self.Hr, self.D), "bf16")
+        dev0["o_other"] = torch.from_numpy(ob.view(np.int16)).cuda().view(torch.bfloat16)
+        dev0["l_other"] = torch.from_numpy(
+            (8 + synth.normal(cfg_id, 10, (self.B, self.S, self.H - self.Hr, 1))).astype(np.float32)).cuda()
+        # rotating copies of the inputs, each in its own allocation
+        self.sets = [dev0] + [{k: ([x.clone() for x in v] if isinstance(v, list) else v.clone())
+                               for k, v in dev0.items()} for _ in range(n_sets - 1)]
+        bf = torch.bfloat16
+        B, S, Hr, D, H = self.B, self.S, self.Hr, self.D, self.H
+        self.qh = {n: torch.empty(B, S, Hr, D, device="cuda", dtype=bf) for n in "qkv"}
+        self.kc = [(self.qh["k"][:, a:b], self.qh["v"][:, a:b]) for a, b in self.ring]
+        self.o_part = [torch.empty(B, S, Hr, D, device="cuda", dtype=bf) for _ in self.ring]
+        self.l_part = [torch.empty(B, S, Hr, device="cuda", dtype=torch.float32) for _ in self.ring]
+        self.o = torch.empty(B, S, Hr, D, device="cuda", dtype=bf)
+        self.lse = torch.empty(B, S, Hr, device="cuda", dtype=torch.float32)
+        S0 = self.seq_off[1]
+        self.o_tok = torch.empty(B, S0, H, D, device="cuda", dtype=bf)
+        self.l_tok = torch.empty(B, S0, H, 1, device="cuda", dtype=torch.float32)
+
+    # algorithmic work per launch
+    def attn_flops(self, chunk):
+        a, b = self.ring[chunk]
+        return 4.0 * self.D * self.Hr * self.B * self.S * (b - a)
+
+    def permute_bytes(self):
+        return 2.0 * 2 * self.B * self.S * self.Hr * self.D          # read + write, bf16
+
+    def merge_bytes(self):
+        rows = self.B * self.S * self.Hr
+        per = rows * self.D * 2 + rows * 4                             # bf16 O + fp32 LSE
+        return 2 * per + per                                           # N=2 in, 1 out
+
+    def head2seq_bytes(self):
+        return 2.0 * 2 * self.B * self.seq_off[1] * self.H * self.D
+
+    def step(self, s, ev=None):
+        """Enqueue one step on input set s; ev(name) brackets launches with events."""
+        uaa = self.uaa
+        d = self.sets[s]
+        rec = ev if ev is not None else (lambda name: _Null())
+        with rec("permute"):
+            uaa.uaa_seq2head_permute(uaa.UAA_SEQ2HEAD, 0, d["q"], self.qh["q"], self.seq_off, self.head_off)
+        with rec("permute"):
+            uaa.uaa_seq2head_permute(uaa.UAA_SEQ2HEAD, 0, d["k"], self.qh["k"], self.seq_off, self.head_off)
+        with rec("permute"):
+            uaa.uaa_seq2head_permute(uaa.UAA_SEQ2HEAD, 0, d["v"], self.qh["v"], self.seq_off, self.head_off)
+        for c, (kc, vc) in enumerate(self.kc):
+            with rec("attn"):
+                uaa.usp_attn_fwd_lse(self.qh["q"], _contig(kc), _contig(vc), self.o_part[c], self.l_part[c],
+                                     self.scale)
+        with rec("merge"):
+            uaa.usp_lse_merge(self.o_part, self.l_part, self.o, self.lse)
+        with rec("head2seq"):
+            uaa.uaa_seq2head_permute(uaa.UAA_HEAD2SEQ, 0, [self.o, d["o_other"]], self.o_tok, self.seq_off,
+                                     self.head_off)
+        with rec("head2seq_lse"):
+            uaa.uaa_seq2head_permute(uaa.UAA_HEAD2SEQ, 0, [self.lse.unsqueeze(-1), d["l_other"]], self.l_tok,
+                                     self.seq_off, self.head_off)
+
+
+class _Null:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        return False
+
+
+def _contig(t):
+    # a K/V chunk of the head-sharded tensor is a slice along S: with B = 1 it
+    # is already contiguous, so no copy is made here
+    return t if t.is_contiguous() else t.contiguous()
+
+
+class EventLog:
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def __call__(self, name):
+        log = self
+
+        class _Ctx:
+            def __enter__(self_):
+                self_.a = log.torch.cuda.Event(enable_timing=True)
+                self_.b = log.torch.cuda.Event(enable_timing=True)
+                self_.a.record()
+                return self_
+
+            def __exit__(self_, *exc):
+                self_.b.record()
+                log.pairs.setdefault(name, []).append((self_.a, self_.b))
+                return False
+        return _Ctx()
+
+    def mean_us(self, name):
+        ps = self.pairs.get(name, [])
+        if not ps:
+            return float("nan")
+        return 1e3 * sum(a.elapsed_time(b) for a, b in ps) / len(ps)
+
+
+def cpu_baseline(share: "Share", target_s: float):
+    """The fp64 oracle (as it stands) on a bounded sample of the same step:
+    the Ulysses gather of Q, K, V, the two Ring-chunk attentions and the merge
+    for a sample of query rows of all 12 heads, and the inverse gather.
+    Returns TFLOP/s of attention work on the sample."""
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    S, H, Hr, D = share.S, share.H, share.Hr, share.D
+    t0 = time.perf_counter()
+    heads = {}
+    for name in "qkv":
+        x = share.host[name]
+        shards = [x[:, a:b] for a, b in zip(share.seq_off[:-1], share.seq_off[1:])]
+        heads[name] = oracle.seq2head(shards, 0, share.seq_off, share.head_off)
+    t_perm = time.perf_counter() - t0
+
+    def run(rows):
+        t = time.perf_counter()
+        parts = [oracle.attention(heads["q"], heads["k"][:, a:b], heads["v"][:, a:b], share.scale, rows=rows)
+                 for a, b in share.ring]
+        oracle.lse_merge([p[0] for p in parts], [p[1] for p in parts])
+        return time.perf_counter() - t
+
+    n = 16
+    rng = np.random.default_rng(0)
+    elapsed = run(np.sort(rng.choice(S, n, replace=False)))
+    while elapsed < target_s / 4 and n < S:
+        n = min(S, int(n * max(2.0, min(8.0, target_s / max(elapsed, 1e-3) / 2))))
+        elapsed = run(np.sort(rng.choice(S, n, replace=False)))
+    # the gather of the whole tensors is pro-rated to the sampled rows
+    t_total = elapsed + t_perm * (n / S)
+    flops = 4.0 * D * Hr * n * S
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of %d query rows x %d heads over all %d keys (2 Ring chunks + merge), fp64, "
+                      "plus the Ulysses gather of Q/K/V pro-rated; %.1f s" % (n, S, Hr, S, t_total)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one rank's share on one GPU; --gpus %d is not supported "
+              "(this build has no multi-GPU path)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    cfg_id, desc = WORKLOADS[args.workload]
+    import synth
+    c = synth.CONFIGS[cfg_id]
+    # enough rotating input sets to exceed 1 GiB of inputs (> 4x the MALL)
+    per_set = 3 * c["B"] * c["S"] * c["H"] * c["D"] * 2 + c["B"] * c["S"] * (c["H"] // 2) * c["D"] * 2
+    n_sets = args.sets or max(2, int(math.ceil((1 << 30) / per_set)))
+    share = Share(cfg_id, n_sets)
+
+    for i in range(max(args.warmup, 1)):
+        share.step(i % n_sets)
+    torch.cuda.synchronize()
+
+    # One HIP graph per input set: a step is 8 launches, and replaying a
+    # captured graph keeps host launch overhead out of the step time.
+    graphs = []
+    for s_ in range(n_sets):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            share.step(s_)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % n_sets].replay()
+    torch.cuda.synchronize()
+
+    # replay check: a replay must reproduce the eager step bit for bit
+    share.step(0)
+    torch.cuda.synchronize()
+    ref_o, ref_l = share.o_tok.clone(), share.l_tok.clone()
+    graphs[1 % n_sets].replay()
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    replay_ok = bool(torch.equal(ref_o.view(torch.int16), share.o_tok.view(torch.int16))
+                     and torch.equal(ref_l, share.l_tok))
+    if not replay_ok:
+        print("graph replay differs from the eager step", file=sys.stderr)
+        sys.exit(1)
+
+    # timed region 1: K graph replays (ms_per_step, value)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        graphs[i % n_sets].replay()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+
+    # timed region 2: the same steps launched one by one with HIP events
+    # around every launch, on the launch stream.  A spin kernel first gives
+    # the host a head start so no launch waits on the host.
+    log = EventLog(torch)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * max(0.02, 1.5 * args.steps * 8 * 40e-6)))
+    for i in range(args.steps):
+        share.step(i % n_sets, log)
+    torch.cuda.synchronize()
+
+    attn_flops = sum(share.attn_flops(c_) for c_ in range(len(share.ring)))
+    value = attn_flops / (ms_step * 1e-3) / 1e12
+    attn_us = log.mean_us("attn")
+    attn_flops_launch = attn_flops / len(share.ring)
+    attn_tf = attn_flops_launch / (attn_us * 1e-6) / 1e12
+    perm_us = log.mean_us("permute")
+    perm_gbps = share.permute_bytes() / (perm_us * 1e-6) / 1e9
+    merge_us = log.mean_us("merge")
+    merge_gbps = share.merge_bytes() / (merge_us * 1e-6) / 1e9
+    h2s_us = log.mean_us("head2seq")
+    h2s_gbps = share.head2seq_bytes() / (h2s_us * 1e-6) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), Q/K RMS-normalised per head; inputs resident in HBM, "
+                "%d rotating sets)" % n_sets,
+        "config": {"workload": desc, "B": share.B, "S": share.S, "heads_total": share.H, "heads_rank": share.Hr,
+                   "D": share.D, "ulysses": share.P, "ring_chunks": len(share.ring),
+                   "attn_flops_per_step": attn_flops},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_bf16_kernel<128,true>", "launch_us": round(attn_us, 2),
+                     "flops_per_launch": attn_flops_launch},
+        "kernels": {
+            "seq2head_permute": {"us": round(perm_us, 2), "GB/s": round(perm_gbps, 1),
+                                 "hbm_frac": round(perm_gbps / PEAK_HBM_GBPS, 4),
+                                 "bytes": share.permute_bytes()},
+            "lse_merge": {"us": round(merge_us, 2), "GB/s": round(merge_gbps, 1),
+                          "hbm_frac": round(merge_gbps / PEAK_HBM_GBPS, 4), "bytes": share.merge_bytes()},
+            "head2seq_permute": {"us": round(h2s_us, 2), "GB/s": round(h2s_gbps, 1),
+                                 "hbm_frac": round(h2s_gbps / PEAK_HBM_GBPS, 4), "bytes": share.head2seq_bytes()},
+            "attention": {"us": round(attn_us, 2), "TFLOP/s": round(attn_tf, 2),
+                          "mfma_frac": round(attn_tf / PEAK_BF16_TFLOPS, 4)},
+        },
+        "permute_GBps": round(perm_gbps, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(share, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
