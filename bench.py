@@ -18,8 +18,9 @@ value = attention FLOPs of the step (4*D*H*Sq*Sk = 130.46 GFLOP) / step time.
 Input sets rotate over more than 4x the 256 MB Infinity Cache so every
 step starts from cold HBM.  Each step is captured once per input set as a
 HIP graph and replayed (a replay is checked bit for bit against the eager
-step first).  Per-kernel times come from HIP events around each launch of
-the same steps launched eagerly, on the stream the kernels run on.
+step first).  Per-kernel times come from HIP events around K back-to-back
+launches of each kernel of the step (same arguments, rotating inputs), on
+the stream the kernels run on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--no-cpu-baseline]
@@ -127,71 +128,51 @@ class Share:
     def head2seq_bytes(self):
         return 2.0 * 2 * self.B * self.seq_off[1] * self.H * self.D
 
-    def step(self, s, ev=None):
-        """Enqueue one step on input set s; ev(name) brackets launches with events."""
+    def launch_one(self, name, s):
+        """Enqueue the launch(es) of one kind that a step makes on set s;
+        returns how many launches were enqueued."""
         uaa = self.uaa
         d = self.sets[s]
-        rec = ev if ev is not None else (lambda name: _Null())
-        with rec("permute"):
+        if name == "permute":
             uaa.uaa_seq2head_permute(uaa.UAA_SEQ2HEAD, 0, d["q"], self.qh["q"], self.seq_off, self.head_off)
-        with rec("permute"):
-            uaa.uaa_seq2head_permute(uaa.UAA_SEQ2HEAD, 0, d["k"], self.qh["k"], self.seq_off, self.head_off)
-        with rec("permute"):
-            uaa.uaa_seq2head_permute(uaa.UAA_SEQ2HEAD, 0, d["v"], self.qh["v"], self.seq_off, self.head_off)
-        for c, (kc, vc) in enumerate(self.kc):
-            with rec("attn"):
+            return 1
+        if name == "attn":
+            for c, (kc, vc) in enumerate(self.kc):
                 uaa.usp_attn_fwd_lse(self.qh["q"], _contig(kc), _contig(vc), self.o_part[c], self.l_part[c],
                                      self.scale)
-        with rec("merge"):
+            return len(self.kc)
+        if name == "merge":
             uaa.usp_lse_merge(self.o_part, self.l_part, self.o, self.lse)
-        with rec("head2seq"):
+            return 1
+        if name == "head2seq":
             uaa.uaa_seq2head_permute(uaa.UAA_HEAD2SEQ, 0, [self.o, d["o_other"]], self.o_tok, self.seq_off,
                                      self.head_off)
-        with rec("head2seq_lse"):
+            return 1
+        if name == "head2seq_lse":
             uaa.uaa_seq2head_permute(uaa.UAA_HEAD2SEQ, 0, [self.lse.unsqueeze(-1), d["l_other"]], self.l_tok,
                                      self.seq_off, self.head_off)
+            return 1
+        raise ValueError(name)
 
+    def step(self, s):
+        """Enqueue one step on input set s."""
+        for name in ("permute3", "attn", "merge", "head2seq", "head2seq_lse"):
+            if name == "permute3":
+                self._seq2head_qkv(s)
+            else:
+                self.launch_one(name, s)
 
-class _Null:
-    def __enter__(self):
-        return self
-
-    def __exit__(self, *a):
-        return False
+    def _seq2head_qkv(self, s):
+        uaa = self.uaa
+        d = self.sets[s]
+        for n in "qkv":
+            uaa.uaa_seq2head_permute(uaa.UAA_SEQ2HEAD, 0, d[n], self.qh[n], self.seq_off, self.head_off)
 
 
 def _contig(t):
     # a K/V chunk of the head-sharded tensor is a slice along S: with B = 1 it
     # is already contiguous, so no copy is made here
     return t if t.is_contiguous() else t.contiguous()
-
-
-class EventLog:
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = {}
-
-    def __call__(self, name):
-        log = self
-
-        class _Ctx:
-            def __enter__(self_):
-                self_.a = log.torch.cuda.Event(enable_timing=True)
-                self_.b = log.torch.cuda.Event(enable_timing=True)
-                self_.a.record()
-                return self_
-
-            def __exit__(self_, *exc):
-                self_.b.record()
-                log.pairs.setdefault(name, []).append((self_.a, self_.b))
-                return False
-        return _Ctx()
-
-    def mean_us(self, name):
-        ps = self.pairs.get(name, [])
-        if not ps:
-            return float("nan")
-        return 1e3 * sum(a.elapsed_time(b) for a, b in ps) / len(ps)
 
 
 def cpu_baseline(share: "Share", target_s: float):
@@ -293,26 +274,35 @@ def main():
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
 
-    # timed region 2: the same steps launched one by one with HIP events
-    # around every launch, on the launch stream.  A spin kernel first gives
-    # the host a head start so no launch waits on the host.
-    log = EventLog(torch)
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(2.4e9 * max(0.02, 1.5 * args.steps * 8 * 40e-6)))
-    for i in range(args.steps):
-        share.step(i % n_sets, log)
+    # timed region 2: per-kernel durations.  Each launch of the step is
+    # repeated back to back over the rotating input sets between two HIP
+    # events on the launch stream; a spin kernel first gives the host a head
+    # start so no launch waits on the host.
+    log = {}
+    for name in ("permute", "attn", "merge", "head2seq", "head2seq_lse"):
+        a_ev = torch.cuda.Event(enable_timing=True)
+        b_ev = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2.4e9 * 0.02))
+        a_ev.record()
+        n = 0
+        for i in range(args.steps):
+            n += share.launch_one(name, i % n_sets)
+        b_ev.record()
+        torch.cuda.synchronize()
+        log[name] = 1e3 * a_ev.elapsed_time(b_ev) / n
     torch.cuda.synchronize()
 
     attn_flops = sum(share.attn_flops(c_) for c_ in range(len(share.ring)))
     value = attn_flops / (ms_step * 1e-3) / 1e12
-    attn_us = log.mean_us("attn")
+    attn_us = log["attn"]
     attn_flops_launch = attn_flops / len(share.ring)
     attn_tf = attn_flops_launch / (attn_us * 1e-6) / 1e12
-    perm_us = log.mean_us("permute")
+    perm_us = log["permute"]
     perm_gbps = share.permute_bytes() / (perm_us * 1e-6) / 1e9
-    merge_us = log.mean_us("merge")
+    merge_us = log["merge"]
     merge_gbps = share.merge_bytes() / (merge_us * 1e-6) / 1e9
-    h2s_us = log.mean_us("head2seq")
+    h2s_us = log["head2seq"]
     h2s_gbps = share.head2seq_bytes() / (h2s_us * 1e-6) / 1e9
 
     out = {

@@ -227,6 +227,8 @@ UAA_EXPORT int usp_attn_fwd_lse(int dtype, int64_t B, int64_t H, int64_t Sq, int
         rc = side_map(*mask, false, Sk, a.kmap);
         if (rc != UAA_OK) return rc;
     }
+    if (dtype == UAA_BF16 && ((double)(Sq > Sk ? Sq : Sk) * H * D * 2 >= 4294967296.0))
+        return fail(UAA_ERR_UNSUPPORTED, "attn: one batch of q or k/v must stay below 4 GiB");
     const int64_t bm = dtype == UAA_BF16 ? 128 : 64;
     const int64_t n_qtiles = (Sq + bm - 1) / bm;
     if (n_qtiles * H * B >= kMaxIdx32) return fail(UAA_ERR_INVALID_ARG, "attn: grid too large");
