@@ -6,13 +6,15 @@ resident in HBM, for the FLUX.1-dev 1024x1024 rank share (B=1, S=4608 =
 rank = head rank 0 / token rank 0):
 
   1. Ulysses gather (SEQ2HEAD) of Q, K and V from the 2 token shards of 2304
-     tokens into this rank's 12 heads over all 4608 tokens      (3 launches)
+     tokens into this rank's 12 heads over all 4608 tokens, the three
+     tensors in one multi-tensor launch                          (1 launch)
   2. attention with LSE of the 4608 queries against the keys/values, taken
      as 2 Ring chunks of 2304                                   (2 launches)
   3. LSE merge of the 2 partial (O, LSE) pairs                  (1 launch)
   4. inverse gather (HEAD2SEQ) of O and of the LSE into this rank's token
      shard; the other head rank's shard stands in for what the exchange
      would deliver                                              (2 launches)
+  (6 launches per step)
 
 value = attention FLOPs of the step (4*D*H*Sq*Sk = 130.46 GFLOP) / step time.
 Input sets rotate over more than 4x the 256 MB Infinity Cache so every
@@ -136,6 +138,9 @@ class Share:
         if name == "permute":
             uaa.uaa_seq2head_permute(uaa.UAA_SEQ2HEAD, 0, d["q"], self.qh["q"], self.seq_off, self.head_off)
             return 1
+        if name == "permute_qkv":
+            self._seq2head_qkv(s)
+            return 1
         if name == "attn":
             for c, (kc, vc) in enumerate(self.kc):
                 uaa.usp_attn_fwd_lse(self.qh["q"], _contig(kc), _contig(vc), self.o_part[c], self.l_part[c],
@@ -165,8 +170,8 @@ class Share:
     def _seq2head_qkv(self, s):
         uaa = self.uaa
         d = self.sets[s]
-        for n in "qkv":
-            uaa.uaa_seq2head_permute(uaa.UAA_SEQ2HEAD, 0, d[n], self.qh[n], self.seq_off, self.head_off)
+        uaa.uaa_seq2head_permute_multi(uaa.UAA_SEQ2HEAD, 0, [d[n] for n in "qkv"], [self.qh[n] for n in "qkv"],
+                                       self.seq_off, self.head_off)
 
 
 def _contig(t):
@@ -279,7 +284,7 @@ def main():
     # events on the launch stream; a spin kernel first gives the host a head
     # start so no launch waits on the host.
     log = {}
-    for name in ("permute", "attn", "merge", "head2seq", "head2seq_lse"):
+    for name in ("permute", "permute_qkv", "attn", "merge", "head2seq", "head2seq_lse"):
         a_ev = torch.cuda.Event(enable_timing=True)
         b_ev = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -303,6 +308,8 @@ def main():
     merge_us = log["merge"]
     merge_gbps = share.merge_bytes() / (merge_us * 1e-6) / 1e9
     h2s_us = log["head2seq"]
+    qkv_us = log["permute_qkv"]
+    qkv_gbps = 3 * share.permute_bytes() / (qkv_us * 1e-6) / 1e9
     h2s_gbps = share.head2seq_bytes() / (h2s_us * 1e-6) / 1e9
 
     out = {
@@ -330,6 +337,9 @@ def main():
             "seq2head_permute": {"us": round(perm_us, 2), "GB/s": round(perm_gbps, 1),
                                  "hbm_frac": round(perm_gbps / PEAK_HBM_GBPS, 4),
                                  "bytes": share.permute_bytes()},
+            "seq2head_permute_qkv": {"us": round(qkv_us, 2), "GB/s": round(qkv_gbps, 1),
+                                     "hbm_frac": round(qkv_gbps / PEAK_HBM_GBPS, 4),
+                                     "bytes": 3 * share.permute_bytes()},
             "lse_merge": {"us": round(merge_us, 2), "GB/s": round(merge_gbps, 1),
                           "hbm_frac": round(merge_gbps / PEAK_HBM_GBPS, 4), "bytes": share.merge_bytes()},
             "head2seq_permute": {"us": round(h2s_us, 2), "GB/s": round(h2s_gbps, 1),

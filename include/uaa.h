@@ -57,9 +57,11 @@ extern "C" {
 #define UAA_SEQ2HEAD 0
 #define UAA_HEAD2SEQ 1
 
-/* Largest Ulysses degree a permute accepts, largest N a merge accepts. */
+/* Largest Ulysses degree a permute accepts, largest N a merge accepts,
+ * largest tensor count of one multi-tensor permute. */
 #define UAA_MAX_WORLD 64
 #define USP_MAX_PARTS 16
+#define UAA_MAX_PERMUTE_TENSORS 4
 
 /* Mask kinds ([YC] ring layouts; "basic" contiguous shards are CAUSAL). */
 #define USP_MASK_FULL 0
@@ -124,13 +126,34 @@ typedef struct usp_mask {
  * elem_bytes: 1, 2, 4 or 8; elements are copied as opaque bit patterns
  * (bit-exact).  Every pointer must be aligned to elem_bytes; the widest
  * access that alignment and the row sizes allow is chosen internally.
- * src and dst must not overlap.  B, H, D >= 1 (B = 0 or S = 0: no work).
- * Returns UAA_OK, UAA_ERR_INVALID_ARG, or UAA_ERR_HIP.
+ * src and dst must not overlap.  H, D >= 1, B >= 0 (B = 0 or an empty
+ * destination: no work, pointers unchecked).  S < 2^31; one source shard
+ * may move fewer than 2^31 access-width elements (else
+ * UAA_ERR_UNSUPPORTED); B <= 65535.
+ * Returns UAA_OK, UAA_ERR_INVALID_ARG, UAA_ERR_UNSUPPORTED or UAA_ERR_HIP.
  */
 int uaa_seq2head_permute(int dir, int rank, int world,
                          const int64_t* seq_off, const int64_t* head_off,
                          int64_t B, int64_t H, int64_t D, int elem_bytes,
                          const void* const* src, void* dst, void* stream);
+
+/*
+ * uaa_seq2head_permute_multi -- the same layout change for n_tensors tensors
+ * of identical shape in one launch (Q, K and V of a layer move together, so
+ * one launch replaces three and the fixed per-launch cost is paid once).
+ *
+ *   src  host array of n_tensors * world device pointers, tensor t's shard
+ *        y at src[t * world + y] (shapes as for uaa_seq2head_permute)
+ *   dst  host array of n_tensors device pointers
+ * Every other argument is shared and means what it means above.  Limits:
+ * 1 <= n_tensors <= UAA_MAX_PERMUTE_TENSORS, n_tensors * world <= 64,
+ * B * n_tensors <= 65535.  The result equals n_tensors separate calls.
+ * Returns UAA_OK, UAA_ERR_INVALID_ARG, UAA_ERR_UNSUPPORTED or UAA_ERR_HIP.
+ */
+int uaa_seq2head_permute_multi(int n_tensors, int dir, int rank, int world,
+                               const int64_t* seq_off, const int64_t* head_off,
+                               int64_t B, int64_t H, int64_t D, int elem_bytes,
+                               const void* const* src, void* const* dst, void* stream);
 
 /*
  * usp_attn_fwd_lse -- softmax attention of one rank's query rows against

@@ -31,4 +31,6 @@ from .binding import (  # noqa: F401
     usp_lse_merge,
     usp_mask,
     uaa_seq2head_permute,
+    uaa_seq2head_permute_multi,
+    UAA_MAX_PERMUTE_TENSORS,
 )

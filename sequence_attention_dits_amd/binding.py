@@ -30,6 +30,7 @@ UAA_SEQ2HEAD = 0
 UAA_HEAD2SEQ = 1
 UAA_MAX_WORLD = 64
 USP_MAX_PARTS = 16
+UAA_MAX_PERMUTE_TENSORS = 4
 USP_MASK_FULL = 0
 USP_MASK_CAUSAL = 1
 USP_MASK_ZIGZAG = 2
@@ -98,6 +99,9 @@ def lib() -> ctypes.CDLL:
         l.uaa_seq2head_permute.restype = ctypes.c_int
         l.uaa_seq2head_permute.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_p, _c_p,
                                            _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_p, _c_p, _c_p]
+        l.uaa_seq2head_permute_multi.restype = ctypes.c_int
+        l.uaa_seq2head_permute_multi.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_p,
+                                                 _c_p, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_p, _c_p, _c_p]
         l.usp_attn_fwd_lse.restype = ctypes.c_int
         l.usp_attn_fwd_lse.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                        _c_p, _c_p, _c_p, _c_p, ctypes.c_int, _c_p,
@@ -141,14 +145,8 @@ def _i64_array(vals):
     return (ctypes.c_int64 * len(vals))(*[int(x) for x in vals])
 
 
-def uaa_seq2head_permute(direction: int, rank: int, src: Sequence[torch.Tensor], dst: torch.Tensor,
-                         seq_off: Sequence[int], head_off: Optional[Sequence[int]] = None) -> None:
-    """Ulysses layout change for one rank (include/uaa.h).
-
-    SEQ2HEAD: src[p] [B,S_p,H,D] -> dst [B,S,H_r,D] for head rank `rank`.
-    HEAD2SEQ: src[r] [B,S,H_r,D] -> dst [B,S_p,H,D] for token rank `rank`.
-    Any element dtype; bits are copied unchanged.
-    """
+def _permute_shapes(direction, rank, src, dst, seq_off, head_off):
+    """Check one tensor's shard shapes against the offsets; returns (B, H, D, head offsets)."""
     world = len(src)
     if len(seq_off) != world + 1:
         raise ValueError("seq_off needs world+1 entries")
@@ -157,7 +155,7 @@ def uaa_seq2head_permute(direction: int, rank: int, src: Sequence[torch.Tensor],
         _dev(x, "src")
         if x.dtype != dst.dtype or x.device != dst.device:
             raise ValueError("src and dst must share dtype and device")
-    if dst.dim() != 4:
+    if dst.dim() != 4 or any(x.dim() != 4 for x in src):
         raise ValueError("tensors are [B, S, H, D]")
     B, D = dst.shape[0], dst.shape[3]
     S = int(seq_off[-1])
@@ -188,10 +186,44 @@ def uaa_seq2head_permute(direction: int, rank: int, src: Sequence[torch.Tensor],
                 raise ValueError("src[%d] shape %s does not match the offsets" % (r, tuple(x.shape)))
         if tuple(dst.shape) != (B, seq_off[rank + 1] - seq_off[rank], H, D):
             raise ValueError("dst shape %s does not match the offsets" % (tuple(dst.shape),))
-    ptrs = (ctypes.c_void_p * world)(*[x.data_ptr() if x.numel() else 0 for x in src])
-    _check(lib().uaa_seq2head_permute(direction, rank, world, _i64_array(seq_off),
+    return B, H, D, hoff
+
+
+def uaa_seq2head_permute(direction: int, rank: int, src: Sequence[torch.Tensor], dst: torch.Tensor,
+                         seq_off: Sequence[int], head_off: Optional[Sequence[int]] = None) -> None:
+    """Ulysses layout change for one rank (include/uaa.h).
+
+    SEQ2HEAD: src[p] [B,S_p,H,D] -> dst [B,S,H_r,D] for head rank `rank`.
+    HEAD2SEQ: src[r] [B,S,H_r,D] -> dst [B,S_p,H,D] for token rank `rank`.
+    Any element dtype; bits are copied unchanged.
+    """
+    B, H, D, hoff = _permute_shapes(direction, rank, src, dst, seq_off, head_off)
+    ptrs = (ctypes.c_void_p * len(src))(*[x.data_ptr() if x.numel() else 0 for x in src])
+    _check(lib().uaa_seq2head_permute(direction, rank, len(src), _i64_array(seq_off),
                                       _i64_array(hoff), B, H, D, dst.element_size(), ptrs,
                                       dst.data_ptr() if dst.numel() else 0, _stream(dst)))
+
+
+def uaa_seq2head_permute_multi(direction: int, rank: int, srcs: Sequence[Sequence[torch.Tensor]],
+                               dsts: Sequence[torch.Tensor], seq_off: Sequence[int],
+                               head_off: Optional[Sequence[int]] = None) -> None:
+    """The same layout change for several same-shaped tensors (e.g. Q, K, V)
+    in one launch: srcs[t] are tensor t's shards, dsts[t] its destination."""
+    if len(srcs) != len(dsts) or not dsts:
+        raise ValueError("need one source list per destination")
+    shapes = None
+    for src, dst in zip(srcs, dsts):
+        got = _permute_shapes(direction, rank, src, dst, seq_off, head_off)
+        if shapes is not None and (got != shapes or dst.dtype != dsts[0].dtype or dst.shape != dsts[0].shape):
+            raise ValueError("all tensors of one call must share shapes and dtype")
+        shapes = got
+    B, H, D, hoff = shapes
+    flat = [x for src in srcs for x in src]
+    ptrs = (ctypes.c_void_p * len(flat))(*[x.data_ptr() if x.numel() else 0 for x in flat])
+    dptrs = (ctypes.c_void_p * len(dsts))(*[d.data_ptr() if d.numel() else 0 for d in dsts])
+    _check(lib().uaa_seq2head_permute_multi(len(dsts), direction, rank, len(srcs[0]), _i64_array(seq_off),
+                                            _i64_array(hoff), B, H, D, dsts[0].element_size(), ptrs, dptrs,
+                                            _stream(dsts[0])))
 
 
 def usp_attn_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,

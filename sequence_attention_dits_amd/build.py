@@ -53,6 +53,13 @@ def build_library(jobs: int = 8, verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
+    # every kernel the library launches must be defined in it: an undefined
+    # kernel symbol would only surface when the library is loaded
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [line for line in nm.stdout.splitlines() if "uaa" in line]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("libuaa.so has undefined symbols of its own:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -48,14 +48,20 @@ UAA_EXPORT const char* uaa_last_error(void) { return g_err; }
 
 UAA_EXPORT int uaa_abi_version(void) { return 1; }
 
-UAA_EXPORT int uaa_seq2head_permute(int dir, int rank, int world, const int64_t* seq_off,
-                                    const int64_t* head_off, int64_t B, int64_t H, int64_t D,
-                                    int elem_bytes, const void* const* src, void* dst, void* stream)
+namespace {
+
+// Shared by the single- and multi-tensor permute entry points.
+int permute_impl(int n_tensors, int dir, int rank, int world, const int64_t* seq_off,
+                 const int64_t* head_off, int64_t B, int64_t H, int64_t D, int elem_bytes,
+                 const void* const* src, void* const* dst, void* stream)
 {
     if (dir != UAA_SEQ2HEAD && dir != UAA_HEAD2SEQ)
         return fail(UAA_ERR_INVALID_ARG, "permute: dir must be UAA_SEQ2HEAD or UAA_HEAD2SEQ, got %d", dir);
     if (world < 1 || world > UAA_MAX_WORLD)
         return fail(UAA_ERR_INVALID_ARG, "permute: world must be in [1, %d], got %d", UAA_MAX_WORLD, world);
+    if (n_tensors < 1 || n_tensors > uaa::kPermMaxTensors || n_tensors * world > uaa::kPermMaxSrc)
+        return fail(UAA_ERR_INVALID_ARG, "permute: need 1 <= n_tensors <= %d and n_tensors * world <= %d",
+                    uaa::kPermMaxTensors, uaa::kPermMaxSrc);
     if (rank < 0 || rank >= world)
         return fail(UAA_ERR_INVALID_ARG, "permute: rank %d outside [0, %d)", rank, world);
     if (B < 0 || H < 1 || D < 1)
@@ -81,56 +87,80 @@ UAA_EXPORT int uaa_seq2head_permute(int dir, int rank, int world, const int64_t*
             return fail(UAA_ERR_INVALID_ARG,
                         "permute: rank %d gets no heads (head_off must strictly increase; world <= H)", p);
     const int64_t S = seq_off[world];
-    if (S > kMaxIdx32 || B * S >= kMaxIdx32 || (double)B * S * H * D * elem_bytes > (double)kMaxElems)
+    if (S >= kMaxIdx32 || H >= kMaxIdx32 || (double)B * S * H * D * elem_bytes > (double)kMaxElems)
         return fail(UAA_ERR_INVALID_ARG, "permute: tensor too large");
-    if (src == nullptr) return fail(UAA_ERR_INVALID_ARG, "permute: src array is NULL");
+    if (src == nullptr || dst == nullptr) return fail(UAA_ERR_INVALID_ARG, "permute: src or dst array is NULL");
 
-    const int64_t Hr = hoff[rank + 1] - hoff[rank];
     const int64_t Sp = seq_off[rank + 1] - seq_off[rank];
     const int64_t out_tokens = dir == UAA_SEQ2HEAD ? S : Sp;
-    const int64_t n_rows = B * out_tokens;
-
-    if (n_rows == 0) return UAA_OK;
+    if (B == 0 || out_tokens == 0) return UAA_OK;
+    if (B * n_tensors > 65535) return fail(UAA_ERR_UNSUPPORTED, "permute: B * n_tensors above 65535");
 
     // Sources that hold data must be present; every pointer must be aligned.
     const int64_t slice = D * elem_bytes;       // bytes of one head of one token
     int vec = 16;
     while (vec > 1 && slice % vec != 0) vec >>= 1;
-    for (int p = 0; p < world; ++p) {
-        // SEQ2HEAD reads every non-empty token shard; HEAD2SEQ every head shard
-        if (dir == UAA_SEQ2HEAD && seq_off[p + 1] == seq_off[p]) continue;
-        if (src[p] == nullptr) return fail(UAA_ERR_INVALID_ARG, "permute: src[%d] is NULL", p);
-        if (!aligned(src[p], elem_bytes))
-            return fail(UAA_ERR_INVALID_ARG, "permute: src[%d] not aligned to %d bytes", p, elem_bytes);
-        while (vec > elem_bytes && !aligned(src[p], vec)) vec >>= 1;
+    for (int t = 0; t < n_tensors; ++t) {
+        for (int p = 0; p < world; ++p) {
+            // SEQ2HEAD reads every non-empty token shard; HEAD2SEQ every head shard
+            if (dir == UAA_SEQ2HEAD && seq_off[p + 1] == seq_off[p]) continue;
+            const void* sp = src[t * world + p];
+            if (sp == nullptr) return fail(UAA_ERR_INVALID_ARG, "permute: src[%d] is NULL", t * world + p);
+            if (!aligned(sp, elem_bytes))
+                return fail(UAA_ERR_INVALID_ARG, "permute: src[%d] not aligned to %d bytes", t * world + p,
+                            elem_bytes);
+            while (vec > elem_bytes && !aligned(sp, vec)) vec >>= 1;
+        }
+        if (dst[t] == nullptr) return fail(UAA_ERR_INVALID_ARG, "permute: dst[%d] is NULL", t);
+        if (!aligned(dst[t], elem_bytes))
+            return fail(UAA_ERR_INVALID_ARG, "permute: dst[%d] not aligned to %d bytes", t, elem_bytes);
+        while (vec > elem_bytes && !aligned(dst[t], vec)) vec >>= 1;
     }
-    if (dst == nullptr) return fail(UAA_ERR_INVALID_ARG, "permute: dst is NULL");
-    if (!aligned(dst, elem_bytes))
-        return fail(UAA_ERR_INVALID_ARG, "permute: dst not aligned to %d bytes", elem_bytes);
-    while (vec > elem_bytes && !aligned(dst, vec)) vec >>= 1;
 
     uaa::PermuteArgs a{};
-    for (int p = 0; p < world; ++p) a.src[p] = static_cast<const unsigned char*>(src[p]);
+    for (int i = 0; i < n_tensors * world; ++i) a.src[i] = static_cast<const unsigned char*>(src[i]);
+    for (int t = 0; t < n_tensors; ++t) a.dst[t] = static_cast<unsigned char*>(dst[t]);
     for (int p = 0; p <= world; ++p) {
-        a.seq_off[p] = seq_off[p];
-        a.head_off[p] = hoff[p];
+        a.seq_off[p] = (int32_t)seq_off[p];
+        a.head_off[p] = (int32_t)hoff[p];
     }
-    a.dst = static_cast<unsigned char*>(dst);
-    a.B = B;
-    a.H = H;
-    a.n_rows = n_rows;
-    a.head_vecs = slice / vec;
+    const int64_t hv = slice / vec;
+    int64_t max_n = 0;
+    for (int y = 0; y < world; ++y) {
+        const int64_t T = dir == UAA_SEQ2HEAD ? seq_off[y + 1] - seq_off[y] : Sp;
+        const int64_t run = (dir == UAA_SEQ2HEAD ? hoff[rank + 1] - hoff[rank] : hoff[y + 1] - hoff[y]) * hv;
+        if (run >= kMaxIdx32 || T * run >= kMaxIdx32 - 4096)
+            return fail(UAA_ERR_UNSUPPORTED, "permute: one shard moves 2^31 or more elements");
+        const uaa::FastDiv f = uaa::make_fastdiv((uint32_t)run);
+        a.run_mul[y] = f.mul;
+        a.run_shift[y] = (uint8_t)f.shift;
+        if (T * run > max_n) max_n = T * run;
+    }
     a.world = world;
     a.rank = rank;
-    const int64_t row_vecs = (dir == UAA_SEQ2HEAD ? Hr : H) * a.head_vecs;
-    if (row_vecs >= kMaxIdx32) return fail(UAA_ERR_INVALID_ARG, "permute: rows too long");
-    a.row_vecs = (int32_t)row_vecs;
-    int lg = 0;
-    while ((int64_t(1) << lg) < row_vecs && lg < 6) ++lg;
-    a.lanes_per_row_log2 = lg;
-    a.div_tokens = uaa::make_fastdiv((uint32_t)out_tokens);
-    a.div_head = uaa::make_fastdiv((uint32_t)a.head_vecs);
-    return hip_status(uaa::launch_permute(dir, vec, a, static_cast<hipStream_t>(stream)), "permute launch");
+    a.n_tensors = n_tensors;
+    a.head_vecs = (int32_t)hv;
+    a.H = (int32_t)H;
+    a.max_rows_x_run = (int32_t)max_n;
+    return hip_status(uaa::launch_permute(dir, vec, a, B, static_cast<hipStream_t>(stream)), "permute launch");
+}
+
+}  // namespace
+
+UAA_EXPORT int uaa_seq2head_permute(int dir, int rank, int world, const int64_t* seq_off,
+                                    const int64_t* head_off, int64_t B, int64_t H, int64_t D,
+                                    int elem_bytes, const void* const* src, void* dst, void* stream)
+{
+    void* dsts[1] = {dst};
+    return permute_impl(1, dir, rank, world, seq_off, head_off, B, H, D, elem_bytes, src, dsts, stream);
+}
+
+UAA_EXPORT int uaa_seq2head_permute_multi(int n_tensors, int dir, int rank, int world, const int64_t* seq_off,
+                                          const int64_t* head_off, int64_t B, int64_t H, int64_t D,
+                                          int elem_bytes, const void* const* src, void* const* dst,
+                                          void* stream)
+{
+    return permute_impl(n_tensors, dir, rank, world, seq_off, head_off, B, H, D, elem_bytes, src, dst, stream);
 }
 
 namespace {
@@ -229,10 +259,8 @@ UAA_EXPORT int usp_attn_fwd_lse(int dtype, int64_t B, int64_t H, int64_t Sq, int
     }
     if (dtype == UAA_BF16 && ((double)(Sq > Sk ? Sq : Sk) * H * D * 2 >= 4294967296.0))
         return fail(UAA_ERR_UNSUPPORTED, "attn: one batch of q or k/v must stay below 4 GiB");
-    const int64_t bm = dtype == UAA_BF16 ? 128 : 64;
-    const int64_t n_qtiles = (Sq + bm - 1) / bm;
-    if (n_qtiles * H * B >= kMaxIdx32) return fail(UAA_ERR_INVALID_ARG, "attn: grid too large");
-    a.n_qtiles = (int32_t)n_qtiles;
+    // the launcher sets the q-tile count for its tile height; bound the grid here
+    if (((Sq + 63) / 64) * H * B >= kMaxIdx32) return fail(UAA_ERR_INVALID_ARG, "attn: grid too large");
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == UAA_BF16) return hip_status(uaa::launch_attn_bf16((int)D, o_dtype, a, s), "attn launch");
     return hip_status(uaa::launch_attn_fp32((int)D, a, s), "attn launch");

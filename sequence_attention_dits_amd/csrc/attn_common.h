@@ -32,6 +32,15 @@ __device__ __forceinline__ void pos_range(const PosMap& m, int64_t lo, int64_t h
     }
 }
 
+// Number of leading indices of the piece base + stride * idx (idx < n,
+// stride >= 1) whose position is <= q: the allowed prefix of that piece.
+__device__ __forceinline__ int64_t allowed_prefix(int64_t base, int64_t stride, int64_t q, int64_t n)
+{
+    if (n <= 0 || q < base) return 0;
+    const int64_t c = (stride == 1 ? (q - base) : (q - base) / stride) + 1;
+    return c < n ? c : n;
+}
+
 // Workgroup index -> (q tile, head, batch).  Workgroups are handed to the
 // 8 XCDs round-robin, and each XCD has its own L2: renumber so that each XCD
 // gets one contiguous run of logical tiles, i.e. the q tiles of the same head

@@ -128,8 +128,10 @@ __global__ __launch_bounds__(256) void attn_fp32_kernel(const AttnArgs a)
     if (part == 0) a.lse[(b * Sq + i) * H + hh] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
-hipError_t launch_attn_fp32(int D, const AttnArgs& a, hipStream_t s)
+hipError_t launch_attn_fp32(int D, const AttnArgs& a0, hipStream_t s)
 {
+    AttnArgs a = a0;
+    a.n_qtiles = (int32_t)((a.Sq + 63) / 64);
     const int64_t blocks = (int64_t)a.n_qtiles * a.H * a.B;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;

@@ -20,9 +20,11 @@ inline hipError_t launch_kernel(void (*kern)(Arg), dim3 grid, dim3 block, size_t
 }
 
 // --------------------------------------------------------------------------
-// Permute: arguments after host validation.  Offsets are in tokens / heads;
-// `vec_bytes` is the access width chosen on the host (1, 2, 4, 8 or 16),
-// and every row, head slice and pointer is a multiple of it.
+// Permute: arguments after host validation.  Offsets are in tokens / heads
+// (< 2^31); `vec_bytes` is the access width chosen on the host (1, 2, 4, 8
+// or 16), and every head slice and pointer is a multiple of it.  The launch
+// grid is (row chunks, source rank, batch * tensor); source y contributes
+// T_y rows of run_y vectors.
 // --------------------------------------------------------------------------
 struct FastDiv {  // n / d for 0 <= n < 2^31, d >= 1, via one mul-hi and a shift
     uint32_t mul;
@@ -31,22 +33,23 @@ struct FastDiv {  // n / d for 0 <= n < 2^31, d >= 1, via one mul-hi and a shift
 };
 FastDiv make_fastdiv(uint32_t d);
 
+constexpr int kPermMaxSrc = 64;       // tensors * world source pointers
+constexpr int kPermMaxTensors = UAA_MAX_PERMUTE_TENSORS;
+
 struct PermuteArgs {
-    const unsigned char* src[UAA_MAX_WORLD];
-    int64_t seq_off[UAA_MAX_WORLD + 1];
-    int64_t head_off[UAA_MAX_WORLD + 1];
-    unsigned char* dst;
-    int64_t B, H;
-    int64_t n_rows;       // destination rows (b, token) to produce
-    int64_t head_vecs;    // vectors per head slice (D * elem_bytes / vec_bytes)
-    int32_t world, rank;
-    int32_t row_vecs;     // vectors per destination row
-    int32_t lanes_per_row_log2;
-    FastDiv div_tokens;   // destination tokens per batch (S or S_p)
-    FastDiv div_head;     // head_vecs, for HEAD2SEQ
+    const unsigned char* src[kPermMaxSrc];   // [tensor * world + y]
+    unsigned char* dst[kPermMaxTensors];
+    int32_t seq_off[UAA_MAX_WORLD + 1];
+    int32_t head_off[UAA_MAX_WORLD + 1];
+    uint32_t run_mul[UAA_MAX_WORLD];         // n / run_y as mul-hi + shift (mul 0: shift only)
+    uint8_t run_shift[UAA_MAX_WORLD];
+    int32_t world, rank, n_tensors;
+    int32_t head_vecs;                       // vectors per head slice of one token
+    int32_t H;
+    int32_t max_rows_x_run;                  // max_y T_y * run_y, sizes grid x
 };
 
-hipError_t launch_permute(int dir, int vec_bytes, const PermuteArgs& a, hipStream_t s);
+hipError_t launch_permute(int dir, int vec_bytes, const PermuteArgs& a, int64_t B, hipStream_t s);
 
 // --------------------------------------------------------------------------
 // Merge.
@@ -84,7 +87,7 @@ struct AttnArgs {
     float scale_log2;     // scale * log2(e)
     int32_t masked;       // 0: every key allowed; 1: kpos(j) <= qpos(i)
     PosMap qmap, kmap;
-    int32_t n_qtiles;     // ceil(Sq / rows per workgroup)
+    int32_t n_qtiles;     // ceil(Sq / rows per workgroup), set by the launcher
 };
 
 hipError_t launch_attn_bf16(int D, int o_dtype, const AttnArgs& a, hipStream_t s);

@@ -98,78 +98,87 @@ template <> struct Slice<float, 1> {              // fp32, any D
 
 // A row's D / VEC slices are spread over `lpr` lanes (a power of two, at most
 // 64; lanes loop when a row has more slices), so a wavefront covers 64 / lpr
-// rows and no lane index needs a division.
-template <typename TIn, typename TOut, int VEC, int NMAX>
+// rows side by side and no lane index needs a division.  Each lane group
+// handles RU rows per pass: the O slices of all partials of all RU rows are
+// loaded first (they do not depend on the LSEs), then the LSEs, then the
+// weights and the weighted sums.
+template <typename TIn, typename TOut, int VEC, int NMAX, int RU>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a, int lpr_log2)
 {
     const int lane = threadIdx.x & 63;
     const int lpr = 1 << lpr_log2;
+    const int groups = 64 >> lpr_log2;
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    const int64_t row = wave * (64 >> lpr_log2) + (lane >> lpr_log2);
-    if (row >= a.rows) return;
+    const int64_t row0 = wave * groups * RU + (lane >> lpr_log2);
     const int N = a.n_parts;
     const int slices = a.D / VEC;              // host guarantees divisibility
 
-    float lse[NMAX];
-    float M = -INFINITY;
-#pragma unroll
-    for (int n = 0; n < NMAX; ++n) {
-        lse[n] = (n < N) ? a.lse_parts[n][row] : -INFINITY;
-        M = fmaxf(M, lse[n]);
-    }
-    float L = -INFINITY;
-    float w[NMAX];
-    if (M != -INFINITY) {
-        float sum = 0.f;
-#pragma unroll
-        for (int n = 0; n < NMAX; ++n)
-            if (n < N) sum += __expf(lse[n] - M);
-        L = M + __logf(sum);
-    }
-#pragma unroll
-    for (int n = 0; n < NMAX; ++n) w[n] = (n < N && M != -INFINITY) ? __expf(lse[n] - L) : 0.f;
-
     for (int seg = lane & (lpr - 1); seg < slices; seg += lpr) {
-        const int64_t elem = row * a.D + (int64_t)seg * VEC;
-        float acc[VEC];
+        float x[RU][NMAX][VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-        if (M != -INFINITY) {
-            // every partial slice is loaded before any arithmetic
-            float x[NMAX][VEC];
+        for (int u = 0; u < RU; ++u) {
+            const int64_t row = row0 + (int64_t)u * groups;
+            if (row < a.rows) {
+                const int64_t elem = row * a.D + (int64_t)seg * VEC;
 #pragma unroll
-            for (int n = 0; n < NMAX; ++n)
-                if (n < N)
-                    Slice<TIn, VEC>::load(reinterpret_cast<const TIn*>(a.o_parts[n]) + elem, x[n]);
-#pragma unroll
-            for (int n = 0; n < NMAX; ++n)
-                if (n < N) {
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) acc[e] = fmaf(w[n], x[n][e], acc[e]);
-                }
+                for (int n = 0; n < NMAX; ++n)
+                    if (n < N) Slice<TIn, VEC>::load(reinterpret_cast<const TIn*>(a.o_parts[n]) + elem, x[u][n]);
+            }
         }
-        Slice<TOut, VEC>::store(reinterpret_cast<TOut*>(a.o_out) + elem, acc);
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+            const int64_t row = row0 + (int64_t)u * groups;
+            if (row >= a.rows) continue;
+            float lse[NMAX];
+            float M = -INFINITY;
+#pragma unroll
+            for (int n = 0; n < NMAX; ++n) {
+                lse[n] = (n < N) ? a.lse_parts[n][row] : -INFINITY;
+                M = fmaxf(M, lse[n]);
+            }
+            float acc[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+            float L = -INFINITY;
+            if (M != -INFINITY) {
+                float sum = 0.f;
+#pragma unroll
+                for (int n = 0; n < NMAX; ++n)
+                    if (n < N) sum += __expf(lse[n] - M);
+                L = M + __logf(sum);
+#pragma unroll
+                for (int n = 0; n < NMAX; ++n)
+                    if (n < N) {
+                        const float w = __expf(lse[n] - L);
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) acc[e] = fmaf(w, x[u][n][e], acc[e]);
+                    }
+            }
+            const int64_t elem = row * a.D + (int64_t)seg * VEC;
+            Slice<TOut, VEC>::store(reinterpret_cast<TOut*>(a.o_out) + elem, acc);
+            if (seg == 0) a.lse_out[row] = L;
+        }
     }
-    if ((lane & (lpr - 1)) == 0) a.lse_out[row] = L;
 }
 
 template <typename TIn, typename TOut, int VEC>
 static hipError_t launch_vec(const MergeArgs& a, hipStream_t s)
 {
+    constexpr int RU = 1;   // measured: one row per lane group per pass is fastest
     const int slices = a.D / VEC;
     int lpr_log2 = 0;
     while ((1 << lpr_log2) < slices && lpr_log2 < 6) ++lpr_log2;
-    const int64_t rows_per_block = 4 * (64 >> lpr_log2);
+    const int64_t rows_per_block = 4 * (64 >> lpr_log2) * RU;
     const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks), block(256);
     void* params[] = {const_cast<MergeArgs*>(&a), &lpr_log2};
     const void* fn;
-    if (a.n_parts <= 2) fn = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, VEC, 2>);
-    else if (a.n_parts <= 4) fn = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, VEC, 4>);
-    else if (a.n_parts <= 8) fn = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, VEC, 8>);
-    else fn = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, VEC, 16>);
+    if (a.n_parts <= 2) fn = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, VEC, 2, RU>);
+    else if (a.n_parts <= 4) fn = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, VEC, 4, RU>);
+    else if (a.n_parts <= 8) fn = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, VEC, 8, RU>);
+    else fn = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, VEC, 16, RU>);
     return hipLaunchKernel(fn, grid, block, params, 0, s);
 }
 

@@ -3,16 +3,23 @@
 // "Context parallelism" (diffusers docs), "Ulysses Attention": the first
 // all-to-all leaves each GPU every token of a subset of heads, the second
 // regroups by token.  "Ulysses Anything Attention": token and head counts per
-// rank are arbitrary and nothing is padded, so the owner of a token (or a
-// head) is found from prefix sums instead of a division by the degree.
+// rank are arbitrary and nothing is padded, so row ranges come from prefix
+// sums instead of a division by the degree.
 //
-// The copy is HBM-bound: every destination row (one token of one batch) is a
-// run of contiguous bytes gathered from one source row (SEQ2HEAD) or from one
-// slice of each head shard (HEAD2SEQ).  A wavefront owns a few destination
-// rows at a time; its lanes stride along each row with the widest access the
-// alignment allows (16 bytes for bf16 rows of 128-wide heads), all loads of a
-// pass are issued before any store so many bytes are in flight per CU, and
-// both sides use non-temporal accesses since nothing is reused.
+// Both directions are a set of 2-D strided copies, one per source rank y
+// (and per tensor and batch when several are moved in one launch):
+//   SEQ2HEAD  source = token shard y: its S_y rows, each the run of this
+//             rank's H_r heads (a contiguous slice of the source row), land
+//             at destination rows seq_off[y] .. seq_off[y+1]-1;
+//   HEAD2SEQ  source = head shard y: this rank's S_p rows of it, each a run
+//             of H_y heads, land at head columns head_off[y] .. of the
+//             destination rows.
+// The launch grid is (chunks, source y, batch * tensor), so every base
+// pointer, stride and run length is uniform in a workgroup (scalar
+// registers); inside a chunk each lane moves U 16-byte vectors of the
+// flattened (row, column) space, loads issued before stores, with
+// non-temporal accesses on both sides since nothing is reused.  The row of a
+// vector comes from one multiply-high by a host-computed reciprocal.
 #include "internal.h"
 
 namespace uaa {
@@ -37,105 +44,64 @@ FastDiv make_fastdiv(uint32_t d)
     return f;
 }
 
-__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f)
-{
-    return f.mul == 0 ? (n >> f.shift) : (__umulhi(n, f.mul) >> f.shift);
-}
-
-// Last index p in [0, world) with off[p] <= x (the rank owning x; with empty
-// ranks several share one offset and the last of them owns the range).
-__device__ __forceinline__ int owner(const int64_t* off, int world, int64_t x)
-{
-    int lo = 0, hi = world - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= x) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
 template <typename V>
 __device__ __forceinline__ V ld_nt(const V* p) { return __builtin_nontemporal_load(p); }
 template <typename V>
 __device__ __forceinline__ void st_nt(V* p, V x) { __builtin_nontemporal_store(x, p); }
 
-constexpr int kWaves = 4;     // wavefronts per workgroup
-constexpr int kRowsUnroll = 2; // destination rows per lane group per pass
-constexpr int kVecUnroll = 4;  // vectors per lane per row per pass
+constexpr int kThreads = 256;
+constexpr int kVecPerThread = 2;   // vectors in flight per lane
 
 template <int DIR, typename V>
-__global__ __launch_bounds__(64 * kWaves) void permute_kernel(const PermuteArgs a)
+__global__ __launch_bounds__(kThreads) void permute_kernel(const PermuteArgs a)
 {
-    const int lane = threadIdx.x & 63;
-    const int lpr_log2 = a.lanes_per_row_log2;
-    const int lpr = 1 << lpr_log2;
-    const int groups = 64 >> lpr_log2;         // rows side by side in a wave
-    const int sub = lane >> lpr_log2;
-    const int sublane = lane & (lpr - 1);
-    const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    const int64_t row0 = wave * (int64_t)(groups * kRowsUnroll);
+    const int y = blockIdx.y;
+    const int tensor = (int)(blockIdx.z % (uint32_t)a.n_tensors);
+    const int64_t b = blockIdx.z / (uint32_t)a.n_tensors;
+    const int64_t hv = a.head_vecs;
+    const int64_t S = a.seq_off[a.world];
 
-    const V* const* src = reinterpret_cast<const V* const*>(a.src);
-    V* dst = reinterpret_cast<V*>(a.dst);
-    const int64_t row_vecs = a.row_vecs;
-
-    bool live[kRowsUnroll];
-    const V* srow[kRowsUnroll];     // SEQ2HEAD: start of the source run
-    int64_t stok[kRowsUnroll];      // HEAD2SEQ: token index inside each head shard
-    V* drow[kRowsUnroll];
-#pragma unroll
-    for (int u = 0; u < kRowsUnroll; ++u) {
-        const int64_t row = row0 + (int64_t)u * groups + sub;
-        live[u] = row < a.n_rows;
-        const int64_t r = live[u] ? row : 0;
-        const uint32_t b = fast_div((uint32_t)r, a.div_tokens);
-        const int64_t tok = r - (int64_t)b * a.div_tokens.d;
-        drow[u] = dst + r * row_vecs;
-        if (DIR == UAA_SEQ2HEAD) {
-            // token tok of the global sequence lives in shard p at tok - off[p]
-            const int p = owner(a.seq_off, a.world, tok);
-            const int64_t Sp = a.seq_off[p + 1] - a.seq_off[p];
-            const int64_t srow_idx = ((int64_t)b * Sp + (tok - a.seq_off[p])) * a.H + a.head_off[a.rank];
-            srow[u] = src[p] + srow_idx * a.head_vecs;
-            stok[u] = 0;
-        } else {
-            const int64_t S = a.seq_off[a.world];
-            stok[u] = (int64_t)b * S + a.seq_off[a.rank] + tok;
-            srow[u] = nullptr;
-        }
+    // uniform description of this source's copy
+    int64_t T, run, src_stride, src_col0, src_row0, dst_stride, dst_col0, dst_row0;
+    if (DIR == UAA_SEQ2HEAD) {
+        T = a.seq_off[y + 1] - a.seq_off[y];
+        run = (int64_t)(a.head_off[a.rank + 1] - a.head_off[a.rank]) * hv;
+        src_stride = a.H * hv;
+        src_col0 = a.head_off[a.rank] * hv;
+        src_row0 = b * T;
+        dst_stride = run;
+        dst_col0 = 0;
+        dst_row0 = b * S + a.seq_off[y];
+    } else {
+        T = a.seq_off[a.rank + 1] - a.seq_off[a.rank];
+        run = (int64_t)(a.head_off[y + 1] - a.head_off[y]) * hv;
+        src_stride = run;
+        src_col0 = 0;
+        src_row0 = b * S + a.seq_off[a.rank];
+        dst_stride = a.H * hv;
+        dst_col0 = a.head_off[y] * hv;
+        dst_row0 = b * T;
     }
+    const uint32_t n = (uint32_t)(T * run);           // < 2^31, checked on the host
+    const uint32_t base = blockIdx.x * (uint32_t)(kThreads * kVecPerThread);
+    if (base >= n) return;
+    const V* src = reinterpret_cast<const V*>(a.src[tensor * a.world + y]) + src_row0 * src_stride + src_col0;
+    V* dst = reinterpret_cast<V*>(a.dst[tensor]) + dst_row0 * dst_stride + dst_col0;
+    const uint32_t mul = a.run_mul[y], shift = a.run_shift[y];
 
-    for (int64_t c0 = 0; c0 < row_vecs; c0 += (int64_t)kVecUnroll * lpr) {
-        V tmp[kRowsUnroll][kVecUnroll];
+    V tmp[kVecPerThread];
+    uint32_t row[kVecPerThread], col[kVecPerThread];
 #pragma unroll
-        for (int u = 0; u < kRowsUnroll; ++u) {
+    for (int u = 0; u < kVecPerThread; ++u) {
+        const uint32_t f = base + threadIdx.x + u * kThreads;
+        row[u] = mul == 0 ? (f >> shift) : (__umulhi(f, mul) >> shift);
+        col[u] = f - row[u] * (uint32_t)run;
+        if (f < n) tmp[u] = ld_nt(src + (int64_t)row[u] * src_stride + col[u]);
+    }
 #pragma unroll
-            for (int k = 0; k < kVecUnroll; ++k) {
-                const int64_t vi = c0 + (int64_t)k * lpr + sublane;
-                if (live[u] && vi < row_vecs) {
-                    if (DIR == UAA_SEQ2HEAD) {
-                        tmp[u][k] = ld_nt(srow[u] + vi);
-                    } else {
-                        // head h of the destination row comes from the shard
-                        // whose head range contains h
-                        const uint32_t h = fast_div((uint32_t)vi, a.div_head);
-                        const int64_t e = vi - (int64_t)h * a.head_vecs;
-                        const int r = owner(a.head_off, a.world, h);
-                        const int64_t Hr = a.head_off[r + 1] - a.head_off[r];
-                        const int64_t off = (stok[u] * Hr + ((int64_t)h - a.head_off[r])) * a.head_vecs + e;
-                        tmp[u][k] = ld_nt(src[r] + off);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kRowsUnroll; ++u) {
-#pragma unroll
-            for (int k = 0; k < kVecUnroll; ++k) {
-                const int64_t vi = c0 + (int64_t)k * lpr + sublane;
-                if (live[u] && vi < row_vecs) st_nt(drow[u] + vi, tmp[u][k]);
-            }
-        }
+    for (int u = 0; u < kVecPerThread; ++u) {
+        const uint32_t f = base + threadIdx.x + u * kThreads;
+        if (f < n) st_nt(dst + (int64_t)row[u] * dst_stride + col[u], tmp[u]);
     }
 }
 
@@ -143,15 +109,14 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 template <int DIR>
-static hipError_t launch_dir(int vec_bytes, const PermuteArgs& a, hipStream_t s)
+static hipError_t launch_dir(int vec_bytes, const PermuteArgs& a, int64_t B, hipStream_t s)
 {
-    const int groups = 64 >> a.lanes_per_row_log2;
-    const int64_t rows_per_wave = (int64_t)groups * kRowsUnroll;
-    const int64_t waves = (a.n_rows + rows_per_wave - 1) / rows_per_wave;
-    const int64_t blocks = (waves + kWaves - 1) / kWaves;
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)blocks), block(64 * kWaves);
+    const int64_t chunk = kThreads * kVecPerThread;
+    const int64_t gx = ((int64_t)a.max_rows_x_run + chunk - 1) / chunk;
+    const int64_t gz = B * a.n_tensors;
+    if (gx <= 0 || gz <= 0) return hipSuccess;
+    if (gx > 0x7fffffff || gz > 65535) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)gx, (unsigned)a.world, (unsigned)gz), block(kThreads);
     switch (vec_bytes) {
     case 16: return launch_kernel(permute_kernel<DIR, u32x4>, grid, block, 0, s, a);
     case 8: return launch_kernel(permute_kernel<DIR, u32x2>, grid, block, 0, s, a);
@@ -162,10 +127,10 @@ static hipError_t launch_dir(int vec_bytes, const PermuteArgs& a, hipStream_t s)
     }
 }
 
-hipError_t launch_permute(int dir, int vec_bytes, const PermuteArgs& a, hipStream_t s)
+hipError_t launch_permute(int dir, int vec_bytes, const PermuteArgs& a, int64_t B, hipStream_t s)
 {
-    return dir == UAA_SEQ2HEAD ? launch_dir<UAA_SEQ2HEAD>(vec_bytes, a, s)
-                               : launch_dir<UAA_HEAD2SEQ>(vec_bytes, a, s);
+    return dir == UAA_SEQ2HEAD ? launch_dir<UAA_SEQ2HEAD>(vec_bytes, a, B, s)
+                               : launch_dir<UAA_HEAD2SEQ>(vec_bytes, a, B, s);
 }
 
 }  // namespace uaa

@@ -165,3 +165,18 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         binding.lib()
+
+
+def test_multi_permute_validation():
+    lib = uaa.lib()
+    src = _ptrs(*([FAKE] * 8))
+    dst = _ptrs(FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert lib.uaa_seq2head_permute_multi(0, 0, 0, 2, _i64(0, 2, 4), None, 1, 2, 8, 2, src, dst, None) == -1
+    assert "n_tensors" in lib.uaa_last_error().decode()
+    assert lib.uaa_seq2head_permute_multi(5, 0, 0, 2, _i64(0, 2, 4), None, 1, 2, 8, 2, src, dst, None) == -1
+    big = _i64(*range(0, 34))   # world 33 with 2 tensors exceeds 64 source pointers
+    assert lib.uaa_seq2head_permute_multi(2, 0, 0, 33, big, None, 1, 40, 8, 2, src, dst, None) == -1
+    assert "n_tensors" in lib.uaa_last_error().decode()
+    dst0 = _ptrs(FAKE, 0)
+    assert lib.uaa_seq2head_permute_multi(2, 0, 0, 2, _i64(0, 2, 4), None, 1, 2, 8, 2, src, dst0, None) == -1
+    assert "dst[1]" in lib.uaa_last_error().decode()

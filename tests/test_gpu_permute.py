@@ -148,3 +148,41 @@ def test_bad_arguments_are_rejected_before_launch():
     y0 = torch.zeros(1, 20, 0, 64, device="cuda", dtype=torch.bfloat16)
     with pytest.raises(uaa.UaaError):        # a rank with no heads
         uaa.uaa_seq2head_permute(uaa.UAA_SEQ2HEAD, 0, [x, x], y0, [0, 10, 20], [0, 0, 4])
+
+
+@pytest.mark.parametrize("direction", [uaa.UAA_SEQ2HEAD, uaa.UAA_HEAD2SEQ])
+@pytest.mark.parametrize("n_t,seq_off,head_off,B,D", [
+    (3, [0, 2304, 4608], [0, 12, 24], 1, 128),
+    (3, [0, 2241, 4481], [0, 12, 24], 1, 128),
+    (4, [0, 5, 5, 40], [0, 1, 3, 5], 2, 64),
+    (2, [0, 100, 130, 131, 300], [0, 3, 4, 6, 9], 3, 128),
+])
+def test_multi_tensor_permute_equals_separate_calls(direction, n_t, seq_off, head_off, B, D):
+    world = len(seq_off) - 1
+    H = head_off[-1]
+    S = seq_off[-1]
+    gen = torch.Generator(device="cpu").manual_seed(n_t * 7 + B)
+    srcs, dsts, refs = [], [], []
+    for t in range(n_t):
+        if direction == uaa.UAA_SEQ2HEAD:
+            src = [torch.randn(B, seq_off[p + 1] - seq_off[p], H, D, generator=gen).to(torch.bfloat16).cuda()
+                   for p in range(world)]
+        else:
+            src = [torch.randn(B, S, head_off[r + 1] - head_off[r], D, generator=gen).to(torch.bfloat16).cuda()
+                   for r in range(world)]
+        srcs.append(src)
+    rank = 1
+    for t in range(n_t):
+        if direction == uaa.UAA_SEQ2HEAD:
+            shape = (B, S, head_off[rank + 1] - head_off[rank], D)
+        else:
+            shape = (B, seq_off[rank + 1] - seq_off[rank], H, D)
+        ref = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        uaa.uaa_seq2head_permute(direction, rank, srcs[t], ref, seq_off, head_off)
+        refs.append(ref)
+        dsts.append(torch.full(shape, 3.0, dtype=torch.bfloat16, device="cuda"))
+    say("permute multi", direction, n_t, seq_off, head_off, B, D)
+    uaa.uaa_seq2head_permute_multi(direction, rank, srcs, dsts, seq_off, head_off)
+    torch.cuda.synchronize()
+    for ref, got in zip(refs, dsts):
+        assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
