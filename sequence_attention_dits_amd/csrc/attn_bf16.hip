@@ -12,12 +12,15 @@
 //  * A workgroup owns 256 query rows of one (batch, head): 8 wavefronts of 32
 //    rows, two per SIMD, so each K/V tile staged in LDS serves 256 rows.  Q
 //    stays in registers.
-//  * K and V stream in tiles of 64 keys through two LDS stages.  K is copied
-//    by buffer loads that write LDS directly (no registers, no store
-//    instructions); V passes through registers, where each lane transposes
-//    an 8-key x 4-feature block so that LDS holds 16-byte units of 8 keys of
-//    one feature.  The loads of tile t+1 are issued before tile t is computed;
-//    one barrier per tile.  Loads past the end of the keys return zeros.
+//  * K and V stream in tiles of 64 keys, issued two tiles ahead of the one
+//    being computed.  K is copied by buffer loads that write LDS directly (no
+//    registers, no store instructions) into three LDS stages.  V passes
+//    through two register sets: each lane loads two keys x 8 features as
+//    16-byte loads that cover whole rows, and writes them transposed into one
+//    of two LDS stages, which hold 16-byte units of 8 keys of one feature.
+//    One barrier per tile; it waits only for the LDS stores and the copies of
+//    the next tile, never for the loads still running.  Loads past the end of
+//    the keys return zeros.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: each lane owns one query row (lane % 32) and 32
 //    of the tile's 64 keys, so the row maximum and sum need one cross-half
@@ -32,12 +35,14 @@
 //    exp2 units (a wave-uniform branch, rare after the first tile); between
 //    raises the exponentials use the stale maximum, which is exact because O
 //    and the sum share it, and stays far from overflow.
-//  * LDS layouts are XOR-swizzled in 16-byte units so operand reads and V
-//    stores are free of bank conflicts.
+//  * K is XOR-swizzled and V padded in 16-byte units so that operand reads
+//    and V stores are free of bank conflicts.
 //  * exp2 with scale * log2(e) folded into one multiply-add; the LSE is
 //    converted back to the natural log at the end.  Rows with no allowed key
 //    give o = 0, lse = -inf.
 #include "attn_common.h"
+
+#include <type_traits>
 
 namespace uaa {
 
@@ -60,6 +65,23 @@ constexpr float kRescaleThreshold = 8.0f;  // in log2 units of the softmax weigh
 __device__ __forceinline__ unsigned int pack_bf16(float lo, float hi)
 {
     return __builtin_bit_cast(unsigned int, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// Workgroup barrier for LDS: global loads and LDS copies still in flight
+// stay in flight (a plain __syncthreads waits for them); the caller waits for
+// the copies it needs with an explicit vmcnt.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS stores are done
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Maximum of three floats (v_maximum3_f32: no NaN quieting of the inputs).
+__device__ __forceinline__ float fmax3(float a, float b, float c)
+{
+    return __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
 }
 
 // Key offset, inside a 16-key chunk, of P operand slot s of lane half h:
@@ -95,9 +117,14 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
     constexpr int NKC = D / 16;              // k-chunks of the score product
     constexpr int NDB = D / 32;              // 32-wide feature blocks of the output
     constexpr int TB = kBN * ROWB;           // bytes of one K or V tile
-    constexpr int VQ = D / 4;                // 4-feature quads per row
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * TB];   // [stage][K, V]
+    // V layout (D = 128): unit group g (8 keys) holds feature f at byte
+    // g * VGS + 16 * f + 16 * (f / 16): one padding unit after every 16
+    // features keeps both the 4-byte stores and the 16-byte operand reads
+    // free of bank conflicts.  D = 64 uses an unpadded XOR-swizzled layout.
+    constexpr int VGS = D == 128 ? (D + D / 16) * 16 : D * 16;   // bytes per unit group
+    constexpr int VTB = 8 * VGS;                                  // bytes of one V stage
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[3 * TB + 2 * VTB];   // K stages 0..2, V stages 0..1
 
     int64_t qt, hh, b;
     decode_tile(a, qt, hh, b);
@@ -113,8 +140,6 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
     const unsigned char* qbase = static_cast<const unsigned char*>(a.q) + ((b * Sq) * H + hh) * D * 2;
     const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + ((b * Sk) * H + hh) * D * 2;
     const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + ((b * Sk) * H + hh) * D * 2;
-    const uint32_t k_bytes = Sk > 0 ? (uint32_t)((Sk - 1) * ld2 + D * 2) : 0u;
-    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, k_bytes, 0x00020000);
 
     // Q operands: lane holds row i, features 16*kc + 8*hg .. +7 (zero past Sq).
     bf16x8 qop[NKC];
@@ -165,42 +190,77 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
         return t;
     };
 
-    // ---- V staging: lane (g, q) = (tid % 8, tid / 8) loads the 8 keys of
-    // unit group g (16*(g/2) + 4*(g%2) + p_slot_key(r), r = 0..7) at features
-    // 4q .. 4q+3, and stores the 4 transposed units (g, 4q + c) at
-    // g * D + ((4q + c) ^ g).
-    const int vg = tid & 7, vq = tid >> 3;
-    const bool v_stager = vq < VQ;
-    const uint32_t v_goff = (uint32_t)(16 * (vg >> 1) + 4 * (vg & 1)) * ld2 + vq * 8;
-    u32x2 vst[8];
-    auto load_v = [&](int t) {
-        if (!v_stager) return;
-        const uint32_t tbase = (uint32_t)t * kBN * ld2;
+    // ---- V staging ---------------------------------------------------------
+    // D = 128: wave w stages unit group g = w.  Lane (i, b) = (lane / 16,
+    // lane % 16) loads keys p_slot_key(2i) and p_slot_key(2i) + 1 of the group
+    // (key 16*(g/2) + 4*(g%2) + p_slot_key(2i)), features 8b .. 8b+7, as two
+    // 16-byte loads that cover four whole rows per instruction, and stores
+    // for each feature the 2-key dword at byte 4i of its unit.
+    // D = 64: lane (g, h, q) = (tid % 8, part, quad) loads KPL = 2 keys x 4
+    // features as 8-byte loads and writes KPL keys of each feature.
+    constexpr int KPL = D == 128 ? 2 : D / 32;   // keys per lane
+    constexpr int VLD = D == 128 ? 4 : 2;        // dwords per V load
+    typedef unsigned int vld_t __attribute__((ext_vector_type(VLD)));
+    vld_t vst[2][KPL];    // two register sets: tiles t+1 and t+2 are in flight
+    uint32_t v_goff, v_soff;   // global byte offset in the tile, LDS byte offset in the stage
+    if constexpr (D == 128) {
+        const int g = wave, vi = lane >> 4, vb = lane & 15;
+        v_goff = (uint32_t)(16 * (g >> 1) + 4 * (g & 1) + p_slot_key(2 * vi)) * ld2 + vb * 16;
+        v_soff = (uint32_t)(g * VGS + 128 * vb + 16 * (vb >> 1) + 4 * vi);
+    } else {
+        constexpr int HPARTS = 8 / KPL;
+        const int vg = tid & 7, vh = (tid >> 3) & (HPARTS - 1), vq = tid / (8 * HPARTS);
+        v_goff = (uint32_t)(16 * (vg >> 1) + 4 * (vg & 1) + p_slot_key(KPL * vh)) * ld2 + vq * 8;
+        v_soff = 0;
+    }
+    // a descriptor per tile (scalar work only) whose range ends at the last key
+    auto load_v = [&](int t, auto set_tag) {
+        constexpr int set = decltype(set_tag)::value;
+        const int64_t j0 = (int64_t)t * kBN;
+        const uint32_t nrec = (uint32_t)((Sk - 1 - j0) * ld2 + D * 2);
+        const __amdgpu_buffer_rsrc_t tr =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + j0 * ld2), (short)0, nrec, 0x00020000);
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            vst[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                   vr, v_goff + tbase + (uint32_t)p_slot_key(r) * ld2, 0, 0));
-    };
-    auto store_v = [&](int st) {
-        if (!v_stager) return;
-        lds_u32x4* V = (lds_u32x4*)(smem + st * 2 * TB + TB);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            // feature 4q + c: dword c/2 of each row, low or high half
-            const int e = c >> 1;
-            const unsigned int sel = (c & 1) ? 0x07060302u : 0x05040100u;
-            u32x4 col;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) col[p] = __builtin_amdgcn_perm(vst[2 * p + 1][e], vst[2 * p][e], sel);
-            V[vg * D + ((4 * vq + c) ^ vg)] = col;
+        for (int r = 0; r < KPL; ++r) {
+            // keys of one lane are consecutive inside each p_slot_key group of 4
+            const uint32_t off = v_goff + (uint32_t)(p_slot_key(r) - p_slot_key(0)) * ld2;
+            if constexpr (VLD == 4)
+                vst[set][r] = __builtin_bit_cast(vld_t, __builtin_amdgcn_raw_buffer_load_b128(tr, off, 0, 0));
+            else
+                vst[set][r] = __builtin_bit_cast(vld_t, __builtin_amdgcn_raw_buffer_load_b64(tr, off, 0, 0));
         }
     };
-    auto issue_tile = [&](int t, int st) {
+    auto store_v = [&](auto set_tag) {   // register set s goes to V stage s
+        constexpr int set = decltype(set_tag)::value;
+        lds_u8* V = (lds_u8*)(smem + 3 * TB + set * VTB) + v_soff;
+        if constexpr (D == 128) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // feature 8b + e: half e%2 of dword e/2 of both keys
+                const unsigned int sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                const unsigned int w = __builtin_amdgcn_perm(vst[set][1][e >> 1], vst[set][0][e >> 1], sel);
+                *(__attribute__((address_space(3))) unsigned int*)(V + 16 * e) = w;
+            }
+        } else {
+            lds_u8* Vs = (lds_u8*)(smem + 3 * TB + set * VTB);
+            const int vg = tid & 7, vh = (tid >> 3) & 3, vq = tid >> 5;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                // feature 4q + c: half c%2 of dword c/2 of each key, in unit (g, (4q + c) ^ g)
+                const int e = c >> 1;
+                const unsigned int sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                *(__attribute__((address_space(3))) unsigned int*)(Vs + (vg * D + ((4 * vq + c) ^ vg)) * 16 + vh * 4) =
+                    __builtin_amdgcn_perm(vst[set][1][e], vst[set][0][e], sel);
+            }
+        }
+    };
+    auto issue_k = [&](int t, int ks) {
         const int64_t j0 = (int64_t)t * kBN;
         const uint32_t nrec = (uint32_t)((Sk - 1 - j0) * ld2 + D * 2);   // bytes of valid rows from j0
-        fill_k<D>(kbase + j0 * ld2, nrec, smem + st * 2 * TB, wave, lane, ld2);
-        load_v(t);
+        fill_k<D>(kbase + j0 * ld2, nrec, smem + ks * TB, wave, lane, ld2);
     };
+    // vector memory operations each wave issues per tile: K copies, V loads
+    constexpr int kVmPerTile = (64 / (1024 / (D * 2))) / kWaves + KPL;
 
     // ---- LDS operand offsets (bytes) -------------------------------------
     // K operand of the score product, block jb, chunk kc: row 32*jb + l32,
@@ -209,12 +269,17 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
     uint32_t kaddr[NKC];
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) kaddr[kc] = l32 * ROWB + (((2 * kc + hg) ^ (l32 & (UPR - 1))) * 16);
+    // V operand, chunk c, feature block db: unit group g = 2c + hg, feature 32*db + l32
     uint32_t vaddr[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int g = 2 * c + hg;
-        vaddr[c] = (uint32_t)(g * D + (l32 ^ g)) * 16;
+        if constexpr (D == 128)
+            vaddr[c] = (uint32_t)(g * VGS + 16 * l32 + 16 * (l32 >> 4));
+        else
+            vaddr[c] = (uint32_t)(g * D + (l32 ^ g)) * 16;
     }
+    constexpr int VDB = D == 128 ? 32 * 16 + 2 * 16 : 512;   // byte step between feature blocks
 
     // ---- per-lane state ---------------------------------------------------
     f32x16 oacc[NDB];
@@ -226,18 +291,37 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
     float lsum = 0.f;      // this lane half's share of the row sum
     const float c2 = a.scale_log2;
 
+    // Loads run two tiles ahead: K through three LDS stages, V through two
+    // register sets and two LDS stages.
     int t = next_live(0);
+    int t1 = t < n_tiles ? next_live(t + 1) : n_tiles;
+    int ks = 0;   // K stage of tile t
     if (t < n_tiles) {
-        issue_tile(t, 0);
-        store_v(0);
+        issue_k(t, 0);
+        load_v(t, std::integral_constant<int, 0>{});
+        if (t1 < n_tiles) {
+            issue_k(t1, 1);
+            load_v(t1, std::integral_constant<int, 1>{});
+        }
+        store_v(std::integral_constant<int, 0>{});
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): the K copy landed
+    __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): every copy issued so far landed
     __syncthreads();
 
-    int st = 0;
-    while (t < n_tiles) {
-        const int tn = next_live(t + 1);
-        if (tn < n_tiles) issue_tile(tn, st ^ 1);
+    // One tile step with the V stage / register set parity P a template
+    // constant.  Returns false after the last live tile.
+    auto step = [&](auto parity_tag) -> bool {
+        constexpr int P = decltype(parity_tag)::value;
+        const int t2 = t1 < n_tiles ? next_live(t1 + 1) : n_tiles;
+        const int ks2 = ks == 0 ? 2 : ks - 1;   // (ks + 2) % 3
+        {
+            // Always issue the copies (of tile t when there is no t2; they
+            // land in buffers nothing reads) so that every wave has exactly
+            // kVmPerTile vector memory operations per step in flight.
+            const int tl = t2 < n_tiles ? t2 : t;
+            issue_k(tl, ks2);
+            load_v(tl, std::integral_constant<int, P>{});
+        }
 
         const int64_t j0 = (int64_t)t * kBN;
         bool any = wave_live, per_elem = j0 + kBN > Sk;
@@ -250,8 +334,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
         }
 
         if (any) {
-            const lds_u8* Kl = (const lds_u8*)(smem + st * 2 * TB);
-            const lds_u8* Vl = Kl + TB;
+            const lds_u8* Kl = (const lds_u8*)(smem + ks * TB);
+            const lds_u8* Vl = (const lds_u8*)(smem + 3 * TB + P * VTB);
 
             // S^T = K Q^T: block jb, register v holds key 32*jb + 8*(v/4) + 4*hg + v%4
             f32x16 sacc[2];
@@ -266,6 +350,14 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
                     const bf16x8 kop = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Kl + kaddr[kc] + jb * 32 * ROWB));
                     sacc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kc], sacc[jb], 0, 0, 0);
                 }
+            // keep 4 operand reads in flight ahead of the matrix instructions
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int r = 0; r < 2 * NKC - 4; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
             if (per_elem) {
 #pragma unroll
@@ -279,16 +371,25 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
             }
 
             // online softmax of row i
-            float mx = -INFINITY;
+            float mx;
+            {
+                // three-input maximum tree over the 32 scores: 16 instructions
+                float r[11];
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(sacc[jb][v], sacc[jb][v + 1]));
+                for (int u = 0; u < 10; ++u) {
+                    const int e0 = 3 * u, e1 = 3 * u + 1, e2 = 3 * u + 2;
+                    r[u] = fmax3(sacc[e0 >> 4][e0 & 15], sacc[e1 >> 4][e1 & 15], sacc[e2 >> 4][e2 & 15]);
+                }
+                r[10] = __builtin_elementwise_maximum(sacc[1][14], sacc[1][15]);
+                const float r0 = fmax3(r[0], r[1], r[2]), r1 = fmax3(r[3], r[4], r[5]);
+                const float r2 = fmax3(r[6], r[7], r[8]), r3 = __builtin_elementwise_maximum(r[9], r[10]);
+                mx = __builtin_elementwise_maximum(fmax3(r0, r1, r2), r3);
+            }
             {
                 const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-                mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
             }
-            const float m_new = fmaxf(m, mx * c2);
+            const float m_new = __builtin_elementwise_maximum(m, mx * c2);
             const bool need = m_new > m + kRescaleThreshold;
             if (__any(need)) {
                 // lanes that keep their maximum (possibly still -inf) scale by 1
@@ -318,19 +419,25 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
                 const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const bf16x8 vop = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Vl + vaddr[c] + db * 512));
+                    const bf16x8 vop = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Vl + vaddr[c] + db * VDB));
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[db], 0, 0, 0);
                 }
             }
             lsum += ps0 + ps1;
         }
 
-        if (tn < n_tiles) store_v(st ^ 1);
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the K copy of the next tile landed
-        __syncthreads();
-        st ^= 1;
-        t = tn;
-    }
+        if (t1 < n_tiles) store_v(std::integral_constant<int, P ^ 1>{});
+        // the K copy of tile t1 must have landed; the copies of this step may still run
+        __builtin_amdgcn_s_waitcnt(0x0F70 | kVmPerTile);
+        lds_barrier();
+        ks = ks == 2 ? 0 : ks + 1;
+        t = t1;
+        t1 = t2;
+        return t < n_tiles;
+    };
+    if (t < n_tiles)
+        while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
+        }
 
     // ---- epilogue: normalise, write O and the natural-log LSE -----------
     float lt;
