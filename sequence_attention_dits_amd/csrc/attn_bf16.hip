@@ -19,8 +19,10 @@
 //    16-byte loads that cover whole rows, and writes them transposed into one
 //    of two LDS stages, which hold 16-byte units of 8 keys of one feature.
 //    One barrier per tile; it waits only for the LDS stores and the copies of
-//    the next tile, never for the loads still running.  Loads past the end of
-//    the keys return zeros.
+//    the next tile, never for the loads still running.  With D = 128 each
+//    wave's four global loads per tile sit between its score instructions,
+//    so the waves do not all queue on the address unit right after the
+//    barrier.  Loads past the end of the keys return zeros.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: each lane owns one query row (lane % 32) and 32
 //    of the tile's 64 keys, so the row maximum and sum need one cross-half
@@ -88,25 +90,22 @@ __device__ __forceinline__ float fmax3(float a, float b, float c)
 // 4h + {0,1,2,3,8,9,10,11}[s].
 __device__ __forceinline__ int p_slot_key(int s) { return s < 4 ? s : s + 4; }
 
-// Issue this wave's buffer loads that copy rows of the K tile into LDS: load
-// i writes the 1 KB at byte (kWaves * i + wave) * 1024 of the tile, lane s its
+// Issue load i of this wave's buffer loads that copy rows of the K tile into
+// LDS (i < 64 / RPD / kWaves): load i writes the 1 KB at byte (kWaves * i + wave) * 1024 of the tile, lane s its
 // 16-byte slot s: tile row (kWaves * i + wave) * RPD + s / UPR, physical unit
 // s % UPR, which holds logical unit (s % UPR) ^ (row % 16).  Bytes past nrec
 // read as zero.
 template <int D>
 __device__ __forceinline__ void fill_k(const unsigned char* ksrc, uint32_t nrec, unsigned char* kdst, int wave,
-                                       int lane, uint32_t ld2)
+                                       int lane, uint32_t ld2, int i)
 {
-    constexpr int UPR = D / 8, RPD = 1024 / (D * 2), NDMA = 64 / RPD;
+    constexpr int UPR = D / 8, RPD = 1024 / (D * 2);
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)ksrc, (short)0, nrec, 0x00020000);
     lds_u8* kd = (lds_u8*)kdst;
-#pragma unroll
-    for (int i = 0; i < NDMA / kWaves; ++i) {
-        const int n = kWaves * i + wave;
-        const int row = n * RPD + lane / UPR;
-        const uint32_t off = (uint32_t)row * ld2 + (uint32_t)(((lane % UPR) ^ (row & (UPR - 1))) * 16);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kd + n * 1024, 16, off, 0, 0, 0);
-    }
+    const int n = kWaves * i + wave;
+    const int row = n * RPD + lane / UPR;
+    const uint32_t off = (uint32_t)row * ld2 + (uint32_t)(((lane % UPR) ^ (row & (UPR - 1))) * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kd + n * 1024, 16, off, 0, 0, 0);
 }
 
 template <int D, bool MASKED, bool OUT_BF16>
@@ -214,21 +213,24 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
         v_soff = 0;
     }
     // a descriptor per tile (scalar work only) whose range ends at the last key
-    auto load_v = [&](int t, auto set_tag) {
-        constexpr int set = decltype(set_tag)::value;
+    auto v_rsrc = [&](int t) {
         const int64_t j0 = (int64_t)t * kBN;
         const uint32_t nrec = (uint32_t)((Sk - 1 - j0) * ld2 + D * 2);
-        const __amdgpu_buffer_rsrc_t tr =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + j0 * ld2), (short)0, nrec, 0x00020000);
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + j0 * ld2), (short)0, nrec, 0x00020000);
+    };
+    auto load_v_part = [&](__amdgpu_buffer_rsrc_t tr, auto set_tag, int r) {
+        constexpr int set = decltype(set_tag)::value;
+        // keys of one lane are consecutive inside each p_slot_key group of 4
+        const uint32_t off = v_goff + (uint32_t)(p_slot_key(r) - p_slot_key(0)) * ld2;
+        if constexpr (VLD == 4)
+            vst[set][r] = __builtin_bit_cast(vld_t, __builtin_amdgcn_raw_buffer_load_b128(tr, off, 0, 0));
+        else
+            vst[set][r] = __builtin_bit_cast(vld_t, __builtin_amdgcn_raw_buffer_load_b64(tr, off, 0, 0));
+    };
+    auto load_v = [&](int t, auto set_tag) {
+        const __amdgpu_buffer_rsrc_t tr = v_rsrc(t);
 #pragma unroll
-        for (int r = 0; r < KPL; ++r) {
-            // keys of one lane are consecutive inside each p_slot_key group of 4
-            const uint32_t off = v_goff + (uint32_t)(p_slot_key(r) - p_slot_key(0)) * ld2;
-            if constexpr (VLD == 4)
-                vst[set][r] = __builtin_bit_cast(vld_t, __builtin_amdgcn_raw_buffer_load_b128(tr, off, 0, 0));
-            else
-                vst[set][r] = __builtin_bit_cast(vld_t, __builtin_amdgcn_raw_buffer_load_b64(tr, off, 0, 0));
-        }
+        for (int r = 0; r < KPL; ++r) load_v_part(tr, set_tag, r);
     };
     auto store_v = [&](auto set_tag) {   // register set s goes to V stage s
         constexpr int set = decltype(set_tag)::value;
@@ -254,13 +256,18 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
             }
         }
     };
-    auto issue_k = [&](int t, int ks) {
+    auto issue_k = [&](int t, int ks, int i) {
         const int64_t j0 = (int64_t)t * kBN;
         const uint32_t nrec = (uint32_t)((Sk - 1 - j0) * ld2 + D * 2);   // bytes of valid rows from j0
-        fill_k<D>(kbase + j0 * ld2, nrec, smem + ks * TB, wave, lane, ld2);
+        fill_k<D>(kbase + j0 * ld2, nrec, smem + ks * TB, wave, lane, ld2, i);
+    };
+    constexpr int kDmaPerWave = (64 / (1024 / (D * 2))) / kWaves;
+    auto issue_k_all = [&](int t, int ks) {
+#pragma unroll
+        for (int i = 0; i < kDmaPerWave; ++i) issue_k(t, ks, i);
     };
     // vector memory operations each wave issues per tile: K copies, V loads
-    constexpr int kVmPerTile = (64 / (1024 / (D * 2))) / kWaves + KPL;
+    constexpr int kVmPerTile = kDmaPerWave + KPL;
 
     // ---- LDS operand offsets (bytes) -------------------------------------
     // K operand of the score product, block jb, chunk kc: row 32*jb + l32,
@@ -297,10 +304,10 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
     int t1 = t < n_tiles ? next_live(t + 1) : n_tiles;
     int ks = 0;   // K stage of tile t
     if (t < n_tiles) {
-        issue_k(t, 0);
+        issue_k_all(t, 0);
         load_v(t, std::integral_constant<int, 0>{});
         if (t1 < n_tiles) {
-            issue_k(t1, 1);
+            issue_k_all(t1, 1);
             load_v(t1, std::integral_constant<int, 1>{});
         }
         store_v(std::integral_constant<int, 0>{});
@@ -314,15 +321,18 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
         constexpr int P = decltype(parity_tag)::value;
         const int t2 = t1 < n_tiles ? next_live(t1 + 1) : n_tiles;
         const int ks2 = ks == 0 ? 2 : ks - 1;   // (ks + 2) % 3
-        {
-            // Always issue the copies (of tile t when there is no t2; they
-            // land in buffers nothing reads) so that every wave has exactly
-            // kVmPerTile vector memory operations per step in flight.
-            const int tl = t2 < n_tiles ? t2 : t;
-            issue_k(tl, ks2);
+        // Always issue the copies (of tile t when there is no t2; they land
+        // in buffers nothing reads) so that every wave has exactly kVmPerTile
+        // vector memory operations per step in flight.  They are issued among
+        // the score instructions below, spread out so that the waves of the
+        // workgroup do not all queue on the address unit at once.
+        const int tl = t2 < n_tiles ? t2 : t;
+
+        if constexpr (D != 128) {
+            // few matrix instructions per tile: the loads go up front
+            issue_k_all(tl, ks2);
             load_v(tl, std::integral_constant<int, P>{});
         }
-
         const int64_t j0 = (int64_t)t * kBN;
         bool any = wave_live, per_elem = j0 + kBN > Sk;
         if (MASKED && wave_live) {
@@ -333,31 +343,71 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
             per_elem = per_elem || kmax > w_qmin;
         }
 
-        if (any) {
+        // With D = 128 every wave computes every live tile (the global loads
+        // sit among its score instructions); smaller D skips tiles none of the
+        // wave's rows can see.
+        if (D == 128 || any) {
             const lds_u8* Kl = (const lds_u8*)(smem + ks * TB);
             const lds_u8* Vl = (const lds_u8*)(smem + 3 * TB + P * VTB);
 
-            // S^T = K Q^T: block jb, register v holds key 32*jb + 8*(v/4) + 4*hg + v%4
+            // S^T = K Q^T: block jb, register v holds key 32*jb + 8*(v/4) + 4*hg + v%4.
             f32x16 sacc[2];
+            if constexpr (D == 128) {
+                // Matrix instruction r of the scores:
+                // Matrix instruction r uses k-chunk r/2 of block r%2; its K operand
+                // is read four instructions ahead.  The global loads for tile tl
+                // are placed between the matrix instructions, one every few, and
+                // scheduling barriers keep that order, so that the waves do not
+                // all queue on the address unit at the top of the step.
+                constexpr int NS = 2 * NKC;
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
+                for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) sacc[jb][v] = 0.f;
+                    for (int v = 0; v < 16; ++v) sacc[jb][v] = 0.f;
+                auto kread = [&](int r) {
+                    return __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Kl + kaddr[r >> 1] + (r & 1) * 32 * ROWB));
+                };
+                const __amdgpu_buffer_rsrc_t vtr = v_rsrc(tl);
+                bf16x8 kop[NS];
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc)
+                for (int r = 0; r < 4; ++r) kop[r] = kread(r);
 #pragma unroll
-                for (int jb = 0; jb < 2; ++jb) {
-                    const bf16x8 kop = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Kl + kaddr[kc] + jb * 32 * ROWB));
-                    sacc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kc], sacc[jb], 0, 0, 0);
+                for (int r = 0; r < NS; ++r) {
+                    sacc[r & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[r], qop[r >> 1], sacc[r & 1], 0, 0, 0);
+                    if (r + 4 < NS) kop[r + 4] = kread(r + 4);
+                    constexpr int kGap = NS / kVmPerTile;
+                    if (r % kGap == kGap / 2) {
+                        const int m = r / kGap;
+                        if (m < kDmaPerWave)
+                            issue_k(tl, ks2, m);
+                        else if (m < kVmPerTile)
+                            load_v_part(vtr, std::integral_constant<int, P>{}, m - kDmaPerWave);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-            // keep 4 operand reads in flight ahead of the matrix instructions
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+
+            } else {
 #pragma unroll
-            for (int r = 0; r < 2 * NKC - 4; ++r) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) sacc[jb][v] = 0.f;
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                    for (int jb = 0; jb < 2; ++jb) {
+                        const bf16x8 kop =
+                            __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Kl + kaddr[kc] + jb * 32 * ROWB));
+                        sacc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kc], sacc[jb], 0, 0, 0);
+                    }
+                // keep 4 operand reads in flight ahead of the matrix instructions
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int r = 0; r < 2 * NKC - 4; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
             if (per_elem) {
 #pragma unroll
