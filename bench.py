@@ -65,6 +65,12 @@ def parse():
     p.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough for 1 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--pmc-probe", action="store_true",
+                   help="only enqueue the dispatches that the HBM traffic counters are read on: a plain "
+                        "device copy of known size, then --steps attention launch pairs")
+    p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="print the traffic summary of two rocprofv3 --pmc runs of --pmc-probe")
+    p.add_argument("--stats-summary", metavar="DIR", help="print the summary of a rocprofv3 --stats run")
     return p.parse_args()
 
 
@@ -219,8 +225,129 @@ def cpu_baseline(share: "Share", target_s: float):
                       "plus the Ulysses gather of Q/K/V pro-rated; %.1f s" % (n, S, Hr, S, t_total)}
 
 
+# ---- HBM traffic of the attention kernel (rocprofv3 counters) ---------------
+PMC_COPY_BYTES = 1 << 30              # calibration copy: a plain device-to-device copy of 1 GiB
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_flux1024_hbm_traffic.txt")
+ATTN_SOURCES = ["attn_bf16.hip", "attn_common.h", "internal.h"]
+
+
+def attn_source_hash():
+    """sha256 over the sources the bf16 attention kernel is built from, so that
+    counters taken on an older kernel are not reported for a newer one."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "sequence_attention_dits_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def pmc_probe(args):
+    import torch
+    torch.cuda.set_device(0)
+    src = torch.ones(PMC_COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    cfg_id, _ = WORKLOADS[args.workload]
+    share = Share(cfg_id, 4)
+    for i in range(args.steps):
+        share.launch_one("attn", i % 4)
+    torch.cuda.synchronize()
+
+
+def _pmc_values(d, counter):
+    """{kernel name: [per-dispatch values]} of one counter from a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def pmc_summary(fetch_dir, write_dir, workload):
+    """Per-dispatch HBM bytes of the attention kernel from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
+    for the calibration copy of PMC_COPY_BYTES."""
+    res = {}
+    for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        vals = _pmc_values(d, counter)
+        copy = sorted(v for k, vs in vals.items() if "copyBuffer" in k or "copy" in k.lower() for v in vs)
+        copy = [v for v in copy if v * 1024 > PMC_COPY_BYTES / 4]
+        attn = [v for k, vs in vals.items() if "attn_bf16_kernel" in k for v in vs]
+        if not copy or not attn:
+            raise SystemExit("no calibration copy or attention dispatch in " + d)
+        scale = PMC_COPY_BYTES / (1024 * sum(copy) / len(copy))
+        res[key] = (sum(copy) / len(copy), scale, sum(attn) / len(attn), len(attn))
+    cfg_id, desc = WORKLOADS[workload]
+    import synth
+    c = synth.CONFIGS[cfg_id]
+    Hr = (c["H"] + 1) // 2
+    sq, sk = c["S"], c["shards"][0]
+    algo = 2 * c["B"] * Hr * c["D"] * (2 * sq + 2 * sk) + 4 * c["B"] * sq * Hr
+    traffic = res["fetch"][1] * res["fetch"][2] * 1024 + res["write"][1] * res["write"][2] * 1024
+    lines = [
+        "rocprofv3 counter summary: HBM traffic of the bf16 attention kernel, one Ring-chunk launch of the",
+        "%s step (Sq=%d, Sk=%d, %d heads, D=%d)" % (workload, sq, sk, Hr, c["D"]),
+        "",
+        "commands (run from the repository root on one MI355X):",
+        "  rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o pmc --output-format csv -- python3 bench.py --pmc-probe",
+        "  rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o pmc --output-format csv -- python3 bench.py --pmc-probe",
+        "  python3 bench.py --pmc-summary gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        "",
+        "calibration: plain device copy of %d bytes" % PMC_COPY_BYTES,
+        "  FETCH_SIZE %.1f KiB per copy -> scale %.4f;  WRITE_SIZE %.1f KiB per copy -> scale %.4f"
+        % (res["fetch"][0], res["fetch"][1], res["write"][0], res["write"][1]),
+        "attention (%d dispatches): FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB per dispatch"
+        % (res["fetch"][3], res["fetch"][2], res["write"][2]),
+        "algorithmic_bytes_per_launch: %d   (Q, K, V read once, O and LSE written once)" % algo,
+        "traffic_bytes_per_launch: %d" % round(traffic),
+        "traffic_over_algorithmic: %.3f" % (traffic / algo),
+        "source_sha256: %s" % attn_source_hash(),
+    ]
+    print("\n".join(lines))
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when it is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(": ", 1) for line in f.read().splitlines() if ": " in line)
+        if kv.get("source_sha256", "").strip() != attn_source_hash():
+            return None
+        return int(kv["traffic_bytes_per_launch"].split()[0])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def stats_summary(d):
+    """Kernel table of a rocprofv3 --kernel-trace --stats run (its *_kernel_stats.csv)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no kernel_stats.csv under " + d)
+    rows = list(csv.DictReader(open(files[0])))
+    print("%-70s %6s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us"))
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"] if len(r["Name"]) <= 70 else r["Name"][:67] + "..."
+        print("%-70s %6d %12.2f %12.2f %12.2f" % (name, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                                                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
+        return
+    if args.stats_summary:
+        stats_summary(args.stats_summary)
+        return
     if args.gpus != 1:
         print("bench.py measures one rank's share on one GPU; --gpus %d is not supported "
               "(this build has no multi-GPU path)" % args.gpus, file=sys.stderr)
@@ -230,6 +357,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.pmc_probe:
+        pmc_probe(args)
+        return
     cfg_id, desc = WORKLOADS[args.workload]
     import synth
     c = synth.CONFIGS[cfg_id]
@@ -242,7 +372,7 @@ def main():
         share.step(i % n_sets)
     torch.cuda.synchronize()
 
-    # One HIP graph per input set: a step is 8 launches, and replaying a
+    # One HIP graph per input set: a step is 6 launches, and replaying a
     # captured graph keeps host launch overhead out of the step time.
     graphs = []
     for s_ in range(n_sets):
@@ -330,7 +460,8 @@ def main():
                    "D": share.D, "ulysses": share.P, "ring_chunks": len(share.ring),
                    "attn_flops_per_step": attn_flops},
         "roofline": {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic() if args.workload == "flux1024" else None,
                      "kernel": "attn_bf16_kernel<128,true>", "launch_us": round(attn_us, 2),
                      "flops_per_launch": attn_flops_launch},
         "kernels": {
