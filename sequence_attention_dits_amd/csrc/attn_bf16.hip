@@ -420,6 +420,10 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
                     }
             }
 
+            // Raised wave priority while this wave runs its softmax and PV
+            // products, so that its vector work is issued ahead of the other
+            // wave's score instructions on the same SIMD.
+            __builtin_amdgcn_s_setprio(1);
             // online softmax of row i
             float mx;
             {
@@ -473,6 +477,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[db], 0, 0, 0);
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
             lsum += ps0 + ps1;
         }
 
