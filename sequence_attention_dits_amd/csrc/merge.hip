@@ -41,7 +41,7 @@ template <typename T, int VEC> struct Slice;
 template <> struct Slice<unsigned short, 8> {     // bf16, 16 bytes
     static __device__ __forceinline__ void load(const void* p, float* x)
     {
-        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        const u32x4 w = *reinterpret_cast<const u32x4*>(p);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             x[2 * e] = __uint_as_float(w[e] << 16);
@@ -61,7 +61,7 @@ template <> struct Slice<unsigned short, 8> {     // bf16, 16 bytes
 template <> struct Slice<float, 4> {              // fp32, 16 bytes
     static __device__ __forceinline__ void load(const void* p, float* x)
     {
-        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        const u32x4 w = *reinterpret_cast<const u32x4*>(p);
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e]);
     }

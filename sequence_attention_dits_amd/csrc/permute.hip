@@ -17,8 +17,9 @@
 // The launch grid is (chunks, source y, batch * tensor), so every base
 // pointer, stride and run length is uniform in a workgroup (scalar
 // registers); inside a chunk each lane moves U 16-byte vectors of the
-// flattened (row, column) space, loads issued before stores, with
-// non-temporal accesses on both sides since nothing is reused.  The row of a
+// flattened (row, column) space, loads issued before stores; stores are
+// non-temporal since nothing reads them back soon (measured: non-temporal
+// loads are ~20 % slower here, non-temporal stores faster).  The row of a
 // vector comes from one multiply-high by a host-computed reciprocal.
 #include "internal.h"
 
@@ -44,8 +45,6 @@ FastDiv make_fastdiv(uint32_t d)
     return f;
 }
 
-template <typename V>
-__device__ __forceinline__ V ld_nt(const V* p) { return __builtin_nontemporal_load(p); }
 template <typename V>
 __device__ __forceinline__ void st_nt(V* p, V x) { __builtin_nontemporal_store(x, p); }
 
@@ -96,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const PermuteArgs a)
         const uint32_t f = base + threadIdx.x + u * kThreads;
         row[u] = mul == 0 ? (f >> shift) : (__umulhi(f, mul) >> shift);
         col[u] = f - row[u] * (uint32_t)run;
-        if (f < n) tmp[u] = ld_nt(src + (int64_t)row[u] * src_stride + col[u]);
+        if (f < n) tmp[u] = src[(int64_t)row[u] * src_stride + col[u]];
     }
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
