@@ -24,6 +24,13 @@ step first).  Per-kernel times come from HIP events around K back-to-back
 launches of each kernel of the step (same arguments, rotating inputs), on
 the stream the kernels run on.
 
+Other workloads (--workload): flux1008 (the same step on the non-divisible
+4481-token UAA share), and two Ring-only shares whose step is one attention
+launch per K/V chunk plus the N-way merge: qwen1328 (Qwen-Image 1328x1328,
+2 chunks of 3493) and longctx (32768-token causal zigzag layout, Q = chunks
+{1, 6}, 8 chunks of 4096 masked by global position, 8-way merge).  There
+`value` counts only the allowed (query, key) pairs.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--no-cpu-baseline]
 """
@@ -53,7 +60,12 @@ WORKLOADS = {
                     "K/V as 2 Ring chunks of 2304, LSE merge, inverse gather"),
     "flux1008": (3, "FLUX.1-dev 1008x1008 UAA rank share: S=4481 (2241/2240), 12 of 24 heads, D=128, bf16, "
                     "K/V as 2 Ring chunks of 2241/2240, LSE merge, inverse gather"),
+    "qwen1328": (4, "Qwen-Image 1328x1328 Ring rank share: Q = 3493 of 6986 tokens, 24 heads, D=128, bf16, "
+                    "K/V as 2 Ring chunks of 3493, LSE merge"),
+    "longctx": (5, "long-context causal zigzag Ring share: S=32768 in 8 chunks of 4096, Q = chunks {1,6}, "
+                   "32 heads, D=128, bf16, K/V over all 8 chunks masked by global position, 8-way LSE merge"),
 }
+RING_WORKLOADS = ("qwen1328", "longctx")
 
 
 def parse():
@@ -165,6 +177,11 @@ class Share:
             return 1
         raise ValueError(name)
 
+    kernel_names = ("permute", "permute_qkv", "attn", "merge", "head2seq", "head2seq_lse")
+
+    def result(self):
+        return self.o_tok, self.l_tok
+
     def step(self, s):
         """Enqueue one step on input set s."""
         for name in ("permute3", "attn", "merge", "head2seq", "head2seq_lse"):
@@ -178,6 +195,132 @@ class Share:
         d = self.sets[s]
         uaa.uaa_seq2head_permute_multi(uaa.UAA_SEQ2HEAD, 0, [d[n] for n in "qkv"], [self.qh[n] for n in "qkv"],
                                        self.seq_off, self.head_off)
+
+
+class RingShare:
+    """Device buffers and launches of a Ring-only share: the rank's queries
+    against every K/V chunk of the ring (one attention launch per chunk, with
+    the causal zigzag mask by global position where the layout has one), then
+    the N-way LSE merge of the partials."""
+
+    def __init__(self, cfg_id: int, n_sets: int):
+        import numpy as np
+        import torch
+
+        import synth
+        import sequence_attention_dits_amd as uaa
+        self.uaa = uaa
+        self.torch = torch
+        c = synth.CONFIGS[cfg_id]
+        self.B, self.H, self.D = c["B"], c["H"], c["D"]
+        self.scale = float(np.float32(1.0 / math.sqrt(self.D)))
+        if "chunks" in c:        # zigzag: Q = this rank's two chunks, K/V = every chunk
+            n, self.qc = c["chunks"], list(c["q_chunks"])
+            self.chunk = c["S"] // n
+            self.Sq = self.chunk * len(self.qc)
+            self.kv = [(i * self.chunk, (i + 1) * self.chunk) for i in range(n)]
+            self.masks = [uaa.mask_zigzag(self.chunk, self.qc, [i]) for i in range(n)]
+            q_rows = np.concatenate([np.arange(i * self.chunk, (i + 1) * self.chunk) for i in self.qc])
+        else:                    # basic ring: Q = shard 0, K/V = both shards
+            sh = c["shards"]
+            self.chunk = None
+            self.Sq = sh[0]
+            self.kv = [(0, sh[0]), (sh[0], sh[0] + sh[1])]
+            self.masks = [None, None]
+            q_rows = np.arange(sh[0])
+        S = c["S"]
+        qb, qv = synth.tensor(cfg_id, 0, (self.B, S, self.H, self.D), "bf16", rms_norm=c["rms"])
+        kb, kv_ = synth.tensor(cfg_id, 1, (self.B, S, self.H, self.D), "bf16", rms_norm=c["rms"])
+        vb, vv = synth.tensor(cfg_id, 2, (self.B, S, self.H, self.D), "bf16", rms_norm=False)
+        self.host = {"q": qv[:, q_rows], "k": kv_, "v": vv, "q_rows": q_rows}
+        dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).cuda().view(torch.bfloat16)
+        d0 = {"q": dev(qb[:, q_rows]), "k": dev(kb), "v": dev(vb)}
+        self.sets = [d0] + [{k: v.clone() for k, v in d0.items()} for _ in range(n_sets - 1)]
+        bf = torch.bfloat16
+        self.o_part = [torch.empty(self.B, self.Sq, self.H, self.D, device="cuda", dtype=bf) for _ in self.kv]
+        self.l_part = [torch.empty(self.B, self.Sq, self.H, device="cuda", dtype=torch.float32) for _ in self.kv]
+        self.o = torch.empty(self.B, self.Sq, self.H, self.D, device="cuda", dtype=bf)
+        self.lse = torch.empty(self.B, self.Sq, self.H, device="cuda", dtype=torch.float32)
+        # allowed (query, key) pairs of each launch, from the position maps
+        self.pairs = []
+        for (a, b), m in zip(self.kv, self.masks):
+            if m is None:
+                self.pairs.append(float(self.Sq) * (b - a))
+            else:
+                qpos = q_rows
+                kpos = np.arange(a, b)
+                self.pairs.append(float(np.searchsorted(np.sort(kpos), qpos, side="right").sum()))
+
+    kernel_names = ("attn", "merge")
+
+    def attn_flops(self, chunk):
+        return 4.0 * self.D * self.H * self.B * self.pairs[chunk]
+
+    def merge_bytes(self):
+        rows = self.B * self.Sq * self.H
+        per = rows * self.D * 2 + rows * 4
+        return len(self.kv) * per + per
+
+    def launch_one(self, name, s):
+        uaa = self.uaa
+        d = self.sets[s]
+        if name == "attn":
+            for c, (a, b) in enumerate(self.kv):
+                uaa.usp_attn_fwd_lse(d["q"], d["k"][:, a:b], d["v"][:, a:b], self.o_part[c], self.l_part[c],
+                                     self.scale, self.masks[c])
+            return len(self.kv)
+        if name == "merge":
+            uaa.usp_lse_merge(self.o_part, self.l_part, self.o, self.lse)
+            return 1
+        raise ValueError(name)
+
+    def step(self, s):
+        self.launch_one("attn", s)
+        self.launch_one("merge", s)
+
+    def result(self):
+        return self.o, self.lse
+
+
+def ring_cpu_baseline(share: "RingShare", target_s: float):
+    """The fp64 oracle on a sample of query rows of a Ring share: attention
+    against every chunk (with the positions of the mask) and the merge."""
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    h = share.host
+
+    def run(rows):
+        t = time.perf_counter()
+        parts = []
+        for (a, b), m in zip(share.kv, share.masks):
+            qpos = kpos = None
+            if m is not None:
+                qpos, kpos = h["q_rows"], np.arange(a, b)
+            parts.append(oracle.attention(h["q"], h["k"][:, a:b], h["v"][:, a:b], share.scale, qpos=qpos,
+                                          kpos=kpos, rows=rows))
+        oracle.lse_merge([p[0] for p in parts], [p[1] for p in parts])
+        return time.perf_counter() - t
+
+    n = 8
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(share.Sq, n, replace=False))
+    elapsed = run(rows)
+    while elapsed < target_s / 4 and n < share.Sq:
+        n = min(share.Sq, int(n * max(2.0, min(8.0, target_s / max(elapsed, 1e-3) / 2))))
+        rows = np.sort(rng.choice(share.Sq, n, replace=False))
+        elapsed = run(rows)
+    # the sample's share of the allowed pairs
+    if share.masks[0] is None:
+        pairs = float(n) * sum(b - a for a, b in share.kv)
+    else:
+        qpos = h["q_rows"][rows]
+        pairs = float(sum(np.searchsorted(np.arange(a, b), qpos, side="right").sum() for a, b in share.kv))
+    flops = 4.0 * share.D * share.H * pairs
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of %d query rows x %d heads against all %d K/V chunks + %d-way merge, fp64; %.1f s"
+                      % (n, share.Sq, share.H, len(share.kv), len(share.kv), elapsed)}
 
 
 def _contig(t):
@@ -363,17 +506,22 @@ def main():
     cfg_id, desc = WORKLOADS[args.workload]
     import synth
     c = synth.CONFIGS[cfg_id]
+    ring = args.workload in RING_WORKLOADS
     # enough rotating input sets to exceed 1 GiB of inputs (> 4x the MALL)
-    per_set = 3 * c["B"] * c["S"] * c["H"] * c["D"] * 2 + c["B"] * c["S"] * (c["H"] // 2) * c["D"] * 2
+    if ring:
+        sq = c["S"] // c["chunks"] * len(c["q_chunks"]) if "chunks" in c else c["shards"][0]
+        per_set = (sq + 2 * c["S"]) * c["B"] * c["H"] * c["D"] * 2
+    else:
+        per_set = 3 * c["B"] * c["S"] * c["H"] * c["D"] * 2 + c["B"] * c["S"] * (c["H"] // 2) * c["D"] * 2
     n_sets = args.sets or max(2, int(math.ceil((1 << 30) / per_set)))
-    share = Share(cfg_id, n_sets)
+    share = RingShare(cfg_id, n_sets) if ring else Share(cfg_id, n_sets)
 
     for i in range(max(args.warmup, 1)):
         share.step(i % n_sets)
     torch.cuda.synchronize()
 
-    # One HIP graph per input set: a step is 6 launches, and replaying a
-    # captured graph keeps host launch overhead out of the step time.
+    # One HIP graph per input set: replaying a captured step keeps host launch
+    # overhead out of the step time.
     graphs = []
     for s_ in range(n_sets):
         g = torch.cuda.CUDAGraph()
@@ -388,12 +536,12 @@ def main():
     # replay check: a replay must reproduce the eager step bit for bit
     share.step(0)
     torch.cuda.synchronize()
-    ref_o, ref_l = share.o_tok.clone(), share.l_tok.clone()
+    ref_o, ref_l = (t.clone() for t in share.result())
     graphs[1 % n_sets].replay()
     graphs[0].replay()
     torch.cuda.synchronize()
-    replay_ok = bool(torch.equal(ref_o.view(torch.int16), share.o_tok.view(torch.int16))
-                     and torch.equal(ref_l, share.l_tok))
+    out_o, out_l = share.result()
+    replay_ok = bool(torch.equal(ref_o.view(torch.int16), out_o.view(torch.int16)) and torch.equal(ref_l, out_l))
     if not replay_ok:
         print("graph replay differs from the eager step", file=sys.stderr)
         sys.exit(1)
@@ -414,7 +562,7 @@ def main():
     # events on the launch stream; a spin kernel first gives the host a head
     # start so no launch waits on the host.
     log = {}
-    for name in ("permute", "permute_qkv", "attn", "merge", "head2seq", "head2seq_lse"):
+    for name in share.kernel_names:
         a_ev = torch.cuda.Event(enable_timing=True)
         b_ev = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -428,19 +576,41 @@ def main():
         log[name] = 1e3 * a_ev.elapsed_time(b_ev) / n
     torch.cuda.synchronize()
 
-    attn_flops = sum(share.attn_flops(c_) for c_ in range(len(share.ring)))
+    n_attn = len(share.kv) if ring else len(share.ring)
+    attn_flops = sum(share.attn_flops(c_) for c_ in range(n_attn))
     value = attn_flops / (ms_step * 1e-3) / 1e12
     attn_us = log["attn"]
-    attn_flops_launch = attn_flops / len(share.ring)
+    attn_flops_launch = attn_flops / n_attn
     attn_tf = attn_flops_launch / (attn_us * 1e-6) / 1e12
-    perm_us = log["permute"]
-    perm_gbps = share.permute_bytes() / (perm_us * 1e-6) / 1e9
     merge_us = log["merge"]
     merge_gbps = share.merge_bytes() / (merge_us * 1e-6) / 1e9
-    h2s_us = log["head2seq"]
-    qkv_us = log["permute_qkv"]
-    qkv_gbps = 3 * share.permute_bytes() / (qkv_us * 1e-6) / 1e9
-    h2s_gbps = share.head2seq_bytes() / (h2s_us * 1e-6) / 1e9
+    kernels = {
+        "lse_merge": {"us": round(merge_us, 2), "GB/s": round(merge_gbps, 1),
+                      "hbm_frac": round(merge_gbps / PEAK_HBM_GBPS, 4), "bytes": share.merge_bytes()},
+        "attention": {"us": round(attn_us, 2), "TFLOP/s": round(attn_tf, 2),
+                      "mfma_frac": round(attn_tf / PEAK_BF16_TFLOPS, 4)},
+    }
+    if ring:
+        config = {"workload": desc, "B": share.B, "Sq": share.Sq, "heads": share.H, "D": share.D,
+                  "ring_chunks": n_attn, "attn_flops_per_step": attn_flops}
+    else:
+        perm_us = log["permute"]
+        perm_gbps = share.permute_bytes() / (perm_us * 1e-6) / 1e9
+        h2s_us = log["head2seq"]
+        qkv_us = log["permute_qkv"]
+        qkv_gbps = 3 * share.permute_bytes() / (qkv_us * 1e-6) / 1e9
+        h2s_gbps = share.head2seq_bytes() / (h2s_us * 1e-6) / 1e9
+        kernels.update({
+            "seq2head_permute": {"us": round(perm_us, 2), "GB/s": round(perm_gbps, 1),
+                                 "hbm_frac": round(perm_gbps / PEAK_HBM_GBPS, 4), "bytes": share.permute_bytes()},
+            "seq2head_permute_qkv": {"us": round(qkv_us, 2), "GB/s": round(qkv_gbps, 1),
+                                     "hbm_frac": round(qkv_gbps / PEAK_HBM_GBPS, 4),
+                                     "bytes": 3 * share.permute_bytes()},
+            "head2seq_permute": {"us": round(h2s_us, 2), "GB/s": round(h2s_gbps, 1),
+                                 "hbm_frac": round(h2s_gbps / PEAK_HBM_GBPS, 4), "bytes": share.head2seq_bytes()},
+        })
+        config = {"workload": desc, "B": share.B, "S": share.S, "heads_total": share.H, "heads_rank": share.Hr,
+                  "D": share.D, "ulysses": share.P, "ring_chunks": n_attn, "attn_flops_per_step": attn_flops}
 
     out = {
         "metric": METRIC,
@@ -454,34 +624,21 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1), Q/K RMS-normalised per head; inputs resident in HBM, "
-                "%d rotating sets)" % n_sets,
-        "config": {"workload": desc, "B": share.B, "S": share.S, "heads_total": share.H, "heads_rank": share.Hr,
-                   "D": share.D, "ulysses": share.P, "ring_chunks": len(share.ring),
-                   "attn_flops_per_step": attn_flops},
+        "data": "synthetic (seeded N(0,1), Q/K RMS-normalised per head where the workload says so; inputs "
+                "resident in HBM, %d rotating sets)" % n_sets,
+        "config": config,
         "roofline": {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic() if args.workload == "flux1024" else None,
-                     "kernel": "attn_bf16_kernel<128,true>", "launch_us": round(attn_us, 2),
-                     "flops_per_launch": attn_flops_launch},
-        "kernels": {
-            "seq2head_permute": {"us": round(perm_us, 2), "GB/s": round(perm_gbps, 1),
-                                 "hbm_frac": round(perm_gbps / PEAK_HBM_GBPS, 4),
-                                 "bytes": share.permute_bytes()},
-            "seq2head_permute_qkv": {"us": round(qkv_us, 2), "GB/s": round(qkv_gbps, 1),
-                                     "hbm_frac": round(qkv_gbps / PEAK_HBM_GBPS, 4),
-                                     "bytes": 3 * share.permute_bytes()},
-            "lse_merge": {"us": round(merge_us, 2), "GB/s": round(merge_gbps, 1),
-                          "hbm_frac": round(merge_gbps / PEAK_HBM_GBPS, 4), "bytes": share.merge_bytes()},
-            "head2seq_permute": {"us": round(h2s_us, 2), "GB/s": round(h2s_gbps, 1),
-                                 "hbm_frac": round(h2s_gbps / PEAK_HBM_GBPS, 4), "bytes": share.head2seq_bytes()},
-            "attention": {"us": round(attn_us, 2), "TFLOP/s": round(attn_tf, 2),
-                          "mfma_frac": round(attn_tf / PEAK_BF16_TFLOPS, 4)},
-        },
-        "permute_GBps": round(perm_gbps, 1),
+                     "kernel": "attn_bf16_kernel<128,%s>" % ("masked" if ring and share.masks[0] is not None
+                                                            else "true"),
+                     "launch_us": round(attn_us, 2), "flops_per_launch": attn_flops_launch},
+        "kernels": kernels,
     }
+    if not ring:
+        out["permute_GBps"] = kernels["seq2head_permute"]["GB/s"]
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(share, args.cpu_seconds)
+        out["cpu_baseline"] = (ring_cpu_baseline if ring else cpu_baseline)(share, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
