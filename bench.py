@@ -128,6 +128,7 @@ class Share:
         self.l_part = [torch.empty(B, S, Hr, device="cuda", dtype=torch.float32) for _ in self.ring]
         self.o = torch.empty(B, S, Hr, D, device="cuda", dtype=bf)
         self.lse = torch.empty(B, S, Hr, device="cuda", dtype=torch.float32)
+        self.ws = _workspace(self.uaa, self.qh["q"], [kc for kc, _ in self.kc], [None] * len(self.kc))
         S0 = self.seq_off[1]
         self.o_tok = torch.empty(B, S0, H, D, device="cuda", dtype=bf)
         self.l_tok = torch.empty(B, S0, H, 1, device="cuda", dtype=torch.float32)
@@ -162,7 +163,7 @@ class Share:
         if name == "attn":
             for c, (kc, vc) in enumerate(self.kc):
                 uaa.usp_attn_fwd_lse(self.qh["q"], _contig(kc), _contig(vc), self.o_part[c], self.l_part[c],
-                                     self.scale)
+                                     self.scale, workspace=self.ws)
             return len(self.kc)
         if name == "merge":
             uaa.usp_lse_merge(self.o_part, self.l_part, self.o, self.lse)
@@ -195,6 +196,18 @@ class Share:
         d = self.sets[s]
         uaa.uaa_seq2head_permute_multi(uaa.UAA_SEQ2HEAD, 0, [d[n] for n in "qkv"], [self.qh[n] for n in "qkv"],
                                        self.seq_off, self.head_off)
+
+
+def _workspace(uaa, q, ks, masks):
+    """One attention workspace for every launch of a step (the launches run
+    in stream order, so they may share it): the largest any of them asks
+    for, or None when none splits its keys."""
+    best = None
+    for k, m in zip(ks, masks):
+        w = uaa.attn_workspace(q, k, m)
+        if w is not None and (best is None or w.numel() > best.numel()):
+            best = w
+    return best
 
 
 class RingShare:
@@ -241,6 +254,7 @@ class RingShare:
         self.l_part = [torch.empty(self.B, self.Sq, self.H, device="cuda", dtype=torch.float32) for _ in self.kv]
         self.o = torch.empty(self.B, self.Sq, self.H, self.D, device="cuda", dtype=bf)
         self.lse = torch.empty(self.B, self.Sq, self.H, device="cuda", dtype=torch.float32)
+        self.ws = _workspace(uaa, d0["q"], [d0["k"][:, a:b] for a, b in self.kv], self.masks)
         # allowed (query, key) pairs of each launch, from the position maps
         self.pairs = []
         for (a, b), m in zip(self.kv, self.masks):
@@ -267,7 +281,7 @@ class RingShare:
         if name == "attn":
             for c, (a, b) in enumerate(self.kv):
                 uaa.usp_attn_fwd_lse(d["q"], d["k"][:, a:b], d["v"][:, a:b], self.o_part[c], self.l_part[c],
-                                     self.scale, self.masks[c])
+                                     self.scale, self.masks[c], workspace=self.ws)
             return len(self.kv)
         if name == "merge":
             uaa.usp_lse_merge(self.o_part, self.l_part, self.o, self.lse)

@@ -37,6 +37,7 @@
 #ifndef UAA_H
 #define UAA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -186,6 +187,45 @@ int usp_attn_fwd_lse(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, in
                      const void* q, const void* k, const void* v,
                      void* o, int o_dtype, float* lse,
                      float scale, const usp_mask* mask, void* stream);
+
+/*
+ * usp_attn_fwd_lse_ws -- usp_attn_fwd_lse with a caller-owned device
+ * workspace, for shapes whose work does not divide evenly over the compute
+ * units.  The plain call runs one workgroup per 256 query rows of one
+ * (batch, head) -- a "unit" -- one workgroup per compute unit at a time, so
+ * e.g. 336 units on 256 compute units take two full rounds.  With a
+ * workspace, bf16 input and USP_MASK_FULL, the kernel instead keeps
+ * floor(units / CUs) rounds' worth of units whole and cuts the keys of each
+ * remaining unit into p <= 8 pieces of about equal length, each run by its
+ * own workgroup ahead of the whole units; the last piece of a unit to finish
+ * merges the pieces' partial states in fp32 -- the Ring merge of key blocks
+ * ([USP]) done inside the kernel -- in piece order, so the result does not
+ * depend on timing.  It equals the plain call's up to rounding (the bf16
+ * probabilities of a piece are taken relative to that piece's maximum).
+ *
+ *   workspace  device, 256-byte aligned, at least
+ *              usp_attn_workspace_bytes(...) bytes, zero-filled before its
+ *              first use; every call leaves it zero-filled again where it
+ *              matters (the arrival counters).  NULL, or fewer bytes than
+ *              needed: the plain call.
+ * Calls that share a workspace must not run concurrently (stream order is
+ * enough).  Every other argument is that of usp_attn_fwd_lse.
+ * Returns UAA_OK, UAA_ERR_INVALID_ARG, UAA_ERR_UNSUPPORTED or UAA_ERR_HIP.
+ */
+int usp_attn_fwd_lse_ws(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                        const void* q, const void* k, const void* v, void* o, int o_dtype,
+                        float* lse, float scale, const usp_mask* mask, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * usp_attn_workspace_bytes -- device workspace usp_attn_fwd_lse_ws uses for
+ * this problem on the current device: 0 when it would run as the plain call
+ * (fp32, a causal-family mask, or no split that saves at least 8 % by a
+ * round-count model); otherwise 136 KiB per piece plus 4 bytes per split
+ * unit.  Arguments as for usp_attn_fwd_lse; invalid ones give 0.
+ */
+size_t usp_attn_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                const usp_mask* mask);
 
 /*
  * usp_lse_merge -- merge N partial (O, LSE) pairs of the same query rows,

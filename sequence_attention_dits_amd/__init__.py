@@ -27,6 +27,7 @@ from .binding import (  # noqa: F401
     mask_full,
     mask_stripe,
     mask_zigzag,
+    attn_workspace,
     usp_attn_fwd_lse,
     usp_lse_merge,
     usp_mask,

@@ -106,6 +106,11 @@ def lib() -> ctypes.CDLL:
         l.usp_attn_fwd_lse.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                        _c_p, _c_p, _c_p, _c_p, ctypes.c_int, _c_p,
                                        ctypes.c_float, ctypes.POINTER(usp_mask), _c_p]
+        l.usp_attn_fwd_lse_ws.restype = ctypes.c_int
+        l.usp_attn_fwd_lse_ws.argtypes = l.usp_attn_fwd_lse.argtypes[:-1] + [_c_p, ctypes.c_size_t, _c_p]
+        l.usp_attn_workspace_bytes.restype = ctypes.c_size_t
+        l.usp_attn_workspace_bytes.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                               ctypes.POINTER(usp_mask)]
         l.usp_lse_merge.restype = ctypes.c_int
         l.usp_lse_merge.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_int,
                                     _c_p, _c_p, ctypes.c_int, _c_p, _c_p]
@@ -226,9 +231,26 @@ def uaa_seq2head_permute_multi(direction: int, rank: int, srcs: Sequence[Sequenc
                                             _stream(dsts[0])))
 
 
+def attn_workspace(q: torch.Tensor, k: torch.Tensor, mask: Optional[usp_mask] = None) -> Optional[torch.Tensor]:
+    """A zero-filled device workspace for usp_attn_fwd_lse(..., workspace=) for
+    this problem on q's device, or None when the call would not use one."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k are [B, S, H, D]")
+    B, Sq, H, D = q.shape
+    m = mask if mask is not None else mask_full()
+    with torch.cuda.device(q.device):
+        n = lib().usp_attn_workspace_bytes(_code(q.dtype, "q"), B, H, Sq, k.shape[1], D, ctypes.byref(m))
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=q.device)
+
+
 def usp_attn_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
-                     lse: torch.Tensor, scale: float, mask: Optional[usp_mask] = None) -> None:
-    """Attention forward with LSE into caller-owned o [B,Sq,H,D], lse [B,Sq,H] fp32."""
+                     lse: torch.Tensor, scale: float, mask: Optional[usp_mask] = None,
+                     workspace: Optional[torch.Tensor] = None) -> None:
+    """Attention forward with LSE into caller-owned o [B,Sq,H,D], lse [B,Sq,H] fp32.
+    With a workspace from attn_workspace() the call is usp_attn_fwd_lse_ws,
+    which may split each unit's keys over several workgroups."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse")):
         _dev(t, n)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
@@ -243,9 +265,17 @@ def usp_attn_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch
         raise ValueError("o must be shaped like q and lse [B, Sq, H] float32")
     dt, odt = _code(q.dtype, "q"), _code(o.dtype, "o")
     m = mask if mask is not None else mask_full()
-    _check(lib().usp_attn_fwd_lse(dt, B, H, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                  o.data_ptr(), odt, lse.data_ptr(), float(scale), ctypes.byref(m),
-                                  _stream(q)))
+    if workspace is None:
+        _check(lib().usp_attn_fwd_lse(dt, B, H, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                      o.data_ptr(), odt, lse.data_ptr(), float(scale), ctypes.byref(m),
+                                      _stream(q)))
+        return
+    _dev(workspace, "workspace")
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor (see attn_workspace)")
+    _check(lib().usp_attn_fwd_lse_ws(dt, B, H, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     o.data_ptr(), odt, lse.data_ptr(), float(scale), ctypes.byref(m),
+                                     workspace.data_ptr(), workspace.numel(), _stream(q)))
 
 
 def usp_lse_merge(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor],

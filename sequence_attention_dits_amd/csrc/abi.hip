@@ -3,8 +3,11 @@
 // arguments, and one asynchronous launch on the caller's stream.  Nothing
 // here synchronises the device or reads device memory.
 #include <math.h>
+#include <stddef.h>
 #include <stdarg.h>
 #include <stdio.h>
+
+#include <atomic>
 
 #include "internal.h"
 
@@ -209,9 +212,49 @@ int side_map(const usp_mask& m, bool q_side, int64_t n, uaa::PosMap& out)
 
 }  // namespace
 
-UAA_EXPORT int usp_attn_fwd_lse(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
-                                const void* q, const void* k, const void* v, void* o, int o_dtype,
-                                float* lse, float scale, const usp_mask* mask, void* stream)
+// Compute units of the current device (cached per device).
+static int device_cu_count()
+{
+    static std::atomic<int> cached[64];   // 0: not yet asked
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Key split the bf16 kernel would use for this problem on the current
+// device with a workspace (p = 1: unsplit).
+static uaa::SplitPlan attn_split_plan(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                      const usp_mask* mask)
+{
+    uaa::SplitPlan none;
+    if (dtype != UAA_BF16 || (D != 64 && D != 128) || B <= 0 || H <= 0 || Sq <= 0 || Sk <= 0) return none;
+    if (mask != nullptr && mask->kind != USP_MASK_FULL) return none;
+    if ((double)B * (Sq > Sk ? Sq : Sk) * H * D > (double)kMaxElems) return none;
+    const int64_t units = uaa::attn_bf16_units(B, H, Sq);
+    if (units > kMaxIdx32 / 8) return none;
+    return uaa::plan_split(units, (Sk + 63) / 64, device_cu_count());
+}
+
+static int64_t plan_ws_bytes(const uaa::SplitPlan& plan, int64_t B, int64_t H, int64_t Sq)
+{
+    if (plan.p <= 1) return 0;
+    return uaa::split_ws_bytes(uaa::attn_bf16_units(B, H, Sq) - plan.n_whole, plan.p);
+}
+
+UAA_EXPORT size_t usp_attn_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                           const usp_mask* mask)
+{
+    return (size_t)plan_ws_bytes(attn_split_plan(dtype, B, H, Sq, Sk, D, mask), B, H, Sq);
+}
+
+static int attn_impl(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, const void* q,
+                     const void* k, const void* v, void* o, int o_dtype, float* lse, float scale,
+                     const usp_mask* mask, void* workspace, size_t workspace_bytes, void* stream)
 {
     if (dtype != UAA_BF16 && dtype != UAA_FP32)
         return fail(UAA_ERR_INVALID_ARG, "attn: dtype must be UAA_BF16 or UAA_FP32, got %d", dtype);
@@ -261,9 +304,36 @@ UAA_EXPORT int usp_attn_fwd_lse(int dtype, int64_t B, int64_t H, int64_t Sq, int
         return fail(UAA_ERR_UNSUPPORTED, "attn: one batch of q or k/v must stay below 4 GiB");
     // the launcher sets the q-tile count for its tile height; bound the grid here
     if (((Sq + 63) / 64) * H * B >= kMaxIdx32) return fail(UAA_ERR_INVALID_ARG, "attn: grid too large");
+    a.split_p = 1;
+    a.n_whole = 0;
+    if (workspace != nullptr) {
+        if (!aligned(workspace, 256)) return fail(UAA_ERR_INVALID_ARG, "attn: workspace must be 256-byte aligned");
+        const uaa::SplitPlan plan = attn_split_plan(dtype, B, H, Sq, Sk, D, mask);
+        if (plan.p > 1 && workspace_bytes >= (size_t)plan_ws_bytes(plan, B, H, Sq)) {
+            a.split_p = plan.p;
+            a.n_whole = plan.n_whole;
+            a.ws = workspace;
+        }
+    }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == UAA_BF16) return hip_status(uaa::launch_attn_bf16((int)D, o_dtype, a, s), "attn launch");
     return hip_status(uaa::launch_attn_fp32((int)D, a, s), "attn launch");
+}
+
+UAA_EXPORT int usp_attn_fwd_lse(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                const void* q, const void* k, const void* v, void* o, int o_dtype,
+                                float* lse, float scale, const usp_mask* mask, void* stream)
+{
+    return attn_impl(dtype, B, H, Sq, Sk, D, q, k, v, o, o_dtype, lse, scale, mask, nullptr, 0, stream);
+}
+
+UAA_EXPORT int usp_attn_fwd_lse_ws(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                   const void* q, const void* k, const void* v, void* o, int o_dtype,
+                                   float* lse, float scale, const usp_mask* mask, void* workspace,
+                                   size_t workspace_bytes, void* stream)
+{
+    return attn_impl(dtype, B, H, Sq, Sk, D, q, k, v, o, o_dtype, lse, scale, mask, workspace, workspace_bytes,
+                     stream);
 }
 
 UAA_EXPORT int usp_lse_merge(int n_parts, int64_t B, int64_t S, int64_t H, int64_t D,

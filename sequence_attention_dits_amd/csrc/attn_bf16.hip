@@ -108,7 +108,7 @@ __device__ __forceinline__ void fill_k(const unsigned char* ksrc, uint32_t nrec,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kd + n * 1024, 16, off, 0, 0, 0);
 }
 
-template <int D, bool MASKED, bool OUT_BF16>
+template <int D, bool MASKED, bool OUT_BF16, bool SPLIT>
 __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a)
 {
     constexpr int UPR = D / 8;               // 16-byte units per row
@@ -126,7 +126,25 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
     __shared__ __attribute__((aligned(1024))) unsigned char smem[3 * TB + 2 * VTB];   // K stages 0..2, V stages 0..1
 
     int64_t qt, hh, b;
-    decode_tile(a, qt, hh, b);
+    uint32_t unit = 0;   // with SPLIT: this workgroup runs key piece `piece` of `np` of this unit
+    int piece = 0, np = 1;
+    if constexpr (SPLIT) {
+        // The pieces of the split units come first, so that they are
+        // dispatched first and their combine overlaps the whole units' work;
+        // then the whole units.  Each range is XCD-grouped on its own.
+        const uint32_t L = blockIdx.x, nw = (uint32_t)a.n_whole, npc = gridDim.x - nw;
+        if (L < npc) {
+            const uint32_t l = xcd_logical(L, npc);
+            np = a.split_p;
+            unit = nw + l / (uint32_t)np;
+            piece = (int)(l % (uint32_t)np);
+        } else {
+            unit = xcd_logical(L - npc, nw);
+        }
+        unit_coords(a, unit, qt, hh, b);
+    } else {
+        decode_tile(a, qt, hh, b);
+    }
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -175,7 +193,10 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
         lim0 = (int32_t)allowed_prefix(a.kmap.base0, a.kmap.stride, qp, segk);
         lim1 = segk + (int32_t)allowed_prefix(a.kmap.base1, a.kmap.stride, qp, Sk - segk);
     }
-    const int n_tiles = (int)((Sk + kBN - 1) / kBN);
+    // key tiles [t_beg, n_tiles) of this workgroup: all of them, or one piece
+    const int n_all = (int)((Sk + kBN - 1) / kBN);
+    const int t_beg = SPLIT ? (int)((int64_t)piece * n_all / np) : 0;
+    const int n_tiles = SPLIT ? (int)((int64_t)(piece + 1) * n_all / np) : n_all;
     auto tile_live = [&](int t) -> bool {  // may any row of the workgroup see a key of tile t?
         if (!MASKED) return true;
         const int64_t j0 = (int64_t)t * kBN;
@@ -300,7 +321,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
 
     // Loads run two tiles ahead: K through three LDS stages, V through two
     // register sets and two LDS stages.
-    int t = next_live(0);
+    int t = next_live(t_beg);
     int t1 = t < n_tiles ? next_live(t + 1) : n_tiles;
     int ks = 0;   // K stage of tile t
     if (t < n_tiles) {
@@ -494,6 +515,82 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
         while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
         }
 
+    if (SPLIT && np > 1) {
+        // Every piece stores its partial state (O accumulators, reference
+        // maximum, half-row sum, as the registers hold them) in its slot and
+        // counts in; the last piece of the unit to arrive combines all slots
+        // in piece order -- the same loads and arithmetic whichever piece it
+        // is, so the result does not depend on timing -- resets the counter
+        // and writes the output.  Pieces may run on different XCDs, whose L2
+        // caches are not coherent with each other: the state moves with
+        // device-scope (L2-bypassing) loads and stores, so no cache-wide
+        // write-back or invalidate is needed, only the order of this wave's
+        // stores before its count.
+        unsigned char* wsb = static_cast<unsigned char*>(a.ws);
+        const uint32_t su = unit - (uint32_t)a.n_whole;   // index among the split units
+        const int64_t n_split = (int64_t)(gridDim.x - (uint32_t)a.n_whole) / np;
+        int32_t* cnt = reinterpret_cast<int32_t*>(wsb + n_split * np * kSplitSlotBytes) + su;
+        // The unit's np slots; in slot q, 16-byte quad r of lane tid sits at
+        // ((q * kSplitQuads + r) * kSplitLanes + tid) * 16: quads below 4 NDB
+        // are the O accumulators, quad 4 NDB holds the maximum and half-row sum.
+        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+            wsb + (int64_t)su * np * kSplitSlotBytes, (short)0, (int)(np * kSplitSlotBytes), 0x00020000);
+        constexpr int kDev = 16;   // cache policy sc1: device-scope access
+        const int voff = tid * 16;
+        auto qoff = [&](int q, int r) { return (q * (int)kSplitQuads + r) * (int)(kSplitLanes * 16); };
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const u32x4 w{__float_as_uint(oacc[db][4 * g]), __float_as_uint(oacc[db][4 * g + 1]),
+                              __float_as_uint(oacc[db][4 * g + 2]), __float_as_uint(oacc[db][4 * g + 3])};
+                __builtin_amdgcn_raw_buffer_store_b128(w, wr, voff, qoff(piece, 4 * db + g), kDev);
+            }
+        {
+            const u32x4 w{__float_as_uint(m), __float_as_uint(lsum), 0u, 0u};
+            __builtin_amdgcn_raw_buffer_store_b128(w, wr, voff, qoff(piece, 4 * NDB), kDev);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the stores above are complete
+        __syncthreads();
+        volatile int* flag = reinterpret_cast<volatile int*>(smem);
+        if (tid == 0) *flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (*flag != np - 1) return;   // pieces of this unit are still running; the last one finishes it
+        auto ldq = [&](int q, int r) { return __builtin_amdgcn_raw_buffer_load_b128(wr, voff, qoff(q, r), kDev); };
+        {
+            const u32x4 ml = ldq(0, 4 * NDB);
+            m = __uint_as_float(ml[0]);
+            lsum = __uint_as_float(ml[1]);
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const u32x4 w = ldq(0, 4 * db + g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) oacc[db][4 * g + e] = __uint_as_float(w[e]);
+            }
+        for (int q = 1; q < np; ++q) {
+            const u32x4 ml = ldq(q, 4 * NDB);
+            const float mq = __uint_as_float(ml[0]), lq = __uint_as_float(ml[1]);
+            const float mm = __builtin_elementwise_maximum(m, mq);
+            const float w0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+            const float w1 = mq == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq - mm);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const u32x4 w = ldq(q, 4 * db + g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        oacc[db][4 * g + e] = fmaf(__uint_as_float(w[e]), w1, oacc[db][4 * g + e] * w0);
+                }
+            lsum = fmaf(lq, w1, lsum * w0);
+            m = mm;
+        }
+        if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
     // ---- epilogue: normalise, write O and the natural-log LSE -----------
     float lt;
     {
@@ -525,16 +622,54 @@ template <int D, bool OB>
 static hipError_t launch_d(const AttnArgs& a, dim3 grid, hipStream_t s)
 {
     const dim3 block(64 * kWaves);
-    if (a.masked) return launch_kernel(attn_bf16_kernel<D, true, OB>, grid, block, 0, s, a);
-    return launch_kernel(attn_bf16_kernel<D, false, OB>, grid, block, 0, s, a);
+    if (a.masked) return launch_kernel(attn_bf16_kernel<D, true, OB, false>, grid, block, 0, s, a);
+    if (a.split_p > 1) return launch_kernel(attn_bf16_kernel<D, false, OB, true>, grid, block, 0, s, a);
+    return launch_kernel(attn_bf16_kernel<D, false, OB, false>, grid, block, 0, s, a);
+}
+
+int64_t attn_bf16_units(int64_t B, int64_t H, int64_t Sq) { return ((Sq + kBM - 1) / kBM) * H * B; }
+
+// One workgroup runs on each compute unit at a time, so U units of N key
+// tiles on C compute units take ceil(U / C) rounds of N tile times, the last
+// one partial when C does not divide U.  The plan keeps f = floor(U / C)
+// rounds' worth of units whole and cuts each of the other r = U - f C units
+// into p pieces, r p <= C, which run first: f N + N / p + e tile times, with
+// e ~ 1.5 tile times for a piece's start-up and combine when the combine
+// overlaps whole units' work (f >= 1) and ~ 3 when it does not.  Picks the
+// best p <= 8 (pieces of at least 4 tiles), and no split unless it saves at
+// least 8 %.
+SplitPlan plan_split(int64_t n_units, int64_t n_tiles, int n_cu)
+{
+    SplitPlan plan;
+    if (n_cu <= 0 || n_units <= 0 || n_tiles < 8) return plan;
+    const int64_t f = n_units / n_cu, r = n_units - f * n_cu;
+    if (r == 0) return plan;
+    const double e = f >= 1 ? 1.5 : 3.0;
+    const double base = (double)(f + 1) * (double)n_tiles;
+    double best = base;
+    for (int p = 2; p <= 8 && n_tiles / p >= 4 && r * p <= n_cu; ++p) {
+        const double t = (double)f * n_tiles + (double)n_tiles / p + e;
+        if (t < best) {
+            best = t;
+            plan.p = p;
+        }
+    }
+    if (!(best < 0.92 * base)) plan.p = 1;
+    plan.n_whole = plan.p > 1 ? f * n_cu : 0;
+    return plan;
 }
 
 hipError_t launch_attn_bf16(int D, int o_dtype, const AttnArgs& a0, hipStream_t s)
 {
     AttnArgs a = a0;
     a.n_qtiles = (int32_t)((a.Sq + kBM - 1) / kBM);
-    const int64_t blocks = (int64_t)a.n_qtiles * a.H * a.B;
-    if (blocks <= 0) return hipSuccess;
+    const int64_t units = (int64_t)a.n_qtiles * a.H * a.B;
+    if (units <= 0) return hipSuccess;
+    if (a.masked || a.ws == nullptr || a.split_p <= 1 || a.n_whole < 0 || a.n_whole >= units) {
+        a.split_p = 1;
+        a.n_whole = 0;
+    }
+    const int64_t blocks = a.split_p > 1 ? a.n_whole + (units - a.n_whole) * a.split_p : units;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks);
     const bool ob = o_dtype == UAA_BF16;

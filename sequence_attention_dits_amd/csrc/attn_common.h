@@ -41,19 +41,28 @@ __device__ __forceinline__ int64_t allowed_prefix(int64_t base, int64_t stride, 
     return c < n ? c : n;
 }
 
-// Workgroup index -> (q tile, head, batch).  Workgroups are handed to the
-// 8 XCDs round-robin, and each XCD has its own L2: renumber so that each XCD
-// gets one contiguous run of logical tiles, i.e. the q tiles of the same head
-// share the L2 that holds that head's K and V.
-__device__ __forceinline__ void decode_tile(const AttnArgs& a, int64_t& qt, int64_t& h, int64_t& b)
+// Workgroup index -> logical work index.  Workgroups are handed to the 8
+// XCDs round-robin, and each XCD has its own L2: renumber so that each XCD
+// gets one contiguous run of logical indices, i.e. the q tiles of the same
+// head share the L2 that holds that head's K and V.
+__device__ __forceinline__ uint32_t xcd_logical(uint32_t L, uint32_t n)
 {
-    const uint32_t n = gridDim.x, L = blockIdx.x;
     const uint32_t per = n / 8u;
-    const uint32_t logical = (L < per * 8u) ? (L % 8u) * per + L / 8u : L;
-    qt = logical % (uint32_t)a.n_qtiles;
-    const int64_t rest = logical / (uint32_t)a.n_qtiles;
+    return (L < per * 8u) ? (L % 8u) * per + L / 8u : L;
+}
+
+// Logical unit -> (q tile, head, batch).
+__device__ __forceinline__ void unit_coords(const AttnArgs& a, uint32_t unit, int64_t& qt, int64_t& h, int64_t& b)
+{
+    qt = unit % (uint32_t)a.n_qtiles;
+    const int64_t rest = unit / (uint32_t)a.n_qtiles;
     h = rest % a.H;
     b = rest / a.H;
+}
+
+__device__ __forceinline__ void decode_tile(const AttnArgs& a, int64_t& qt, int64_t& h, int64_t& b)
+{
+    unit_coords(a, xcd_logical(blockIdx.x, gridDim.x), qt, h, b);
 }
 
 }  // namespace uaa

@@ -88,7 +88,33 @@ struct AttnArgs {
     int32_t masked;       // 0: every key allowed; 1: kpos(j) <= qpos(i)
     PosMap qmap, kmap;
     int32_t n_qtiles;     // ceil(Sq / rows per workgroup), set by the launcher
+    // Key split (bf16, unmasked): units [0, n_whole) run whole, one
+    // workgroup each; the keys of every later unit (those of the last,
+    // partial round of workgroups) are cut into split_p pieces of about
+    // equal length, each run by its own workgroup, and the last piece of a
+    // unit to finish combines the pieces.
+    int32_t split_p;      // 1: no split
+    int32_t n_whole;      // units run whole, set by the caller with split_p
+    void* ws;             // workspace: piece partials, then arrival counters
 };
+
+// Workspace of the key split: one partial slot per piece of a split unit
+// (the 512 lanes' O accumulators and each lane's reference maximum and
+// half-row sum), then one int32 arrival counter per split unit.
+constexpr int64_t kSplitLanes = 512;
+constexpr int64_t kSplitQuads = 17;   // 16-byte quads per lane: 16 of O accumulators, 1 of (max, sum)
+constexpr int64_t kSplitSlotBytes = kSplitLanes * kSplitQuads * 16;
+
+struct SplitPlan {
+    int p = 1;            // pieces per split unit; 1: no split
+    int64_t n_whole = 0;  // units run whole
+};
+inline int64_t split_ws_bytes(int64_t n_split, int p) { return n_split * p * kSplitSlotBytes + 4 * n_split; }
+
+// Split plan for n_units units of n_tiles key tiles on n_cu compute units,
+// and the unit count of the bf16 kernel.
+SplitPlan plan_split(int64_t n_units, int64_t n_tiles, int n_cu);
+int64_t attn_bf16_units(int64_t B, int64_t H, int64_t Sq);
 
 hipError_t launch_attn_bf16(int D, int o_dtype, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_fp32(int D, const AttnArgs& a, hipStream_t s);

@@ -25,7 +25,8 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert {"uaa_seq2head_permute", "usp_attn_fwd_lse", "usp_lse_merge", "uaa_last_error"} <= set(names)
+    assert {"uaa_seq2head_permute", "usp_attn_fwd_lse", "usp_attn_fwd_lse_ws", "usp_attn_workspace_bytes",
+            "usp_lse_merge", "uaa_last_error"} <= set(names)
     lib = uaa.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -124,6 +125,31 @@ def _attn(dtype=0, B=1, H=1, Sq=4, Sk=4, D=128, q=FAKE, k=FAKE, v=FAKE, o=FAKE, 
 def test_attention_validation(kw, code, text):
     rc, msg = _attn(**kw)
     assert rc == code and text in msg, (rc, msg)
+
+
+def _attn_ws(ws, nbytes, dtype=0, D=128, mask=None):
+    lib = uaa.lib()
+    m = mask if mask is not None else uaa.mask_full()
+    rc = lib.usp_attn_fwd_lse_ws(dtype, 1, 1, 4, 4, D, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0.1, ctypes.byref(m),
+                                 ws, nbytes, None)
+    return rc, lib.uaa_last_error().decode()
+
+
+def test_workspace_call_validates_like_the_plain_call():
+    assert _attn_ws(FAKE, 1 << 20, dtype=5) == (-1, _attn(dtype=5)[1])
+    assert _attn_ws(FAKE, 1 << 20, D=96)[0] == -2
+    rc, msg = _attn_ws(FAKE + 16, 1 << 20)
+    assert rc == -1 and "256-byte" in msg, (rc, msg)
+
+
+def test_workspace_bytes_zero_where_no_split_applies():
+    lib = uaa.lib()
+    full, causal = uaa.mask_full(), uaa.mask_causal(0, 0)
+    big = (1, 24, 3493, 3493)   # B, H, Sq, Sk
+    assert lib.usp_attn_workspace_bytes(1, *big, 128, ctypes.byref(full)) == 0       # fp32
+    assert lib.usp_attn_workspace_bytes(0, *big, 128, ctypes.byref(causal)) == 0     # masked
+    assert lib.usp_attn_workspace_bytes(0, *big, 96, ctypes.byref(full)) == 0        # head dim
+    assert lib.usp_attn_workspace_bytes(0, 1, 24, -1, 3493, 128, ctypes.byref(full)) == 0
 
 
 def test_attention_empty_work_is_ok():

@@ -166,12 +166,15 @@ def test_flux_shares_sampled_rows(cfg):
     check_pair(host_f64(o[0, rows]), host_f64(lse[0, rows]), o_ref, l_ref, "bf16", "cfg%d" % cfg)
 
 
-def test_qwen_ring_share_two_chunks_and_merge():
-    """Qwen-Image Ring share: Q = tokens 0..3492, K/V in 2 chunks of 3493."""
+@pytest.mark.parametrize("split", [False, True], ids=["plain", "key_split"])
+def test_qwen_ring_share_two_chunks_and_merge(split):
+    """Qwen-Image Ring share: Q = tokens 0..3492, K/V in 2 chunks of 3493;
+    with key_split each chunk's launch runs with a workspace (336 units on
+    256 compute units: the last 80 are split)."""
     c = synth.CONFIGS[4]
     B, S, H, D = c["B"], c["S"], c["H"], c["D"]
     Sq = S // 2
-    say("attn cfg4: generating inputs")
+    say("attn cfg4: generating inputs", "key split" if split else "plain")
     qb, qv = _load(4, 0, (B, S, H, D), "bf16", True)
     kb, kv_ = _load(4, 1, (B, S, H, D), "bf16", True)
     vb, vv = _load(4, 2, (B, S, H, D), "bf16", False)
@@ -179,7 +182,17 @@ def test_qwen_ring_share_two_chunks_and_merge():
     ks = [dev(np.ascontiguousarray(kb[:, a:a + Sq]), "bf16") for a in (0, Sq)]
     vs = [dev(np.ascontiguousarray(vb[:, a:a + Sq]), "bf16") for a in (0, Sq)]
     scale = float(np.float32(1.0 / math.sqrt(D)))
-    parts = [_attn(q, ks[n], vs[n], scale) for n in range(2)]
+    if split:
+        ws = uaa.attn_workspace(q, ks[0])
+        assert ws is not None
+        parts = []
+        for n in range(2):
+            o_n = torch.empty_like(q)
+            l_n = torch.empty(q.shape[:3], device="cuda", dtype=torch.float32)
+            uaa.usp_attn_fwd_lse(q, ks[n], vs[n], o_n, l_n, scale, workspace=ws)
+            parts.append((o_n, l_n))
+    else:
+        parts = [_attn(q, ks[n], vs[n], scale) for n in range(2)]
     o = torch.empty_like(parts[0][0])
     lse = torch.empty_like(parts[0][1])
     uaa.usp_lse_merge([p[0] for p in parts], [p[1] for p in parts], o, lse)
