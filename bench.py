@@ -66,6 +66,11 @@ WORKLOADS = {
                    "32 heads, D=128, bf16, K/V over all 8 chunks masked by global position, 8-way LSE merge"),
 }
 RING_WORKLOADS = ("qwen1328", "longctx")
+# Workloads whose chunk launches run on two streams by default.  Measured:
+# the 8 masked long-context launches gain ~5 % (their skipped tiles leave
+# compute units idle); the FLUX and Qwen chunks lose 3-6 % (two chunks' K/V
+# no longer fit the per-XCD L2 together).
+OVERLAP_WORKLOADS = ("longctx",)
 
 
 def parse():
@@ -74,6 +79,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="flux1024", choices=sorted(WORKLOADS))
+    p.add_argument("--overlap-chunks", choices=["auto", "on", "off"], default="auto",
+                   help="run the Ring chunks' attention launches on two streams (auto: per workload)")
     p.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough for 1 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -89,7 +96,7 @@ def parse():
 class Share:
     """Device buffers of one workload and the launches of one step."""
 
-    def __init__(self, cfg_id: int, n_sets: int):
+    def __init__(self, cfg_id: int, n_sets: int, overlap_chunks: bool = False):
         import numpy as np
         import torch
 
@@ -97,6 +104,7 @@ class Share:
         import sequence_attention_dits_amd as uaa
         self.uaa = uaa
         self.torch = torch
+        self.overlap_chunks = overlap_chunks
         c = synth.CONFIGS[cfg_id]
         self.B, self.S, self.H, self.D = c["B"], c["S"], c["H"], c["D"]
         self.P = 2
@@ -128,7 +136,11 @@ class Share:
         self.l_part = [torch.empty(B, S, Hr, device="cuda", dtype=torch.float32) for _ in self.ring]
         self.o = torch.empty(B, S, Hr, D, device="cuda", dtype=bf)
         self.lse = torch.empty(B, S, Hr, device="cuda", dtype=torch.float32)
-        self.ws = _workspace(self.uaa, self.qh["q"], [kc for kc, _ in self.kc], [None] * len(self.kc))
+        # the chunk launches alternate between two streams (below); each
+        # stream has its own split workspace, if the shape asks for one
+        self.ws = [_workspace(self.uaa, self.qh["q"], [kc for kc, _ in self.kc], [None] * len(self.kc))
+                   for _ in range(2)]
+        self.side = torch.cuda.Stream()   # default priority
         S0 = self.seq_off[1]
         self.o_tok = torch.empty(B, S0, H, D, device="cuda", dtype=bf)
         self.l_tok = torch.empty(B, S0, H, 1, device="cuda", dtype=torch.float32)
@@ -161,9 +173,8 @@ class Share:
             self._seq2head_qkv(s)
             return 1
         if name == "attn":
-            for c, (kc, vc) in enumerate(self.kc):
-                uaa.usp_attn_fwd_lse(self.qh["q"], _contig(kc), _contig(vc), self.o_part[c], self.l_part[c],
-                                     self.scale, workspace=self.ws)
+            for c in range(len(self.kc)):
+                self.attn_chunk(s, c, self.ws[0])
             return len(self.kc)
         if name == "merge":
             uaa.usp_lse_merge(self.o_part, self.l_part, self.o, self.lse)
@@ -180,22 +191,54 @@ class Share:
 
     kernel_names = ("permute", "permute_qkv", "attn", "merge", "head2seq", "head2seq_lse")
 
+    def attn_chunk(self, s, c, ws):
+        kc, vc = self.kc[c]
+        self.uaa.usp_attn_fwd_lse(self.qh["q"], _contig(kc), _contig(vc), self.o_part[c], self.l_part[c],
+                                  self.scale, workspace=ws)
+
     def result(self):
         return self.o_tok, self.l_tok
 
     def step(self, s):
-        """Enqueue one step on input set s."""
-        for name in ("permute3", "attn", "merge", "head2seq", "head2seq_lse"):
-            if name == "permute3":
-                self._seq2head_qkv(s)
-            else:
-                self.launch_one(name, s)
+        """Enqueue one step on input set s: the Q/K/V gather, the attention
+        of every Ring chunk (independent launches; with overlap_chunks they
+        alternate between two streams, as the ring overlaps a chunk's arrival
+        with compute), the merge, then the O and LSE inverse gathers.  (The
+        two gathers on two streams measured slower: the fork and join inside
+        the graph cost more than the small launch they hide.)"""
+        torch = self.torch
+        main = torch.cuda.current_stream()
+        self._seq2head_qkv(s)
+        chunks = [lambda w, c=c: self.attn_chunk(s, c, w) for c in range(len(self.kc))]
+        if self.overlap_chunks:
+            _two_streams(torch, main, self.side, chunks, self.ws)
+        else:
+            for fn in chunks:
+                fn(self.ws[0])
+        self.launch_one("merge", s)
+        self.launch_one("head2seq", s)
+        self.launch_one("head2seq_lse", s)
 
     def _seq2head_qkv(self, s):
         uaa = self.uaa
         d = self.sets[s]
         uaa.uaa_seq2head_permute_multi(uaa.UAA_SEQ2HEAD, 0, [d[n] for n in "qkv"], [self.qh[n] for n in "qkv"],
                                        self.seq_off, self.head_off)
+
+
+def _two_streams(torch, main, side, launches, ws):
+    """Enqueue independent launches alternately on `main` and `side` (fork
+    after the work already on `main`, join before anything later on it);
+    launch i gets workspace ws[i % 2].  Under graph capture the fork and join
+    become graph edges."""
+    side.wait_stream(main)
+    for i, fn in enumerate(launches):
+        if i % 2 == 0:
+            fn(ws[0])
+        else:
+            with torch.cuda.stream(side):
+                fn(ws[1])
+    main.wait_stream(side)
 
 
 def _workspace(uaa, q, ks, masks):
@@ -216,7 +259,7 @@ class RingShare:
     the causal zigzag mask by global position where the layout has one), then
     the N-way LSE merge of the partials."""
 
-    def __init__(self, cfg_id: int, n_sets: int):
+    def __init__(self, cfg_id: int, n_sets: int, overlap_chunks: bool = False):
         import numpy as np
         import torch
 
@@ -224,6 +267,7 @@ class RingShare:
         import sequence_attention_dits_amd as uaa
         self.uaa = uaa
         self.torch = torch
+        self.overlap_chunks = overlap_chunks
         c = synth.CONFIGS[cfg_id]
         self.B, self.H, self.D = c["B"], c["H"], c["D"]
         self.scale = float(np.float32(1.0 / math.sqrt(self.D)))
@@ -254,7 +298,8 @@ class RingShare:
         self.l_part = [torch.empty(self.B, self.Sq, self.H, device="cuda", dtype=torch.float32) for _ in self.kv]
         self.o = torch.empty(self.B, self.Sq, self.H, self.D, device="cuda", dtype=bf)
         self.lse = torch.empty(self.B, self.Sq, self.H, device="cuda", dtype=torch.float32)
-        self.ws = _workspace(uaa, d0["q"], [d0["k"][:, a:b] for a, b in self.kv], self.masks)
+        self.ws = [_workspace(uaa, d0["q"], [d0["k"][:, a:b] for a, b in self.kv], self.masks) for _ in range(2)]
+        self.side = torch.cuda.Stream()   # default priority
         # allowed (query, key) pairs of each launch, from the position maps
         self.pairs = []
         for (a, b), m in zip(self.kv, self.masks):
@@ -279,17 +324,30 @@ class RingShare:
         uaa = self.uaa
         d = self.sets[s]
         if name == "attn":
-            for c, (a, b) in enumerate(self.kv):
-                uaa.usp_attn_fwd_lse(d["q"], d["k"][:, a:b], d["v"][:, a:b], self.o_part[c], self.l_part[c],
-                                     self.scale, self.masks[c], workspace=self.ws)
+            for c in range(len(self.kv)):
+                self.attn_chunk(s, c, self.ws[0])
             return len(self.kv)
         if name == "merge":
             uaa.usp_lse_merge(self.o_part, self.l_part, self.o, self.lse)
             return 1
         raise ValueError(name)
 
+    def attn_chunk(self, s, c, ws):
+        d = self.sets[s]
+        a, b = self.kv[c]
+        self.uaa.usp_attn_fwd_lse(d["q"], d["k"][:, a:b], d["v"][:, a:b], self.o_part[c], self.l_part[c],
+                                  self.scale, self.masks[c], workspace=ws)
+
     def step(self, s):
-        self.launch_one("attn", s)
+        """The attention of every chunk (on two streams with overlap_chunks,
+        see Share.step), then the N-way merge."""
+        torch = self.torch
+        chunks = [lambda w, c=c: self.attn_chunk(s, c, w) for c in range(len(self.kv))]
+        if self.overlap_chunks:
+            _two_streams(torch, torch.cuda.current_stream(), self.side, chunks, self.ws)
+        else:
+            for fn in chunks:
+                fn(self.ws[0])
         self.launch_one("merge", s)
 
     def result(self):
@@ -528,7 +586,8 @@ def main():
     else:
         per_set = 3 * c["B"] * c["S"] * c["H"] * c["D"] * 2 + c["B"] * c["S"] * (c["H"] // 2) * c["D"] * 2
     n_sets = args.sets or max(2, int(math.ceil((1 << 30) / per_set)))
-    share = RingShare(cfg_id, n_sets) if ring else Share(cfg_id, n_sets)
+    overlap = {"on": True, "off": False}.get(args.overlap_chunks, args.workload in OVERLAP_WORKLOADS)
+    share = RingShare(cfg_id, n_sets, overlap) if ring else Share(cfg_id, n_sets, overlap)
 
     for i in range(max(args.warmup, 1)):
         share.step(i % n_sets)
