@@ -514,6 +514,38 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
     if (t < n_tiles)
         while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
         }
+    // the copies the last step issued (into buffers nothing reads) land
+    // before the workgroup ends and its LDS can be reused
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+
+    // ---- epilogue: normalise, write O and the natural-log LSE -----------
+    // (acc, mref, ls): O accumulators, reference maximum, half-row sum
+    auto write_out = [&](const f32x16 (&acc)[NDB], float mref, float ls) {
+        float lt;
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ls), __float_as_uint(ls), false, false);
+            lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+        if (i >= Sq) return;
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const int64_t orow = ((b * Sq + i) * H + hh) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = 32 * db + 8 * g + 4 * hg;   // 4 consecutive features
+                const float x0 = acc[db][4 * g] * inv, x1 = acc[db][4 * g + 1] * inv;
+                const float x2 = acc[db][4 * g + 2] * inv, x3 = acc[db][4 * g + 3] * inv;
+                if (OUT_BF16) {
+                    u32x2 w{pack_bf16(x0, x1), pack_bf16(x2, x3)};
+                    *reinterpret_cast<u32x2*>(static_cast<unsigned short*>(a.o) + orow + d0) = w;
+                } else {
+                    u32x4 w{__float_as_uint(x0), __float_as_uint(x1), __float_as_uint(x2), __float_as_uint(x3)};
+                    *reinterpret_cast<u32x4*>(static_cast<float*>(a.o) + orow + d0) = w;
+                }
+            }
+        if (hg == 0) a.lse[(b * Sq + i) * H + hh] = lt > 0.f ? (mref + __log2f(lt)) * kLn2 : -INFINITY;
+    };
 
     if (SPLIT && np > 1) {
         // Every piece stores its partial state (O accumulators, reference
@@ -556,11 +588,15 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
         if (tid == 0) *flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         if (*flag != np - 1) return;   // pieces of this unit are still running; the last one finishes it
+        // The combine has registers of its own (the loop's accumulators are
+        // dead once stored) and writes the output itself.
         auto ldq = [&](int q, int r) { return __builtin_amdgcn_raw_buffer_load_b128(wr, voff, qoff(q, r), kDev); };
+        f32x16 cacc[NDB];
+        float cm, cl;
         {
             const u32x4 ml = ldq(0, 4 * NDB);
-            m = __uint_as_float(ml[0]);
-            lsum = __uint_as_float(ml[1]);
+            cm = __uint_as_float(ml[0]);
+            cl = __uint_as_float(ml[1]);
         }
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -568,13 +604,13 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
             for (int g = 0; g < 4; ++g) {
                 const u32x4 w = ldq(0, 4 * db + g);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) oacc[db][4 * g + e] = __uint_as_float(w[e]);
+                for (int e = 0; e < 4; ++e) cacc[db][4 * g + e] = __uint_as_float(w[e]);
             }
         for (int q = 1; q < np; ++q) {
             const u32x4 ml = ldq(q, 4 * NDB);
             const float mq = __uint_as_float(ml[0]), lq = __uint_as_float(ml[1]);
-            const float mm = __builtin_elementwise_maximum(m, mq);
-            const float w0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+            const float mm = __builtin_elementwise_maximum(cm, mq);
+            const float w0 = cm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(cm - mm);
             const float w1 = mq == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq - mm);
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -583,40 +619,18 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
                     const u32x4 w = ldq(q, 4 * db + g);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        oacc[db][4 * g + e] = fmaf(__uint_as_float(w[e]), w1, oacc[db][4 * g + e] * w0);
+                        cacc[db][4 * g + e] = fmaf(__uint_as_float(w[e]), w1, cacc[db][4 * g + e] * w0);
                 }
-            lsum = fmaf(lq, w1, lsum * w0);
-            m = mm;
+            cl = fmaf(lq, w1, cl * w0);
+            cm = mm;
         }
         if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        write_out(cacc, cm, cl);
+        return;
     }
-
-    // ---- epilogue: normalise, write O and the natural-log LSE -----------
-    float lt;
-    {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
-        lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    }
-    if (i >= Sq) return;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int64_t orow = ((b * Sq + i) * H + hh) * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int d0 = 32 * db + 8 * g + 4 * hg;   // 4 consecutive features
-            const float x0 = oacc[db][4 * g] * inv, x1 = oacc[db][4 * g + 1] * inv;
-            const float x2 = oacc[db][4 * g + 2] * inv, x3 = oacc[db][4 * g + 3] * inv;
-            if (OUT_BF16) {
-                u32x2 w{pack_bf16(x0, x1), pack_bf16(x2, x3)};
-                *reinterpret_cast<u32x2*>(static_cast<unsigned short*>(a.o) + orow + d0) = w;
-            } else {
-                u32x4 w{__float_as_uint(x0), __float_as_uint(x1), __float_as_uint(x2), __float_as_uint(x3)};
-                *reinterpret_cast<u32x4*>(static_cast<float*>(a.o) + orow + d0) = w;
-            }
-        }
-    if (hg == 0) a.lse[(b * Sq + i) * H + hh] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+    write_out(oacc, m, lsum);
 }
+
 
 template <int D, bool OB>
 static hipError_t launch_d(const AttnArgs& a, dim3 grid, hipStream_t s)
