@@ -526,25 +526,51 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ls), __float_as_uint(ls), false, false);
             lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         }
-        if (i >= Sq) return;
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        const int64_t orow = ((b * Sq + i) * H + hh) * D;
+        if constexpr (OUT_BF16) {
+            // The wave's 32 x D output tile goes through LDS (free once every
+            // wave has left the main loop and the last copies have landed) so
+            // that each global store writes whole rows: 4 rows of 256 bytes
+            // per instruction for D = 128, instead of 16-byte pieces of 32 rows.
+            constexpr int RS = D * 2 + 16;        // LDS row stride (bytes)
+            constexpr int UR = D * 2 / 16;        // 16-byte units per row
+            constexpr int RPI = 64 / UR;          // rows per store instruction
+            lds_barrier();
+            lds_u8* R = (lds_u8*)smem + wave * 32 * RS;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = 32 * db + 8 * g + 4 * hg;   // 4 consecutive features
-                const float x0 = acc[db][4 * g] * inv, x1 = acc[db][4 * g + 1] * inv;
-                const float x2 = acc[db][4 * g + 2] * inv, x3 = acc[db][4 * g + 3] * inv;
-                if (OUT_BF16) {
-                    u32x2 w{pack_bf16(x0, x1), pack_bf16(x2, x3)};
-                    *reinterpret_cast<u32x2*>(static_cast<unsigned short*>(a.o) + orow + d0) = w;
-                } else {
-                    u32x4 w{__float_as_uint(x0), __float_as_uint(x1), __float_as_uint(x2), __float_as_uint(x3)};
-                    *reinterpret_cast<u32x4*>(static_cast<float*>(a.o) + orow + d0) = w;
+                for (int g = 0; g < 4; ++g) {
+                    const int d0 = 32 * db + 8 * g + 4 * hg;   // 4 consecutive features
+                    const u32x2 w{pack_bf16(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv),
+                                  pack_bf16(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+                    *(__attribute__((address_space(3))) u32x2*)(R + l32 * RS + d0 * 2) = w;
                 }
+            const int rr = lane / UR, cu = lane % UR;
+#pragma unroll
+            for (int k = 0; k < 32 / RPI; ++k) {
+                const int r = RPI * k + rr;
+                const u32x4 w = *(const lds_u32x4*)(R + r * RS + cu * 16);
+                const int64_t row = q0 + 32 * wave + r;
+                if (row < Sq)
+                    *reinterpret_cast<u32x4*>(static_cast<unsigned char*>(a.o) + ((b * Sq + row) * H + hh) * D * 2 +
+                                              cu * 16) = w;
             }
-        if (hg == 0) a.lse[(b * Sq + i) * H + hh] = lt > 0.f ? (mref + __log2f(lt)) * kLn2 : -INFINITY;
+        } else {
+            if (i < Sq) {
+                const int64_t orow = ((b * Sq + i) * H + hh) * D;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int d0 = 32 * db + 8 * g + 4 * hg;   // 4 consecutive features
+                        u32x4 w{__float_as_uint(acc[db][4 * g] * inv), __float_as_uint(acc[db][4 * g + 1] * inv),
+                                __float_as_uint(acc[db][4 * g + 2] * inv), __float_as_uint(acc[db][4 * g + 3] * inv)};
+                        *reinterpret_cast<u32x4*>(static_cast<float*>(a.o) + orow + d0) = w;
+                    }
+            }
+        }
+        if (hg == 0 && i < Sq) a.lse[(b * Sq + i) * H + hh] = lt > 0.f ? (mref + __log2f(lt)) * kLn2 : -INFINITY;
     };
 
     if (SPLIT && np > 1) {
