@@ -12,9 +12,9 @@ rank = head rank 0 / token rank 0):
      as 2 Ring chunks of 2304                                   (2 launches)
   3. LSE merge of the 2 partial (O, LSE) pairs                  (1 launch)
   4. inverse gather (HEAD2SEQ) of O and of the LSE into this rank's token
-     shard; the other head rank's shard stands in for what the exchange
-     would deliver                                              (2 launches)
-  (6 launches per step)
+     shard, both in one launch; the other head rank's shard stands in for
+     what the exchange would deliver                            (1 launch)
+  (5 launches per step)
 
 value = attention FLOPs of the step (4*D*H*Sq*Sk = 130.46 GFLOP) / step time.
 Input sets rotate over more than 4x the 256 MB Infinity Cache so every
@@ -158,6 +158,9 @@ class Share:
         per = rows * self.D * 2 + rows * 4                             # bf16 O + fp32 LSE
         return 2 * per + per                                           # N=2 in, 1 out
 
+    def head2seq_lse_bytes(self):
+        return 2.0 * 4 * self.B * self.seq_off[1] * self.H
+
     def head2seq_bytes(self):
         return 2.0 * 2 * self.B * self.seq_off[1] * self.H * self.D
 
@@ -183,13 +186,19 @@ class Share:
             uaa.uaa_seq2head_permute(uaa.UAA_HEAD2SEQ, 0, [self.o, d["o_other"]], self.o_tok, self.seq_off,
                                      self.head_off)
             return 1
+        if name == "head2seq_o_lse":
+            # O and its LSE back to the token layout in one launch
+            uaa.uaa_seq2head_permute_multi(uaa.UAA_HEAD2SEQ, 0, [[self.o, d["o_other"]],
+                                                                 [self.lse.unsqueeze(-1), d["l_other"]]],
+                                           [self.o_tok, self.l_tok], self.seq_off, self.head_off)
+            return 1
         if name == "head2seq_lse":
             uaa.uaa_seq2head_permute(uaa.UAA_HEAD2SEQ, 0, [self.lse.unsqueeze(-1), d["l_other"]], self.l_tok,
                                      self.seq_off, self.head_off)
             return 1
         raise ValueError(name)
 
-    kernel_names = ("permute", "permute_qkv", "attn", "merge", "head2seq", "head2seq_lse")
+    kernel_names = ("permute", "permute_qkv", "attn", "merge", "head2seq", "head2seq_lse", "head2seq_o_lse")
 
     def attn_chunk(self, s, c, ws):
         kc, vc = self.kc[c]
@@ -203,9 +212,8 @@ class Share:
         """Enqueue one step on input set s: the Q/K/V gather, the attention
         of every Ring chunk (independent launches; with overlap_chunks they
         alternate between two streams, as the ring overlaps a chunk's arrival
-        with compute), the merge, then the O and LSE inverse gathers.  (The
-        two gathers on two streams measured slower: the fork and join inside
-        the graph cost more than the small launch they hide.)"""
+        with compute), the merge, then the inverse gather of O and its LSE
+        in one launch."""
         torch = self.torch
         main = torch.cuda.current_stream()
         self._seq2head_qkv(s)
@@ -216,8 +224,7 @@ class Share:
             for fn in chunks:
                 fn(self.ws[0])
         self.launch_one("merge", s)
-        self.launch_one("head2seq", s)
-        self.launch_one("head2seq_lse", s)
+        self.launch_one("head2seq_o_lse", s)
 
     def _seq2head_qkv(self, s):
         uaa = self.uaa
@@ -681,6 +688,8 @@ def main():
                                      "bytes": 3 * share.permute_bytes()},
             "head2seq_permute": {"us": round(h2s_us, 2), "GB/s": round(h2s_gbps, 1),
                                  "hbm_frac": round(h2s_gbps / PEAK_HBM_GBPS, 4), "bytes": share.head2seq_bytes()},
+            "head2seq_permute_o_lse": {"us": round(log["head2seq_o_lse"], 2),
+                                       "bytes": share.head2seq_bytes() + share.head2seq_lse_bytes()},
         })
         config = {"workload": desc, "B": share.B, "S": share.S, "heads_total": share.H, "heads_rank": share.Hr,
                   "D": share.D, "ulysses": share.P, "ring_chunks": n_attn, "attn_flops_per_step": attn_flops}

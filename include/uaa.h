@@ -157,6 +157,21 @@ int uaa_seq2head_permute_multi(int n_tensors, int dir, int rank, int world,
                                const void* const* src, void* const* dst, void* stream);
 
 /*
+ * uaa_seq2head_permute_multi_ex -- as uaa_seq2head_permute_multi, for
+ * tensors that share B, H and the token / head split but not the size of a
+ * head slice: tensor t has D[t] features of elem_bytes[t] bytes (host arrays
+ * of n_tensors entries).  The output O and its LSE (D = 1, 4 bytes) of the
+ * Unified path ([USP]) go back to the token layout in one launch this way.
+ * Each tensor moves in the widest access its head slice and pointers
+ * allow; the result equals n_tensors separate calls.
+ * Returns UAA_OK, UAA_ERR_INVALID_ARG, UAA_ERR_UNSUPPORTED or UAA_ERR_HIP.
+ */
+int uaa_seq2head_permute_multi_ex(int n_tensors, int dir, int rank, int world,
+                                  const int64_t* seq_off, const int64_t* head_off,
+                                  int64_t B, int64_t H, const int64_t* D, const int* elem_bytes,
+                                  const void* const* src, void* const* dst, void* stream);
+
+/*
  * usp_attn_fwd_lse -- softmax attention of one rank's query rows against
  * one block of keys/values, returning both the output and the per-row
  * log-sum-exp: the (out, lse) pair each Ring step produces ([USP]; [CP]

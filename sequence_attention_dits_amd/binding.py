@@ -102,6 +102,9 @@ def lib() -> ctypes.CDLL:
         l.uaa_seq2head_permute_multi.restype = ctypes.c_int
         l.uaa_seq2head_permute_multi.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_p,
                                                  _c_p, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_p, _c_p, _c_p]
+        l.uaa_seq2head_permute_multi_ex.restype = ctypes.c_int
+        l.uaa_seq2head_permute_multi_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_p,
+                                                    _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p]
         l.usp_attn_fwd_lse.restype = ctypes.c_int
         l.usp_attn_fwd_lse.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                        _c_p, _c_p, _c_p, _c_p, ctypes.c_int, _c_p,
@@ -212,23 +215,31 @@ def uaa_seq2head_permute(direction: int, rank: int, src: Sequence[torch.Tensor],
 def uaa_seq2head_permute_multi(direction: int, rank: int, srcs: Sequence[Sequence[torch.Tensor]],
                                dsts: Sequence[torch.Tensor], seq_off: Sequence[int],
                                head_off: Optional[Sequence[int]] = None) -> None:
-    """The same layout change for several same-shaped tensors (e.g. Q, K, V)
-    in one launch: srcs[t] are tensor t's shards, dsts[t] its destination."""
+    """The same layout change for several tensors in one launch: srcs[t] are
+    tensor t's shards, dsts[t] its destination.  The tensors share B, H and
+    the offsets; when they also share D and dtype (e.g. Q, K, V) this is
+    uaa_seq2head_permute_multi, otherwise (e.g. O and its LSE)
+    uaa_seq2head_permute_multi_ex."""
     if len(srcs) != len(dsts) or not dsts:
         raise ValueError("need one source list per destination")
-    shapes = None
+    shapes = []
     for src, dst in zip(srcs, dsts):
-        got = _permute_shapes(direction, rank, src, dst, seq_off, head_off)
-        if shapes is not None and (got != shapes or dst.dtype != dsts[0].dtype or dst.shape != dsts[0].shape):
-            raise ValueError("all tensors of one call must share shapes and dtype")
-        shapes = got
-    B, H, D, hoff = shapes
+        shapes.append(_permute_shapes(direction, rank, src, dst, seq_off, head_off))
+        if (shapes[-1][0], shapes[-1][1], shapes[-1][3]) != (shapes[0][0], shapes[0][1], shapes[0][3]):
+            raise ValueError("all tensors of one call must share B, H and the offsets")
+    B, H, D, hoff = shapes[0]
     flat = [x for src in srcs for x in src]
     ptrs = (ctypes.c_void_p * len(flat))(*[x.data_ptr() if x.numel() else 0 for x in flat])
     dptrs = (ctypes.c_void_p * len(dsts))(*[d.data_ptr() if d.numel() else 0 for d in dsts])
-    _check(lib().uaa_seq2head_permute_multi(len(dsts), direction, rank, len(srcs[0]), _i64_array(seq_off),
-                                            _i64_array(hoff), B, H, D, dsts[0].element_size(), ptrs, dptrs,
-                                            _stream(dsts[0])))
+    if all(sh[2] == D for sh in shapes) and all(d.dtype == dsts[0].dtype for d in dsts):
+        _check(lib().uaa_seq2head_permute_multi(len(dsts), direction, rank, len(srcs[0]), _i64_array(seq_off),
+                                                _i64_array(hoff), B, H, D, dsts[0].element_size(), ptrs, dptrs,
+                                                _stream(dsts[0])))
+        return
+    Ds = _i64_array([sh[2] for sh in shapes])
+    elems = (ctypes.c_int * len(dsts))(*[d.element_size() for d in dsts])
+    _check(lib().uaa_seq2head_permute_multi_ex(len(dsts), direction, rank, len(srcs[0]), _i64_array(seq_off),
+                                               _i64_array(hoff), B, H, Ds, elems, ptrs, dptrs, _stream(dsts[0])))
 
 
 def attn_workspace(q: torch.Tensor, k: torch.Tensor, mask: Optional[usp_mask] = None) -> Optional[torch.Tensor]:

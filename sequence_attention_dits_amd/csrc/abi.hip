@@ -53,9 +53,10 @@ UAA_EXPORT int uaa_abi_version(void) { return 1; }
 
 namespace {
 
-// Shared by the single- and multi-tensor permute entry points.
+// Shared by the permute entry points; Ds[t], elems[t]: features and element
+// bytes of tensor t.
 int permute_impl(int n_tensors, int dir, int rank, int world, const int64_t* seq_off,
-                 const int64_t* head_off, int64_t B, int64_t H, int64_t D, int elem_bytes,
+                 const int64_t* head_off, int64_t B, int64_t H, const int64_t* Ds, const int* elems,
                  const void* const* src, void* const* dst, void* stream)
 {
     if (dir != UAA_SEQ2HEAD && dir != UAA_HEAD2SEQ)
@@ -67,11 +68,14 @@ int permute_impl(int n_tensors, int dir, int rank, int world, const int64_t* seq
                     uaa::kPermMaxTensors, uaa::kPermMaxSrc);
     if (rank < 0 || rank >= world)
         return fail(UAA_ERR_INVALID_ARG, "permute: rank %d outside [0, %d)", rank, world);
-    if (B < 0 || H < 1 || D < 1)
-        return fail(UAA_ERR_INVALID_ARG, "permute: need B >= 0, H >= 1, D >= 1 (got %lld, %lld, %lld)",
-                    (long long)B, (long long)H, (long long)D);
-    if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
-        return fail(UAA_ERR_INVALID_ARG, "permute: elem_bytes must be 1, 2, 4 or 8, got %d", elem_bytes);
+    if (Ds == nullptr || elems == nullptr) return fail(UAA_ERR_INVALID_ARG, "permute: D or elem_bytes array is NULL");
+    for (int t = 0; t < n_tensors; ++t) {
+        if (B < 0 || H < 1 || Ds[t] < 1)
+            return fail(UAA_ERR_INVALID_ARG, "permute: need B >= 0, H >= 1, D >= 1 (got %lld, %lld, %lld)",
+                        (long long)B, (long long)H, (long long)Ds[t]);
+        if (elems[t] != 1 && elems[t] != 2 && elems[t] != 4 && elems[t] != 8)
+            return fail(UAA_ERR_INVALID_ARG, "permute: elem_bytes must be 1, 2, 4 or 8, got %d", elems[t]);
+    }
     if (seq_off == nullptr) return fail(UAA_ERR_INVALID_ARG, "permute: seq_off is NULL");
     if (seq_off[0] != 0) return fail(UAA_ERR_INVALID_ARG, "permute: seq_off[0] must be 0");
     for (int p = 0; p < world; ++p)
@@ -90,8 +94,9 @@ int permute_impl(int n_tensors, int dir, int rank, int world, const int64_t* seq
             return fail(UAA_ERR_INVALID_ARG,
                         "permute: rank %d gets no heads (head_off must strictly increase; world <= H)", p);
     const int64_t S = seq_off[world];
-    if (S >= kMaxIdx32 || H >= kMaxIdx32 || (double)B * S * H * D * elem_bytes > (double)kMaxElems)
-        return fail(UAA_ERR_INVALID_ARG, "permute: tensor too large");
+    for (int t = 0; t < n_tensors; ++t)
+        if (S >= kMaxIdx32 || H >= kMaxIdx32 || (double)B * S * H * Ds[t] * elems[t] > (double)kMaxElems)
+            return fail(UAA_ERR_INVALID_ARG, "permute: tensor too large");
     if (src == nullptr || dst == nullptr) return fail(UAA_ERR_INVALID_ARG, "permute: src or dst array is NULL");
 
     const int64_t Sp = seq_off[rank + 1] - seq_off[rank];
@@ -100,10 +105,13 @@ int permute_impl(int n_tensors, int dir, int rank, int world, const int64_t* seq
     if (B * n_tensors > 65535) return fail(UAA_ERR_UNSUPPORTED, "permute: B * n_tensors above 65535");
 
     // Sources that hold data must be present; every pointer must be aligned.
-    const int64_t slice = D * elem_bytes;       // bytes of one head of one token
-    int vec = 16;
-    while (vec > 1 && slice % vec != 0) vec >>= 1;
+    // Each tensor moves in the widest vector that divides its head slice
+    // and that all its pointers' alignment allows.
+    int vecs[uaa::kPermMaxTensors];
     for (int t = 0; t < n_tensors; ++t) {
+        const int elem_bytes = elems[t];
+        int vec = 16;
+        while (vec > 1 && (Ds[t] * elem_bytes) % vec != 0) vec >>= 1;
         for (int p = 0; p < world; ++p) {
             // SEQ2HEAD reads every non-empty token shard; HEAD2SEQ every head shard
             if (dir == UAA_SEQ2HEAD && seq_off[p + 1] == seq_off[p]) continue;
@@ -112,12 +120,13 @@ int permute_impl(int n_tensors, int dir, int rank, int world, const int64_t* seq
             if (!aligned(sp, elem_bytes))
                 return fail(UAA_ERR_INVALID_ARG, "permute: src[%d] not aligned to %d bytes", t * world + p,
                             elem_bytes);
-            while (vec > elem_bytes && !aligned(sp, vec)) vec >>= 1;
+            while (vec > 1 && !aligned(sp, vec)) vec >>= 1;
         }
         if (dst[t] == nullptr) return fail(UAA_ERR_INVALID_ARG, "permute: dst[%d] is NULL", t);
         if (!aligned(dst[t], elem_bytes))
             return fail(UAA_ERR_INVALID_ARG, "permute: dst[%d] not aligned to %d bytes", t, elem_bytes);
-        while (vec > elem_bytes && !aligned(dst[t], vec)) vec >>= 1;
+        while (vec > 1 && !aligned(dst[t], vec)) vec >>= 1;
+        vecs[t] = vec;
     }
 
     uaa::PermuteArgs a{};
@@ -127,25 +136,28 @@ int permute_impl(int n_tensors, int dir, int rank, int world, const int64_t* seq
         a.seq_off[p] = (int32_t)seq_off[p];
         a.head_off[p] = (int32_t)hoff[p];
     }
-    const int64_t hv = slice / vec;
     int64_t max_n = 0;
-    for (int y = 0; y < world; ++y) {
-        const int64_t T = dir == UAA_SEQ2HEAD ? seq_off[y + 1] - seq_off[y] : Sp;
-        const int64_t run = (dir == UAA_SEQ2HEAD ? hoff[rank + 1] - hoff[rank] : hoff[y + 1] - hoff[y]) * hv;
-        if (run >= kMaxIdx32 || T * run >= kMaxIdx32 - 4096)
-            return fail(UAA_ERR_UNSUPPORTED, "permute: one shard moves 2^31 or more elements");
-        const uaa::FastDiv f = uaa::make_fastdiv((uint32_t)run);
-        a.run_mul[y] = f.mul;
-        a.run_shift[y] = (uint8_t)f.shift;
-        if (T * run > max_n) max_n = T * run;
+    for (int t = 0; t < n_tensors; ++t) {
+        const int64_t hv = Ds[t] * elems[t] / vecs[t];
+        a.head_vecs[t] = (int32_t)hv;
+        a.vec_bytes[t] = vecs[t];
+        for (int y = 0; y < world; ++y) {
+            const int64_t T = dir == UAA_SEQ2HEAD ? seq_off[y + 1] - seq_off[y] : Sp;
+            const int64_t run = (dir == UAA_SEQ2HEAD ? hoff[rank + 1] - hoff[rank] : hoff[y + 1] - hoff[y]) * hv;
+            if (run >= kMaxIdx32 || T * run >= kMaxIdx32 - 4096)
+                return fail(UAA_ERR_UNSUPPORTED, "permute: one shard moves 2^31 or more elements");
+            const uaa::FastDiv f = uaa::make_fastdiv((uint32_t)run);
+            a.run_mul[t][y] = f.mul;
+            a.run_shift[t][y] = (uint8_t)f.shift;
+            if (T * run > max_n) max_n = T * run;
+        }
     }
     a.world = world;
     a.rank = rank;
     a.n_tensors = n_tensors;
-    a.head_vecs = (int32_t)hv;
     a.H = (int32_t)H;
     a.max_rows_x_run = (int32_t)max_n;
-    return hip_status(uaa::launch_permute(dir, vec, a, B, static_cast<hipStream_t>(stream)), "permute launch");
+    return hip_status(uaa::launch_permute(dir, a, B, static_cast<hipStream_t>(stream)), "permute launch");
 }
 
 }  // namespace
@@ -155,13 +167,30 @@ UAA_EXPORT int uaa_seq2head_permute(int dir, int rank, int world, const int64_t*
                                     int elem_bytes, const void* const* src, void* dst, void* stream)
 {
     void* dsts[1] = {dst};
-    return permute_impl(1, dir, rank, world, seq_off, head_off, B, H, D, elem_bytes, src, dsts, stream);
+    return permute_impl(1, dir, rank, world, seq_off, head_off, B, H, &D, &elem_bytes, src, dsts, stream);
 }
 
 UAA_EXPORT int uaa_seq2head_permute_multi(int n_tensors, int dir, int rank, int world, const int64_t* seq_off,
                                           const int64_t* head_off, int64_t B, int64_t H, int64_t D,
                                           int elem_bytes, const void* const* src, void* const* dst,
                                           void* stream)
+{
+    if (n_tensors < 1 || n_tensors > uaa::kPermMaxTensors)
+        return fail(UAA_ERR_INVALID_ARG, "permute: need 1 <= n_tensors <= %d and n_tensors * world <= %d",
+                    uaa::kPermMaxTensors, uaa::kPermMaxSrc);
+    int64_t Ds[uaa::kPermMaxTensors];
+    int elems[uaa::kPermMaxTensors];
+    for (int t = 0; t < n_tensors; ++t) {
+        Ds[t] = D;
+        elems[t] = elem_bytes;
+    }
+    return permute_impl(n_tensors, dir, rank, world, seq_off, head_off, B, H, Ds, elems, src, dst, stream);
+}
+
+UAA_EXPORT int uaa_seq2head_permute_multi_ex(int n_tensors, int dir, int rank, int world,
+                                             const int64_t* seq_off, const int64_t* head_off, int64_t B,
+                                             int64_t H, const int64_t* D, const int* elem_bytes,
+                                             const void* const* src, void* const* dst, void* stream)
 {
     return permute_impl(n_tensors, dir, rank, world, seq_off, head_off, B, H, D, elem_bytes, src, dst, stream);
 }

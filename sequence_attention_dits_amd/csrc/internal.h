@@ -41,15 +41,17 @@ struct PermuteArgs {
     unsigned char* dst[kPermMaxTensors];
     int32_t seq_off[UAA_MAX_WORLD + 1];
     int32_t head_off[UAA_MAX_WORLD + 1];
-    uint32_t run_mul[UAA_MAX_WORLD];         // n / run_y as mul-hi + shift (mul 0: shift only)
-    uint8_t run_shift[UAA_MAX_WORLD];
+    // n / run as mul-hi + shift (mul 0: shift only), per tensor and source y
+    uint32_t run_mul[kPermMaxTensors][UAA_MAX_WORLD];
+    uint8_t run_shift[kPermMaxTensors][UAA_MAX_WORLD];
     int32_t world, rank, n_tensors;
-    int32_t head_vecs;                       // vectors per head slice of one token
+    int32_t head_vecs[kPermMaxTensors];      // vectors per head slice of one token, per tensor
+    int32_t vec_bytes[kPermMaxTensors];      // vector width of each tensor: 16, 8, 4, 2 or 1
     int32_t H;
-    int32_t max_rows_x_run;                  // max_y T_y * run_y, sizes grid x
+    int32_t max_rows_x_run;                  // max over tensors and y of T_y * run_y, sizes grid x
 };
 
-hipError_t launch_permute(int dir, int vec_bytes, const PermuteArgs& a, int64_t B, hipStream_t s);
+hipError_t launch_permute(int dir, const PermuteArgs& a, int64_t B, hipStream_t s);
 
 // --------------------------------------------------------------------------
 // Merge.

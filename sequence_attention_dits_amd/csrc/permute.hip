@@ -16,7 +16,8 @@
 //             destination rows.
 // The launch grid is (chunks, source y, batch * tensor), so every base
 // pointer, stride and run length is uniform in a workgroup (scalar
-// registers); inside a chunk each lane moves U 16-byte vectors of the
+// registers); tensors of one launch may differ in row size (e.g. O and its
+// LSE), each moving in the widest vector its rows and pointers allow; inside a chunk each lane moves U 16-byte vectors of the
 // flattened (row, column) space, loads issued before stores; stores are
 // non-temporal since nothing reads them back soon (measured: non-temporal
 // loads are ~20 % slower here, non-temporal stores faster).  The row of a
@@ -51,13 +52,11 @@ __device__ __forceinline__ void st_nt(V* p, V x) { __builtin_nontemporal_store(x
 constexpr int kThreads = 256;
 constexpr int kVecPerThread = 2;   // vectors in flight per lane
 
+// The copy of one (source y, tensor, batch b) chunk in vectors of type V.
 template <int DIR, typename V>
-__global__ __launch_bounds__(kThreads) void permute_kernel(const PermuteArgs a)
+__device__ __forceinline__ void permute_chunk(const PermuteArgs& a, int y, int tensor, int64_t b)
 {
-    const int y = blockIdx.y;
-    const int tensor = (int)(blockIdx.z % (uint32_t)a.n_tensors);
-    const int64_t b = blockIdx.z / (uint32_t)a.n_tensors;
-    const int64_t hv = a.head_vecs;
+    const int64_t hv = a.head_vecs[tensor];
     const int64_t S = a.seq_off[a.world];
 
     // uniform description of this source's copy
@@ -86,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const PermuteArgs a)
     if (base >= n) return;
     const V* src = reinterpret_cast<const V*>(a.src[tensor * a.world + y]) + src_row0 * src_stride + src_col0;
     V* dst = reinterpret_cast<V*>(a.dst[tensor]) + dst_row0 * dst_stride + dst_col0;
-    const uint32_t mul = a.run_mul[y], shift = a.run_shift[y];
+    const uint32_t mul = a.run_mul[tensor][y], shift = a.run_shift[tensor][y];
 
     V tmp[kVecPerThread];
     uint32_t row[kVecPerThread], col[kVecPerThread];
@@ -107,8 +106,26 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const PermuteArgs a)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+// Each tensor moves in its own vector width (a uniform branch per
+// workgroup), so a launch that carries O and its 4-byte LSE still moves O in
+// 16-byte vectors.
 template <int DIR>
-static hipError_t launch_dir(int vec_bytes, const PermuteArgs& a, int64_t B, hipStream_t s)
+__global__ __launch_bounds__(kThreads) void permute_kernel(const PermuteArgs a)
+{
+    const int y = blockIdx.y;
+    const int tensor = (int)(blockIdx.z % (uint32_t)a.n_tensors);
+    const int64_t b = blockIdx.z / (uint32_t)a.n_tensors;
+    switch (a.vec_bytes[tensor]) {
+    case 16: permute_chunk<DIR, u32x4>(a, y, tensor, b); break;
+    case 8: permute_chunk<DIR, u32x2>(a, y, tensor, b); break;
+    case 4: permute_chunk<DIR, unsigned int>(a, y, tensor, b); break;
+    case 2: permute_chunk<DIR, unsigned short>(a, y, tensor, b); break;
+    default: permute_chunk<DIR, unsigned char>(a, y, tensor, b); break;
+    }
+}
+
+template <int DIR>
+static hipError_t launch_dir(const PermuteArgs& a, int64_t B, hipStream_t s)
 {
     const int64_t chunk = kThreads * kVecPerThread;
     const int64_t gx = ((int64_t)a.max_rows_x_run + chunk - 1) / chunk;
@@ -116,20 +133,12 @@ static hipError_t launch_dir(int vec_bytes, const PermuteArgs& a, int64_t B, hip
     if (gx <= 0 || gz <= 0) return hipSuccess;
     if (gx > 0x7fffffff || gz > 65535) return hipErrorInvalidValue;
     const dim3 grid((unsigned)gx, (unsigned)a.world, (unsigned)gz), block(kThreads);
-    switch (vec_bytes) {
-    case 16: return launch_kernel(permute_kernel<DIR, u32x4>, grid, block, 0, s, a);
-    case 8: return launch_kernel(permute_kernel<DIR, u32x2>, grid, block, 0, s, a);
-    case 4: return launch_kernel(permute_kernel<DIR, unsigned int>, grid, block, 0, s, a);
-    case 2: return launch_kernel(permute_kernel<DIR, unsigned short>, grid, block, 0, s, a);
-    case 1: return launch_kernel(permute_kernel<DIR, unsigned char>, grid, block, 0, s, a);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_kernel(permute_kernel<DIR>, grid, block, 0, s, a);
 }
 
-hipError_t launch_permute(int dir, int vec_bytes, const PermuteArgs& a, int64_t B, hipStream_t s)
+hipError_t launch_permute(int dir, const PermuteArgs& a, int64_t B, hipStream_t s)
 {
-    return dir == UAA_SEQ2HEAD ? launch_dir<UAA_SEQ2HEAD>(vec_bytes, a, B, s)
-                               : launch_dir<UAA_HEAD2SEQ>(vec_bytes, a, B, s);
+    return dir == UAA_SEQ2HEAD ? launch_dir<UAA_SEQ2HEAD>(a, B, s) : launch_dir<UAA_HEAD2SEQ>(a, B, s);
 }
 
 }  // namespace uaa

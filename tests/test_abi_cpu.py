@@ -193,6 +193,26 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         binding.lib()
 
 
+def test_multi_ex_permute_validation():
+    lib = uaa.lib()
+    ptrs = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    dsts = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    so = (ctypes.c_int64 * 3)(0, 2, 4)
+    Ds = (ctypes.c_int64 * 2)(128, 1)
+    for elems, text in (((2, 3), "elem_bytes"), ((2, 4), None)):
+        e = (ctypes.c_int * 2)(*elems)
+        rc = lib.uaa_seq2head_permute_multi_ex(2, 0, 0, 2, so, None, 0, 4, Ds, e, ptrs, dsts, None)
+        if text is None:
+            assert rc == 0          # B = 0: validated, no work
+        else:
+            assert rc == -1 and text in lib.uaa_last_error().decode()
+    e = (ctypes.c_int * 2)(2, 4)
+    assert lib.uaa_seq2head_permute_multi_ex(2, 0, 0, 2, so, None, 1, 4, None, e, ptrs, dsts, None) == -1
+    bad = (ctypes.c_int64 * 2)(128, 0)
+    assert lib.uaa_seq2head_permute_multi_ex(2, 0, 0, 2, so, None, 1, 4, bad, e, ptrs, dsts, None) == -1
+    assert lib.uaa_seq2head_permute_multi_ex(5, 0, 0, 2, so, None, 1, 4, Ds, e, ptrs, dsts, None) == -1
+
+
 def test_multi_permute_validation():
     lib = uaa.lib()
     src = _ptrs(*([FAKE] * 8))

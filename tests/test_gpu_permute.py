@@ -186,3 +186,39 @@ def test_multi_tensor_permute_equals_separate_calls(direction, n_t, seq_off, hea
     torch.cuda.synchronize()
     for ref, got in zip(refs, dsts):
         assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
+
+
+@pytest.mark.parametrize("direction", [uaa.UAA_SEQ2HEAD, uaa.UAA_HEAD2SEQ])
+@pytest.mark.parametrize("seq_off,head_off", [([0, 129, 257], [0, 7, 13]), ([0, 2241, 4481], [0, 12, 24])])
+def test_multi_tensor_mixed_row_sizes_equal_separate_calls(direction, seq_off, head_off):
+    """O (bf16, D=128), its LSE (fp32, D=1) and an odd fp32 D=3 tensor in one
+    launch (uaa_seq2head_permute_multi_ex) equal three separate calls."""
+    world = len(seq_off) - 1
+    H, S, B, rank = head_off[-1], seq_off[-1], 1, 1
+    gen = torch.Generator(device="cpu").manual_seed(S)
+    kinds = [(128, torch.bfloat16), (1, torch.float32), (3, torch.float32)]
+    srcs, dsts, refs = [], [], []
+    for D, dt in kinds:
+        if direction == uaa.UAA_SEQ2HEAD:
+            src = [torch.randn(B, seq_off[p + 1] - seq_off[p], H, D, generator=gen).to(dt).cuda() for p in range(world)]
+            shape = (B, S, head_off[rank + 1] - head_off[rank], D)
+        else:
+            src = [torch.randn(B, S, head_off[r + 1] - head_off[r], D, generator=gen).to(dt).cuda() for r in range(world)]
+            shape = (B, seq_off[rank + 1] - seq_off[rank], H, D)
+        ref = torch.empty(shape, dtype=dt, device="cuda")
+        uaa.uaa_seq2head_permute(direction, rank, src, ref, seq_off, head_off)
+        srcs.append(src)
+        refs.append(ref)
+        dsts.append(torch.full(shape, 3.0, dtype=dt, device="cuda"))
+    say("permute multi_ex", direction, seq_off, head_off)
+    uaa.uaa_seq2head_permute_multi(direction, rank, srcs, dsts, seq_off, head_off)
+    torch.cuda.synchronize()
+    for ref, got in zip(refs, dsts):
+        iv = torch.int16 if ref.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(ref.view(iv), got.view(iv))
+    # and the O + LSE pair alone (the step's inverse gather)
+    d2 = [torch.full_like(refs[0], 5.0), torch.full_like(refs[1], 5.0)]
+    uaa.uaa_seq2head_permute_multi(direction, rank, srcs[:2], d2, seq_off, head_off)
+    torch.cuda.synchronize()
+    assert torch.equal(refs[0].view(torch.int16), d2[0].view(torch.int16))
+    assert torch.equal(refs[1].view(torch.int32), d2[1].view(torch.int32))
