@@ -10,11 +10,13 @@ rank = head rank 0 / token rank 0):
      tensors in one multi-tensor launch                          (1 launch)
   2. attention with LSE of the 4608 queries against the keys/values, taken
      as 2 Ring chunks of 2304                                   (2 launches)
-  3. LSE merge of the 2 partial (O, LSE) pairs                  (1 launch)
+  3. LSE merge of the 2 partial (O, LSE) pairs: by default the Ring-step
+     update inside the second chunk's launch (usp_attn_fwd_lse_acc);
+     --ring-update merge runs it as its own usp_lse_merge launch
   4. inverse gather (HEAD2SEQ) of O and of the LSE into this rank's token
      shard, both in one launch; the other head rank's shard stands in for
      what the exchange would deliver                            (1 launch)
-  (5 launches per step)
+  (4 launches per step; 5 with --ring-update merge)
 
 value = attention FLOPs of the step (4*D*H*Sq*Sk = 130.46 GFLOP) / step time.
 Input sets rotate over more than 4x the 256 MB Infinity Cache so every
@@ -26,10 +28,12 @@ the stream the kernels run on.
 
 Other workloads (--workload): flux1008 (the same step on the non-divisible
 4481-token UAA share), and two Ring-only shares whose step is one attention
-launch per K/V chunk plus the N-way merge: qwen1328 (Qwen-Image 1328x1328,
-2 chunks of 3493) and longctx (32768-token causal zigzag layout, Q = chunks
-{1, 6}, 8 chunks of 4096 masked by global position, 8-way merge).  There
-`value` counts only the allowed (query, key) pairs.
+launch per K/V chunk plus the merge: qwen1328 (Qwen-Image 1328x1328, 2
+chunks of 3493, Ring-step update) and longctx (32768-token causal zigzag
+layout, Q = chunks {1, 6}, 8 chunks of 4096 masked by global position, on
+two streams, then one 8-way merge launch).  There `value` counts only the
+allowed (query, key) pairs.  The per-kernel figures include the standalone
+merge and permute launches whether or not the step uses them.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--no-cpu-baseline]
@@ -71,6 +75,12 @@ RING_WORKLOADS = ("qwen1328", "longctx")
 # compute units idle); the FLUX and Qwen chunks lose 3-6 % (two chunks' K/V
 # no longer fit the per-XCD L2 together).
 OVERLAP_WORKLOADS = ("longctx",)
+# Workloads whose chunk partials are merged by the Ring-step update inside
+# the attention launches (usp_attn_fwd_lse_acc) rather than by one N-way
+# merge launch: the two-chunk shares, where it saves the merge pass.  The
+# 8-chunk long-context share keeps the N-way merge (its launches overlap on
+# two streams, which a running accumulator would serialise).
+ACC_WORKLOADS = ("flux1024", "flux1008", "qwen1328")
 
 
 def parse():
@@ -81,6 +91,9 @@ def parse():
     p.add_argument("--workload", default="flux1024", choices=sorted(WORKLOADS))
     p.add_argument("--overlap-chunks", choices=["auto", "on", "off"], default="auto",
                    help="run the Ring chunks' attention launches on two streams (auto: per workload)")
+    p.add_argument("--ring-update", choices=["auto", "acc", "merge"], default="auto",
+                   help="merge the chunk partials inside the attention launches (acc) or with one N-way "
+                        "merge launch (auto: per workload)")
     p.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough for 1 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -96,7 +109,7 @@ def parse():
 class Share:
     """Device buffers of one workload and the launches of one step."""
 
-    def __init__(self, cfg_id: int, n_sets: int, overlap_chunks: bool = False):
+    def __init__(self, cfg_id: int, n_sets: int, overlap_chunks: bool = False, ring_acc: bool = False):
         import numpy as np
         import torch
 
@@ -105,6 +118,7 @@ class Share:
         self.uaa = uaa
         self.torch = torch
         self.overlap_chunks = overlap_chunks
+        self.ring_acc = ring_acc
         c = synth.CONFIGS[cfg_id]
         self.B, self.S, self.H, self.D = c["B"], c["S"], c["H"], c["D"]
         self.P = 2
@@ -179,6 +193,10 @@ class Share:
             for c in range(len(self.kc)):
                 self.attn_chunk(s, c, self.ws[0])
             return len(self.kc)
+        if name == "attn_acc":   # the accumulating launches of a Ring-step-update pass
+            for c in range(1, len(self.kc)):
+                self.attn_chunk(s, c, self.ws[0], acc=True)
+            return len(self.kc) - 1
         if name == "merge":
             uaa.usp_lse_merge(self.o_part, self.l_part, self.o, self.lse)
             return 1
@@ -198,32 +216,43 @@ class Share:
             return 1
         raise ValueError(name)
 
-    kernel_names = ("permute", "permute_qkv", "attn", "merge", "head2seq", "head2seq_lse", "head2seq_o_lse")
+    kernel_names = ("permute", "permute_qkv", "attn", "attn_acc", "merge", "head2seq", "head2seq_lse",
+                    "head2seq_o_lse")
 
-    def attn_chunk(self, s, c, ws):
+    def attn_chunk(self, s, c, ws, acc=False):
+        """Chunk c's attention into its partial buffers, or with acc into the
+        running (o, lse): chunk 0 writes it, later chunks merge into it."""
         kc, vc = self.kc[c]
-        self.uaa.usp_attn_fwd_lse(self.qh["q"], _contig(kc), _contig(vc), self.o_part[c], self.l_part[c],
-                                  self.scale, workspace=ws)
+        o, l = (self.o, self.lse) if acc else (self.o_part[c], self.l_part[c])
+        self.uaa.usp_attn_fwd_lse(self.qh["q"], _contig(kc), _contig(vc), o, l, self.scale, workspace=ws,
+                                  accumulate=acc and c > 0)
 
     def result(self):
         return self.o_tok, self.l_tok
 
     def step(self, s):
         """Enqueue one step on input set s: the Q/K/V gather, the attention
-        of every Ring chunk (independent launches; with overlap_chunks they
-        alternate between two streams, as the ring overlaps a chunk's arrival
-        with compute), the merge, then the inverse gather of O and its LSE
-        in one launch."""
+        of every Ring chunk with the LSE merge of the partials -- with
+        ring_acc as the Ring-step update (chunk 0 writes the running (O,
+        LSE), each later chunk's launch merges itself into it), otherwise as
+        independent launches (alternating between two streams with
+        overlap_chunks) followed by one N-way merge launch -- then the
+        inverse gather of O and its LSE in one launch."""
         torch = self.torch
         main = torch.cuda.current_stream()
         self._seq2head_qkv(s)
-        chunks = [lambda w, c=c: self.attn_chunk(s, c, w) for c in range(len(self.kc))]
-        if self.overlap_chunks:
-            _two_streams(torch, main, self.side, chunks, self.ws)
+        if self.ring_acc:
+            # each chunk merged into the running result as it is computed
+            for c in range(len(self.kc)):
+                self.attn_chunk(s, c, self.ws[0], acc=True)
         else:
-            for fn in chunks:
-                fn(self.ws[0])
-        self.launch_one("merge", s)
+            chunks = [lambda w, c=c: self.attn_chunk(s, c, w) for c in range(len(self.kc))]
+            if self.overlap_chunks:
+                _two_streams(torch, main, self.side, chunks, self.ws)
+            else:
+                for fn in chunks:
+                    fn(self.ws[0])
+            self.launch_one("merge", s)
         self.launch_one("head2seq_o_lse", s)
 
     def _seq2head_qkv(self, s):
@@ -266,7 +295,7 @@ class RingShare:
     the causal zigzag mask by global position where the layout has one), then
     the N-way LSE merge of the partials."""
 
-    def __init__(self, cfg_id: int, n_sets: int, overlap_chunks: bool = False):
+    def __init__(self, cfg_id: int, n_sets: int, overlap_chunks: bool = False, ring_acc: bool = False):
         import numpy as np
         import torch
 
@@ -275,6 +304,7 @@ class RingShare:
         self.uaa = uaa
         self.torch = torch
         self.overlap_chunks = overlap_chunks
+        self.ring_acc = ring_acc
         c = synth.CONFIGS[cfg_id]
         self.B, self.H, self.D = c["B"], c["H"], c["D"]
         self.scale = float(np.float32(1.0 / math.sqrt(self.D)))
@@ -317,7 +347,7 @@ class RingShare:
                 kpos = np.arange(a, b)
                 self.pairs.append(float(np.searchsorted(np.sort(kpos), qpos, side="right").sum()))
 
-    kernel_names = ("attn", "merge")
+    kernel_names = ("attn", "attn_acc", "merge")
 
     def attn_flops(self, chunk):
         return 4.0 * self.D * self.H * self.B * self.pairs[chunk]
@@ -334,21 +364,30 @@ class RingShare:
             for c in range(len(self.kv)):
                 self.attn_chunk(s, c, self.ws[0])
             return len(self.kv)
+        if name == "attn_acc":
+            for c in range(1, len(self.kv)):
+                self.attn_chunk(s, c, self.ws[0], acc=True)
+            return len(self.kv) - 1
         if name == "merge":
             uaa.usp_lse_merge(self.o_part, self.l_part, self.o, self.lse)
             return 1
         raise ValueError(name)
 
-    def attn_chunk(self, s, c, ws):
+    def attn_chunk(self, s, c, ws, acc=False):
         d = self.sets[s]
         a, b = self.kv[c]
-        self.uaa.usp_attn_fwd_lse(d["q"], d["k"][:, a:b], d["v"][:, a:b], self.o_part[c], self.l_part[c],
-                                  self.scale, self.masks[c], workspace=ws)
+        o, l = (self.o, self.lse) if acc else (self.o_part[c], self.l_part[c])
+        self.uaa.usp_attn_fwd_lse(d["q"], d["k"][:, a:b], d["v"][:, a:b], o, l, self.scale, self.masks[c],
+                                  workspace=ws, accumulate=acc and c > 0)
 
     def step(self, s):
-        """The attention of every chunk (on two streams with overlap_chunks,
-        see Share.step), then the N-way merge."""
+        """The attention of every chunk with the merge of the partials (see
+        Share.step)."""
         torch = self.torch
+        if self.ring_acc:
+            for c in range(len(self.kv)):
+                self.attn_chunk(s, c, self.ws[0], acc=True)
+            return
         chunks = [lambda w, c=c: self.attn_chunk(s, c, w) for c in range(len(self.kv))]
         if self.overlap_chunks:
             _two_streams(torch, torch.cuda.current_stream(), self.side, chunks, self.ws)
@@ -594,7 +633,8 @@ def main():
         per_set = 3 * c["B"] * c["S"] * c["H"] * c["D"] * 2 + c["B"] * c["S"] * (c["H"] // 2) * c["D"] * 2
     n_sets = args.sets or max(2, int(math.ceil((1 << 30) / per_set)))
     overlap = {"on": True, "off": False}.get(args.overlap_chunks, args.workload in OVERLAP_WORKLOADS)
-    share = RingShare(cfg_id, n_sets, overlap) if ring else Share(cfg_id, n_sets, overlap)
+    ring_acc = {"acc": True, "merge": False}.get(args.ring_update, args.workload in ACC_WORKLOADS)
+    share = (RingShare if ring else Share)(cfg_id, n_sets, overlap, ring_acc)
 
     for i in range(max(args.warmup, 1)):
         share.step(i % n_sets)
@@ -669,6 +709,7 @@ def main():
                       "hbm_frac": round(merge_gbps / PEAK_HBM_GBPS, 4), "bytes": share.merge_bytes()},
         "attention": {"us": round(attn_us, 2), "TFLOP/s": round(attn_tf, 2),
                       "mfma_frac": round(attn_tf / PEAK_BF16_TFLOPS, 4)},
+        "attention_acc": {"us": round(log["attn_acc"], 2)},
     }
     if ring:
         config = {"workload": desc, "B": share.B, "Sq": share.Sq, "heads": share.H, "D": share.D,

@@ -233,6 +233,28 @@ int usp_attn_fwd_lse_ws(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
                         size_t workspace_bytes, void* stream);
 
 /*
+ * usp_attn_fwd_lse_acc -- one step of a Ring pass in one call: the
+ * attention of this key/value block merged into the running result ([USP]:
+ * each Ring step's (out, lse) is folded into the accumulated one by the LSE
+ * merge; [CP] "Ring Attention").  On entry (o, lse) hold the result over the
+ * keys seen so far (lse = -inf for a row with none; its o is then not read);
+ * on return they hold the result over those keys and this block:
+ *   lse' = log(e^lse + e^lse_b),  o' = e^(lse - lse') o + e^(lse_b - lse') o_b
+ * with (o_b, lse_b) what usp_attn_fwd_lse would give for this block.  The
+ * merge runs in fp32 in the epilogue, o_b rounded to o_dtype first when that
+ * is bf16 (as if merged by usp_lse_merge), and saves the separate merge pass
+ * when the blocks arrive one at a time.  o and lse are read and written in
+ * place; every other argument (workspace included) is that of
+ * usp_attn_fwd_lse_ws.  The first block of a pass uses usp_attn_fwd_lse(_ws)
+ * (or starts from lse = -inf).
+ * Returns UAA_OK, UAA_ERR_INVALID_ARG, UAA_ERR_UNSUPPORTED or UAA_ERR_HIP.
+ */
+int usp_attn_fwd_lse_acc(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                         const void* q, const void* k, const void* v, void* o, int o_dtype,
+                         float* lse, float scale, const usp_mask* mask, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
  * usp_attn_workspace_bytes -- device workspace usp_attn_fwd_lse_ws uses for
  * this problem on the current device: 0 when it would run as the plain call
  * (fp32, a causal-family mask, or no split that saves at least 8 % by a

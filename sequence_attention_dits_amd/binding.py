@@ -111,6 +111,8 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_float, ctypes.POINTER(usp_mask), _c_p]
         l.usp_attn_fwd_lse_ws.restype = ctypes.c_int
         l.usp_attn_fwd_lse_ws.argtypes = l.usp_attn_fwd_lse.argtypes[:-1] + [_c_p, ctypes.c_size_t, _c_p]
+        l.usp_attn_fwd_lse_acc.restype = ctypes.c_int
+        l.usp_attn_fwd_lse_acc.argtypes = l.usp_attn_fwd_lse_ws.argtypes
         l.usp_attn_workspace_bytes.restype = ctypes.c_size_t
         l.usp_attn_workspace_bytes.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                                ctypes.POINTER(usp_mask)]
@@ -258,10 +260,12 @@ def attn_workspace(q: torch.Tensor, k: torch.Tensor, mask: Optional[usp_mask] = 
 
 def usp_attn_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                      lse: torch.Tensor, scale: float, mask: Optional[usp_mask] = None,
-                     workspace: Optional[torch.Tensor] = None) -> None:
+                     workspace: Optional[torch.Tensor] = None, accumulate: bool = False) -> None:
     """Attention forward with LSE into caller-owned o [B,Sq,H,D], lse [B,Sq,H] fp32.
     With a workspace from attn_workspace() the call is usp_attn_fwd_lse_ws,
-    which may split each unit's keys over several workgroups."""
+    which may split each unit's keys over several workgroups.  With
+    accumulate=True it is usp_attn_fwd_lse_acc: (o, lse) hold the running
+    result of a Ring pass and this block is merged into them in place."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse")):
         _dev(t, n)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
@@ -276,17 +280,20 @@ def usp_attn_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch
         raise ValueError("o must be shaped like q and lse [B, Sq, H] float32")
     dt, odt = _code(q.dtype, "q"), _code(o.dtype, "o")
     m = mask if mask is not None else mask_full()
-    if workspace is None:
+    if workspace is None and not accumulate:
         _check(lib().usp_attn_fwd_lse(dt, B, H, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                       o.data_ptr(), odt, lse.data_ptr(), float(scale), ctypes.byref(m),
                                       _stream(q)))
         return
-    _dev(workspace, "workspace")
-    if workspace.dtype != torch.uint8 or workspace.dim() != 1:
-        raise ValueError("workspace must be a 1-D uint8 tensor (see attn_workspace)")
-    _check(lib().usp_attn_fwd_lse_ws(dt, B, H, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                     o.data_ptr(), odt, lse.data_ptr(), float(scale), ctypes.byref(m),
-                                     workspace.data_ptr(), workspace.numel(), _stream(q)))
+    ws_ptr, ws_n = 0, 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+            raise ValueError("workspace must be a 1-D uint8 tensor (see attn_workspace)")
+        ws_ptr, ws_n = workspace.data_ptr(), workspace.numel()
+    fn = lib().usp_attn_fwd_lse_acc if accumulate else lib().usp_attn_fwd_lse_ws
+    _check(fn(dt, B, H, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), odt, lse.data_ptr(),
+              float(scale), ctypes.byref(m), ws_ptr, ws_n, _stream(q)))
 
 
 def usp_lse_merge(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor],

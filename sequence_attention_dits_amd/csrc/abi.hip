@@ -283,7 +283,7 @@ UAA_EXPORT size_t usp_attn_workspace_bytes(int dtype, int64_t B, int64_t H, int6
 
 static int attn_impl(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, const void* q,
                      const void* k, const void* v, void* o, int o_dtype, float* lse, float scale,
-                     const usp_mask* mask, void* workspace, size_t workspace_bytes, void* stream)
+                     const usp_mask* mask, void* workspace, size_t workspace_bytes, int acc, void* stream)
 {
     if (dtype != UAA_BF16 && dtype != UAA_FP32)
         return fail(UAA_ERR_INVALID_ARG, "attn: dtype must be UAA_BF16 or UAA_FP32, got %d", dtype);
@@ -322,6 +322,7 @@ static int attn_impl(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, in
     a.scale = scale;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
     a.masked = 0;
+    a.acc = acc;
     if (mask != nullptr && mask->kind != USP_MASK_FULL) {
         a.masked = 1;
         int rc = side_map(*mask, true, Sq, a.qmap);
@@ -353,7 +354,7 @@ UAA_EXPORT int usp_attn_fwd_lse(int dtype, int64_t B, int64_t H, int64_t Sq, int
                                 const void* q, const void* k, const void* v, void* o, int o_dtype,
                                 float* lse, float scale, const usp_mask* mask, void* stream)
 {
-    return attn_impl(dtype, B, H, Sq, Sk, D, q, k, v, o, o_dtype, lse, scale, mask, nullptr, 0, stream);
+    return attn_impl(dtype, B, H, Sq, Sk, D, q, k, v, o, o_dtype, lse, scale, mask, nullptr, 0, 0, stream);
 }
 
 UAA_EXPORT int usp_attn_fwd_lse_ws(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
@@ -362,7 +363,16 @@ UAA_EXPORT int usp_attn_fwd_lse_ws(int dtype, int64_t B, int64_t H, int64_t Sq, 
                                    size_t workspace_bytes, void* stream)
 {
     return attn_impl(dtype, B, H, Sq, Sk, D, q, k, v, o, o_dtype, lse, scale, mask, workspace, workspace_bytes,
-                     stream);
+                     0, stream);
+}
+
+UAA_EXPORT int usp_attn_fwd_lse_acc(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                    const void* q, const void* k, const void* v, void* o, int o_dtype,
+                                    float* lse, float scale, const usp_mask* mask, void* workspace,
+                                    size_t workspace_bytes, void* stream)
+{
+    return attn_impl(dtype, B, H, Sq, Sk, D, q, k, v, o, o_dtype, lse, scale, mask, workspace, workspace_bytes,
+                     1, stream);
 }
 
 UAA_EXPORT int usp_lse_merge(int n_parts, int64_t B, int64_t S, int64_t H, int64_t D,

@@ -52,6 +52,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -61,9 +62,14 @@ constexpr int kBM = 256;  // query rows per workgroup
 constexpr int kBN = 64;   // keys per tile
 constexpr int kWaves = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kRescaleThreshold = 8.0f;  // in log2 units of the softmax weights
 
 // two floats -> packed bf16, round to nearest even (one v_cvt_pk_bf16_f32)
+// the two bf16 halves of a dword as floats
+__device__ __forceinline__ float bf16_lo(unsigned int x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned int x) { return __uint_as_float(x & 0xffff0000u); }
+
 __device__ __forceinline__ unsigned int pack_bf16(float lo, float hi)
 {
     return __builtin_bit_cast(unsigned int, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
@@ -520,6 +526,11 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
 
     // ---- epilogue: normalise, write O and the natural-log LSE -----------
     // (acc, mref, ls): O accumulators, reference maximum, half-row sum
+    // With a.acc the call continues a Ring pass: (o, lse) hold on entry the
+    // result over the keys seen so far (lse = -inf: none), and this block's
+    // result is merged in -- weights e^(lse_n - lse) as in the LSE merge --
+    // so that they hold on return the result over all keys seen.
+    // (acc, mref, ls): O accumulators, reference maximum, half-row sum
     auto write_out = [&](const f32x16 (&acc)[NDB], float mref, float ls) {
         float lt;
         {
@@ -527,16 +538,36 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
             lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         }
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        // log2-domain LSE of this block, and with a.acc the weights of the
+        // previous result (wp) and of this block (wb) and the merged LSE
+        const float lb2 = lt > 0.f ? mref + __log2f(lt) : -INFINITY;
+        float wp = 0.f, wb = 1.f, lse_out2 = lb2;
+        if (a.acc) {
+            const float lp2 = i < Sq ? a.lse[(b * Sq + i) * H + hh] * kLog2e : -INFINITY;
+            const float mm = __builtin_elementwise_maximum(lp2, lb2);
+            if (mm == -INFINITY) {
+                wp = 0.f;
+                wb = 0.f;
+                lse_out2 = -INFINITY;
+            } else {
+                const float ep = __builtin_amdgcn_exp2f(lp2 - mm), eb = __builtin_amdgcn_exp2f(lb2 - mm);
+                const float sum = ep + eb;
+                wp = ep / sum;
+                wb = eb / sum;
+                lse_out2 = mm + __log2f(sum);
+            }
+        }
         if constexpr (OUT_BF16) {
             // The wave's 32 x D output tile goes through LDS (free once every
             // wave has left the main loop and the last copies have landed) so
             // that each global store writes whole rows: 4 rows of 256 bytes
             // per instruction for D = 128, instead of 16-byte pieces of 32 rows.
             constexpr int RS = D * 2 + 16;        // LDS row stride (bytes)
+            constexpr int WS = 32 * RS + 32 * 8;  // per wave: the tile, then (wp, wb) of each row
             constexpr int UR = D * 2 / 16;        // 16-byte units per row
             constexpr int RPI = 64 / UR;          // rows per store instruction
             lds_barrier();
-            lds_u8* R = (lds_u8*)smem + wave * 32 * RS;
+            lds_u8* R = (lds_u8*)smem + wave * WS;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -546,31 +577,70 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
                                   pack_bf16(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
                     *(__attribute__((address_space(3))) u32x2*)(R + l32 * RS + d0 * 2) = w;
                 }
+            if (a.acc && hg == 0) *(__attribute__((address_space(3))) f32x2*)(R + 32 * RS + l32 * 8) = f32x2{wp, wb};
             const int rr = lane / UR, cu = lane % UR;
+            constexpr int NK = 32 / RPI;
+            auto dst_of = [&](int k) {
+                const int64_t row = q0 + 32 * wave + RPI * k + rr;
+                return reinterpret_cast<u32x4*>(static_cast<unsigned char*>(a.o) + ((b * Sq + row) * H + hh) * D * 2 +
+                                                cu * 16);
+            };
+            auto row_ok = [&](int k) { return q0 + 32 * wave + RPI * k + rr < Sq; };
+            // the previous result's rows, all loaded before any store (stores
+            // to o could alias later loads, which would serialise each pair)
+            u32x4 pv[NK];
+            if (a.acc) {
 #pragma unroll
-            for (int k = 0; k < 32 / RPI; ++k) {
+                for (int k = 0; k < NK; ++k) pv[k] = row_ok(k) ? *dst_of(k) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int k = 0; k < NK; ++k) {
                 const int r = RPI * k + rr;
-                const u32x4 w = *(const lds_u32x4*)(R + r * RS + cu * 16);
-                const int64_t row = q0 + 32 * wave + r;
-                if (row < Sq)
-                    *reinterpret_cast<u32x4*>(static_cast<unsigned char*>(a.o) + ((b * Sq + row) * H + hh) * D * 2 +
-                                              cu * 16) = w;
+                u32x4 w = *(const lds_u32x4*)(R + r * RS + cu * 16);
+                if (a.acc) {
+                    const f32x2 wr = *(const __attribute__((address_space(3))) f32x2*)(R + 32 * RS + r * 8);
+                    // a previous result of weight 0 (lse = -inf) is not used
+                    const bool use = wr[0] != 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float lo = fmaf(wr[0], use ? bf16_lo(pv[k][e]) : 0.f, wr[1] * bf16_lo(w[e]));
+                        const float hi = fmaf(wr[0], use ? bf16_hi(pv[k][e]) : 0.f, wr[1] * bf16_hi(w[e]));
+                        w[e] = pack_bf16(lo, hi);
+                    }
+                }
+                if (row_ok(k)) *dst_of(k) = w;
             }
         } else {
             if (i < Sq) {
                 const int64_t orow = ((b * Sq + i) * H + hh) * D;
+                const float sb = wb * inv;
+                auto dst_of = [&](int db, int g) {
+                    return reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + orow + 32 * db + 8 * g + 4 * hg);
+                };
+                // previous result loaded before any store (see above); weight 0: not read
+                f32x4 pv[NDB][4];
+                const bool use = a.acc && wp != 0.f;
+                if (use) {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) pv[db][g] = *dst_of(db, g);
+                }
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        const int d0 = 32 * db + 8 * g + 4 * hg;   // 4 consecutive features
-                        u32x4 w{__float_as_uint(acc[db][4 * g] * inv), __float_as_uint(acc[db][4 * g + 1] * inv),
-                                __float_as_uint(acc[db][4 * g + 2] * inv), __float_as_uint(acc[db][4 * g + 3] * inv)};
-                        *reinterpret_cast<u32x4*>(static_cast<float*>(a.o) + orow + d0) = w;
+                        f32x4 x{acc[db][4 * g] * sb, acc[db][4 * g + 1] * sb, acc[db][4 * g + 2] * sb,
+                                acc[db][4 * g + 3] * sb};
+                        if (use) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) x[e] = fmaf(wp, pv[db][g][e], x[e]);
+                        }
+                        *dst_of(db, g) = x;
                     }
             }
         }
-        if (hg == 0 && i < Sq) a.lse[(b * Sq + i) * H + hh] = lt > 0.f ? (mref + __log2f(lt)) * kLn2 : -INFINITY;
+        if (hg == 0 && i < Sq) a.lse[(b * Sq + i) * H + hh] = lse_out2 * kLn2;
     };
 
     if (SPLIT && np > 1) {

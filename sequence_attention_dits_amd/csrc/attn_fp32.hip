@@ -123,9 +123,37 @@ __global__ __launch_bounds__(256) void attn_fp32_kernel(const AttnArgs a)
     if (!row_ok) return;
     f32x4* O = reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + ((b * Sq + i) * H + hh) * D);
     const float inv = l > 0.f ? 1.f / l : 0.f;
+    float lse = l > 0.f ? m + logf(l) : -INFINITY;
+    if (a.acc) {
+        // continue a Ring pass: merge this block into the result already in
+        // (o, lse), weights e^(lse_n - lse); a previous weight of 0 is not read
+        const float lp = a.lse[(b * Sq + i) * H + hh];
+        const float mm = fmaxf(lp, lse);
+        float wp = 0.f, wb = 0.f;
+        if (mm != -INFINITY) {
+            const float ep = expf(lp - mm), eb = expf(lse - mm);
+            wp = ep / (ep + eb);
+            wb = eb / (ep + eb);
+            lse = mm + logf(ep + eb);
+        }
+        const float sb = wb * inv;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) O[4 * e + part] = o[e] * inv;
-    if (part == 0) a.lse[(b * Sq + i) * H + hh] = l > 0.f ? m + logf(l) : -INFINITY;
+        for (int e = 0; e < NE; ++e) {
+            f32x4 x = o[e] * sb;
+            if (wp != 0.f) {
+                const f32x4 pv = O[4 * e + part];
+                x[0] = fmaf(wp, pv[0], x[0]);
+                x[1] = fmaf(wp, pv[1], x[1]);
+                x[2] = fmaf(wp, pv[2], x[2]);
+                x[3] = fmaf(wp, pv[3], x[3]);
+            }
+            O[4 * e + part] = x;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) O[4 * e + part] = o[e] * inv;
+    }
+    if (part == 0) a.lse[(b * Sq + i) * H + hh] = lse;
 }
 
 hipError_t launch_attn_fp32(int D, const AttnArgs& a0, hipStream_t s)

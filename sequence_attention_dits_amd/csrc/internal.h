@@ -88,6 +88,7 @@ struct AttnArgs {
     float scale;          // softmax scale as given
     float scale_log2;     // scale * log2(e)
     int32_t masked;       // 0: every key allowed; 1: kpos(j) <= qpos(i)
+    int32_t acc;          // 1: merge into the (o, lse) already there (a Ring pass continues)
     PosMap qmap, kmap;
     int32_t n_qtiles;     // ceil(Sq / rows per workgroup), set by the launcher
     // Key split (bf16, unmasked): units [0, n_whole) run whole, one

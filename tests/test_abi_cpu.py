@@ -135,6 +135,17 @@ def _attn_ws(ws, nbytes, dtype=0, D=128, mask=None):
     return rc, lib.uaa_last_error().decode()
 
 
+def test_accumulate_call_validates_like_the_plain_call():
+    lib = uaa.lib()
+    m = uaa.mask_full()
+    for kw, code in ((dict(dtype=5), -1), (dict(D=96), -2)):
+        args = dict(dtype=0, D=128)
+        args.update(kw)
+        rc = lib.usp_attn_fwd_lse_acc(args["dtype"], 1, 1, 4, 4, args["D"], FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0.1,
+                                      ctypes.byref(m), None, 0, None)
+        assert rc == code and lib.uaa_last_error().decode() == _attn(**kw)[1]
+
+
 def test_workspace_call_validates_like_the_plain_call():
     assert _attn_ws(FAKE, 1 << 20, dtype=5) == (-1, _attn(dtype=5)[1])
     assert _attn_ws(FAKE, 1 << 20, D=96)[0] == -2
