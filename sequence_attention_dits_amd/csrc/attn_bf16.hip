@@ -114,8 +114,11 @@ __device__ __forceinline__ void fill_k(const unsigned char* ksrc, uint32_t nrec,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kd + n * 1024, 16, off, 0, 0, 0);
 }
 
+// Occupancy target: 2 waves per SIMD (one workgroup per CU) for D = 128;
+// for D = 64 4 waves per SIMD, i.e. at most 128 VGPRs, so that two
+// workgroups share a CU (72 KB of LDS each) -- one VGPR more halves it.
 template <int D, bool MASKED, bool OUT_BF16, bool SPLIT>
-__global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a)
+__global__ __launch_bounds__(64 * kWaves, D == 64 ? 4 : 2) void attn_bf16_kernel(const AttnArgs a)
 {
     constexpr int UPR = D / 8;               // 16-byte units per row
     constexpr int ROWB = D * 2;              // bytes per row
@@ -129,7 +132,10 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
     // free of bank conflicts.  D = 64 uses an unpadded XOR-swizzled layout.
     constexpr int VGS = D == 128 ? (D + D / 16) * 16 : D * 16;   // bytes per unit group
     constexpr int VTB = 8 * VGS;                                  // bytes of one V stage
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[3 * TB + 2 * VTB];   // K stages 0..2, V stages 0..1
+    constexpr int QB = kWaves * 32 * ROWB;   // Q staging: 32 rows per wave
+    // K stages 0..2, V stages 0..1, then the Q staging region (one workgroup
+    // runs per CU, so the 146 KB for D = 128 cost no occupancy)
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[3 * TB + 2 * VTB + QB];
 
     int64_t qt, hh, b;
     uint32_t unit = 0;   // with SPLIT: this workgroup runs key piece `piece` of `np` of this unit
@@ -164,15 +170,24 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
     const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + ((b * Sk) * H + hh) * D * 2;
     const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + ((b * Sk) * H + hh) * D * 2;
 
-    // Q operands: lane holds row i, features 16*kc + 8*hg .. +7 (zero past Sq).
-    bf16x8 qop[NKC];
+    // Q: each wave copies its own 32 rows into its own LDS region with
+    // whole-row loads (1 KB, RPD rows, per instruction; 16-byte units
+    // swizzled as in the K tile; rows past Sq read as zero) and reads its
+    // operands back once the prologue's copies have landed -- instead of
+    // gathering 16-byte pieces of 32 rows per load instruction.
+    lds_u8* const qst = (lds_u8*)(smem + 3 * TB + 2 * VTB) + wave * 32 * ROWB;
     {
-        const uint32_t q_bytes = Sq > 0 ? (uint32_t)((Sq - 1) * ld2 + D * 2) : 0u;
-        const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc((void*)qbase, (short)0, q_bytes, 0x00020000);
-        const uint32_t off = (uint32_t)(i < Sq ? i : Sq) * ld2 + hg * 16;
+        constexpr int UPRQ = D / 8, RPD = 1024 / ROWB;
+        const int64_t r0 = q0 + 32 * wave;
+        const uint32_t nrec = Sq > r0 ? (uint32_t)((Sq - 1 - r0) * ld2 + D * 2) : 0u;
+        const __amdgpu_buffer_rsrc_t qr =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(qbase + (Sq > r0 ? r0 : 0) * ld2), (short)0, nrec, 0x00020000);
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
-            qop[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, off + kc * 32, 0, 0));
+        for (int n = 0; n < 32 * ROWB / 1024; ++n) {
+            const int row = n * RPD + lane / UPRQ;
+            const uint32_t off = (uint32_t)row * ld2 + (uint32_t)(((lane % UPRQ) ^ (row & (UPRQ - 1))) * 16);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, qst + n * 1024, 16, off, 0, 0, 0);
+        }
     }
 
     // Masking: position ranges of the workgroup's rows and of this wave's,
@@ -341,6 +356,13 @@ __global__ __launch_bounds__(64 * kWaves) void attn_bf16_kernel(const AttnArgs a
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): every copy issued so far landed
     __syncthreads();
+
+    // Q operands: lane holds row i, features 16*kc + 8*hg .. +7 (zero past Sq)
+    bf16x8 qop[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+        qop[kc] = __builtin_bit_cast(
+            bf16x8, *(const lds_u32x4*)(qst + l32 * ROWB + (((2 * kc + hg) ^ (l32 & (UPR - 1))) * 16)));
 
     // One tile step with the V stage / register set parity P a template
     // constant.  Returns false after the last live tile.
