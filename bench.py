@@ -753,8 +753,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic() if args.workload == "flux1024" else None,
-                     "kernel": "attn_bf16_kernel<128,%s>" % ("masked" if ring and share.masks[0] is not None
-                                                            else "true"),
+                     # template arguments: D, masked, bf16 output, key split
+                     "kernel": "attn_bf16_kernel<128,%s,true,%s>" % (
+                         "true" if ring and share.masks[0] is not None else "false",
+                         "true" if share.ws[0] is not None else "false"),
                      "launch_us": round(attn_us, 2), "flops_per_launch": attn_flops_launch},
         "kernels": kernels,
     }
