@@ -17,11 +17,14 @@
 // The launch grid is (chunks, source y, batch * tensor), so every base
 // pointer, stride and run length is uniform in a workgroup (scalar
 // registers); tensors of one launch may differ in row size (e.g. O and its
-// LSE), each moving in the widest vector its rows and pointers allow; inside a chunk each lane moves U 16-byte vectors of the
-// flattened (row, column) space, loads issued before stores; stores are
-// non-temporal since nothing reads them back soon (measured: non-temporal
-// loads are ~20 % slower here, non-temporal stores faster).  The row of a
-// vector comes from one multiply-high by a host-computed reciprocal.
+// LSE), each moving in the widest vector its rows and pointers allow.
+// Inside a chunk each lane moves U vectors of the flattened (row, column)
+// space, loads issued before stores.  Loads and stores are plain: the
+// gathered Q, K, V are read by the attention right after, and leaving them
+// in the caches is worth more to the whole step (-1.4 %) than the
+// non-temporal stores that make the gather alone faster; non-temporal loads
+// were ~20 % slower.  The row of a vector comes from one multiply-high by a
+// host-computed reciprocal.
 #include "internal.h"
 
 namespace uaa {
@@ -45,9 +48,6 @@ FastDiv make_fastdiv(uint32_t d)
     f.shift = l - 1;                           // applied after the high 32 bits
     return f;
 }
-
-template <typename V>
-__device__ __forceinline__ void st_nt(V* p, V x) { __builtin_nontemporal_store(x, p); }
 
 constexpr int kThreads = 256;
 constexpr int kVecPerThread = 2;   // vectors in flight per lane
@@ -99,7 +99,7 @@ __device__ __forceinline__ void permute_chunk(const PermuteArgs& a, int y, int t
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
         const uint32_t f = base + threadIdx.x + u * kThreads;
-        if (f < n) st_nt(dst + (int64_t)row[u] * dst_stride + col[u], tmp[u]);
+        if (f < n) dst[(int64_t)row[u] * dst_stride + col[u]] = tmp[u];
     }
 }
 
