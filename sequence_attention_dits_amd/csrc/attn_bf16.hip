@@ -630,9 +630,10 @@ __global__ __launch_bounds__(64 * kWaves, D == 64 ? 4 : 2) void attn_bf16_kernel
                         w[e] = pack_bf16(lo, hi);
                     }
                 }
-                // non-temporal: whole rows, not read again by this kernel
-                // (measured: -1.3 us per FLUX chunk launch, -0.7 % per step)
-                if (row_ok(k)) __builtin_nontemporal_store(w, dst_of(k));
+                // Plain stores: non-temporal ones make this kernel ~1 us faster but
+                // the next kernel (the inverse gather) then misses the caches;
+                // on the whole step plain stores measured ~0.5 % faster.
+                if (row_ok(k)) *dst_of(k) = w;
             }
         } else {
             if (i < Sq) {
