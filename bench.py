@@ -255,6 +255,17 @@ class Share:
             self.launch_one("merge", s)
         self.launch_one("head2seq_o_lse", s)
 
+    def step_fused(self, s):
+        """The same step with the Q/K/V gather done inside the attention's
+        loads (usp_attn_fwd_lse_gather: queries from both token shards, the
+        keys of chunk c = token shard c), the chunks merged by the Ring-step
+        update, then the inverse gather: 3 launches."""
+        d = self.sets[s]
+        for c in range(len(self.ring)):
+            self.uaa.usp_attn_fwd_lse_gather(0, d["q"], d["k"], d["v"], c, self.o, self.lse, self.scale,
+                                             self.seq_off, self.head_off, workspace=self.ws[0], accumulate=c > 0)
+        self.launch_one("head2seq_o_lse", s)
+
     def _seq2head_qkv(self, s):
         uaa = self.uaa
         d = self.sets[s]
@@ -677,6 +688,42 @@ def main():
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
 
+    # the fused-gather variant of the FLUX-type step (SEQ2HEAD inside the
+    # attention's loads), checked bit for bit against the step above
+    variants = {}
+    if not ring:
+        share.step(0)
+        torch.cuda.synchronize()
+        ref_o, ref_l = (t.clone() for t in share.result())
+        share.step_fused(0)
+        torch.cuda.synchronize()
+        out_o, out_l = share.result()
+        same = bool(torch.equal(ref_o.view(torch.int16), out_o.view(torch.int16)) and torch.equal(ref_l, out_l))
+        fgraphs = []
+        for s_ in range(n_sets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                share.step_fused(s_)
+            fgraphs.append(g)
+        for i in range(args.warmup):
+            fgraphs[i % n_sets].replay()
+        torch.cuda.synchronize()
+        f0 = torch.cuda.Event(enable_timing=True)
+        f1 = torch.cuda.Event(enable_timing=True)
+        f0.record()
+        for i in range(args.steps):
+            fgraphs[i % n_sets].replay()
+        f1.record()
+        torch.cuda.synchronize()
+        ms_fused = f0.elapsed_time(f1) / args.steps
+        variants["fused_gather"] = {
+            "ms_per_step": round(ms_fused, 4),
+            "value": round(sum(share.attn_flops(c_) for c_ in range(len(share.ring))) / (ms_fused * 1e-3) / 1e12, 2),
+            "launches_per_step": 3,
+            "equals_default_step_bitwise": same,
+        }
+        del fgraphs
+
     # timed region 2: per-kernel durations.  Each launch of the step is
     # repeated back to back over the rotating input sets between two HIP
     # events on the launch stream; a spin kernel first gives the host a head
@@ -760,6 +807,8 @@ def main():
                      "launch_us": round(attn_us, 2), "flops_per_launch": attn_flops_launch},
         "kernels": kernels,
     }
+    if variants:
+        out["variants"] = variants
     if not ring:
         out["permute_GBps"] = kernels["seq2head_permute"]["GB/s"]
     if not args.no_cpu_baseline:

@@ -59,10 +59,12 @@ extern "C" {
 #define UAA_HEAD2SEQ 1
 
 /* Largest Ulysses degree a permute accepts, largest N a merge accepts,
- * largest tensor count of one multi-tensor permute. */
+ * largest tensor count of one multi-tensor permute, largest Ulysses degree
+ * of the gathering attention (usp_attn_fwd_lse_gather). */
 #define UAA_MAX_WORLD 64
 #define USP_MAX_PARTS 16
 #define UAA_MAX_PERMUTE_TENSORS 4
+#define UAA_MAX_GATHER_WORLD 8
 
 /* Mask kinds ([YC] ring layouts; "basic" contiguous shards are CAUSAL). */
 #define USP_MASK_FULL 0
@@ -253,6 +255,39 @@ int usp_attn_fwd_lse_acc(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk
                          const void* q, const void* k, const void* v, void* o, int o_dtype,
                          float* lse, float scale, const usp_mask* mask, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * usp_attn_fwd_lse_gather -- usp_attn_fwd_lse(_acc) on this rank's Ulysses
+ * view of token-sharded Q, K and V, read straight from the shards instead
+ * of from a gathered copy: the SEQ2HEAD gather of uaa_seq2head_permute
+ * ([CP] "Ulysses Attention", "Ulysses Anything Attention": any token and head
+ * counts, no padding) done inside the attention's loads.  For rank `rank` it
+ * computes exactly
+ *   Yq = SEQ2HEAD(q_shards), Yk = SEQ2HEAD(k_shards), Yv = SEQ2HEAD(v_shards)
+ *   usp_attn_fwd_lse(_acc)(Yq, Yk[:, keys of shard k_shard], Yv[...], ...)
+ * i.e. the queries are all S = seq_off[world] tokens, the keys the tokens of
+ * shard k_shard (a Ring chunk is one rank's token shard in the Unified
+ * composition, [USP]; attention over every token is one call per shard,
+ * the first plain and the rest with accumulate = 1).
+ *
+ *   world <= UAA_MAX_GATHER_WORLD, rank, seq_off, head_off (NULL = even):
+ *        as for uaa_seq2head_permute; H = total heads
+ *   q_shards, k_shards, v_shards: host arrays of `world` device pointers,
+ *        shard p is [B, S_p, H, D] bf16 (16-byte aligned; NULL allowed for
+ *        an empty shard, and for the k/v shards other than k_shard)
+ *   o   device [B, S, H_r, D] o_dtype, lse device [B, S, H_r] fp32, with H_r
+ *        this rank's heads; mask positions are indices into these S queries
+ *        and the keys of shard k_shard; scale, mask, workspace as for
+ *        usp_attn_fwd_lse_ws; accumulate != 0: as usp_attn_fwd_lse_acc.
+ * Results are identical, bit for bit, to the gathered-copy calls above.
+ * Returns UAA_OK, UAA_ERR_INVALID_ARG, UAA_ERR_UNSUPPORTED (fp32 input, D
+ * not 64 or 128) or UAA_ERR_HIP.
+ */
+int usp_attn_fwd_lse_gather(int dtype, int world, int rank, const int64_t* seq_off, const int64_t* head_off,
+                            int64_t B, int64_t H, int64_t D, const void* const* q_shards,
+                            const void* const* k_shards, const void* const* v_shards, int k_shard, void* o,
+                            int o_dtype, float* lse, float scale, const usp_mask* mask, void* workspace,
+                            size_t workspace_bytes, int accumulate, void* stream);
 
 /*
  * usp_attn_workspace_bytes -- device workspace usp_attn_fwd_lse_ws uses for

@@ -29,6 +29,7 @@ from .binding import (  # noqa: F401
     mask_zigzag,
     attn_workspace,
     usp_attn_fwd_lse,
+    usp_attn_fwd_lse_gather,
     usp_lse_merge,
     usp_mask,
     uaa_seq2head_permute,

@@ -113,6 +113,11 @@ def lib() -> ctypes.CDLL:
         l.usp_attn_fwd_lse_ws.argtypes = l.usp_attn_fwd_lse.argtypes[:-1] + [_c_p, ctypes.c_size_t, _c_p]
         l.usp_attn_fwd_lse_acc.restype = ctypes.c_int
         l.usp_attn_fwd_lse_acc.argtypes = l.usp_attn_fwd_lse_ws.argtypes
+        l.usp_attn_fwd_lse_gather.restype = ctypes.c_int
+        l.usp_attn_fwd_lse_gather.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_p, _c_p, _c_i64, _c_i64,
+                                              _c_i64, _c_p, _c_p, _c_p, ctypes.c_int, _c_p, ctypes.c_int, _c_p,
+                                              ctypes.c_float, ctypes.POINTER(usp_mask), _c_p, ctypes.c_size_t,
+                                              ctypes.c_int, _c_p]
         l.usp_attn_workspace_bytes.restype = ctypes.c_size_t
         l.usp_attn_workspace_bytes.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                                ctypes.POINTER(usp_mask)]
@@ -321,3 +326,49 @@ def usp_lse_merge(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Ten
     lptr = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lse_parts])
     _check(lib().usp_lse_merge(n, B, S, H, D, optr, pdt, lptr, o_out.data_ptr(),
                                _code(o_out.dtype, "o_out"), lse_out.data_ptr(), _stream(o_out)))
+
+
+def usp_attn_fwd_lse_gather(rank: int, q_shards: Sequence[torch.Tensor], k_shards: Sequence[torch.Tensor],
+                            v_shards: Sequence[torch.Tensor], k_shard: int, o: torch.Tensor, lse: torch.Tensor,
+                            scale: float, seq_off: Sequence[int], head_off: Optional[Sequence[int]] = None,
+                            mask: Optional[usp_mask] = None, workspace: Optional[torch.Tensor] = None,
+                            accumulate: bool = False) -> None:
+    """Attention of rank `rank`'s Ulysses view read straight from token shards
+    [B, S_p, H, D] (bf16): queries = all tokens, keys = shard k_shard; into
+    o [B, S, H_r, D] and lse [B, S, H_r] (usp_attn_fwd_lse_gather)."""
+    world = len(q_shards)
+    if len(k_shards) != world or len(v_shards) != world or len(seq_off) != world + 1:
+        raise ValueError("need world shards of q, k and v and world+1 seq_off entries")
+    for t in list(q_shards) + list(k_shards) + list(v_shards):
+        _dev(t, "shard")
+        if t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise ValueError("shards are bf16 [B, S_p, H, D]")
+    B, _, H, D = q_shards[0].shape
+    S = int(seq_off[-1])
+    for p in range(world):
+        Sp = int(seq_off[p + 1]) - int(seq_off[p])
+        for t in (q_shards[p], k_shards[p], v_shards[p]):
+            if tuple(t.shape) != (B, Sp, H, D):
+                raise ValueError("shard %d shape %s does not match the offsets" % (p, tuple(t.shape)))
+    if head_off is None:
+        base, extra = divmod(H, world)
+        hoff = [0]
+        for p in range(world):
+            hoff.append(hoff[-1] + base + (1 if p < extra else 0))
+    else:
+        hoff = [int(x) for x in head_off]
+    Hr = hoff[rank + 1] - hoff[rank]
+    _dev(o, "o")
+    _dev(lse, "lse")
+    if tuple(o.shape) != (B, S, Hr, D) or tuple(lse.shape) != (B, S, Hr) or lse.dtype != torch.float32:
+        raise ValueError("o must be [B, S, H_r, D] and lse [B, S, H_r] fp32")
+    m = mask if mask is not None else mask_full()
+    ws_ptr, ws_n = 0, 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_ptr, ws_n = workspace.data_ptr(), workspace.numel()
+    ptrs = lambda ts: (ctypes.c_void_p * world)(*[t.data_ptr() if t.numel() else 0 for t in ts])
+    _check(lib().usp_attn_fwd_lse_gather(UAA_BF16, world, rank, _i64_array(seq_off), _i64_array(hoff), B, H, D,
+                                         ptrs(q_shards), ptrs(k_shards), ptrs(v_shards), k_shard, o.data_ptr(),
+                                         _code(o.dtype, "o"), lse.data_ptr(), float(scale), ctypes.byref(m),
+                                         ws_ptr, ws_n, 1 if accumulate else 0, _stream(o)))

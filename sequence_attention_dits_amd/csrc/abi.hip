@@ -281,9 +281,20 @@ UAA_EXPORT size_t usp_attn_workspace_bytes(int dtype, int64_t B, int64_t H, int6
     return (size_t)plan_ws_bytes(attn_split_plan(dtype, B, H, Sq, Sk, D, mask), B, H, Sq);
 }
 
+// Queries gathered from token shards (usp_attn_fwd_lse_gather): every shard
+// holds its tokens with row_heads heads each, of which this rank reads
+// head0 .. head0 + H - 1.
+struct GatherSrc {
+    int world;
+    const int64_t* seq_off;   // host, world + 1, validated by the caller
+    const void* const* q_shards;
+    int64_t row_heads, head0;
+};
+
 static int attn_impl(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, const void* q,
                      const void* k, const void* v, void* o, int o_dtype, float* lse, float scale,
-                     const usp_mask* mask, void* workspace, size_t workspace_bytes, int acc, void* stream)
+                     const usp_mask* mask, void* workspace, size_t workspace_bytes, int acc, const GatherSrc* g,
+                     void* stream)
 {
     if (dtype != UAA_BF16 && dtype != UAA_FP32)
         return fail(UAA_ERR_INVALID_ARG, "attn: dtype must be UAA_BF16 or UAA_FP32, got %d", dtype);
@@ -298,16 +309,23 @@ static int attn_impl(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, in
     if (D != 64 && D != 128) return fail(UAA_ERR_UNSUPPORTED, "attn: D must be 64 or 128, got %lld", (long long)D);
     if (dtype == UAA_FP32 && o_dtype != UAA_FP32)
         return fail(UAA_ERR_UNSUPPORTED, "attn: fp32 input needs fp32 output");
-    if ((double)B * (Sq > Sk ? Sq : Sk) * H * D > (double)kMaxElems)
+    const int64_t RH = g != nullptr ? g->row_heads : H;   // heads per input token
+    if ((double)B * (Sq > Sk ? Sq : Sk) * RH * D > (double)kMaxElems)
         return fail(UAA_ERR_INVALID_ARG, "attn: tensor too large");
     if (B == 0 || H == 0 || Sq == 0) return UAA_OK;
-    if (q == nullptr || o == nullptr || lse == nullptr)
+    if ((g == nullptr && q == nullptr) || o == nullptr || lse == nullptr)
         return fail(UAA_ERR_INVALID_ARG, "attn: q, o and lse must not be NULL");
     if (Sk > 0 && (k == nullptr || v == nullptr))
         return fail(UAA_ERR_INVALID_ARG, "attn: k and v must not be NULL when Sk > 0");
-    if (!aligned(q, 16) || !aligned(o, 16) || (Sk > 0 && (!aligned(k, 16) || !aligned(v, 16))))
+    if ((g == nullptr && !aligned(q, 16)) || !aligned(o, 16) || (Sk > 0 && (!aligned(k, 16) || !aligned(v, 16))))
         return fail(UAA_ERR_INVALID_ARG, "attn: q, k, v and o must be 16-byte aligned");
     if (!aligned(lse, 4)) return fail(UAA_ERR_INVALID_ARG, "attn: lse must be 4-byte aligned");
+    if (g != nullptr)
+        for (int p = 0; p < g->world; ++p) {
+            if (g->seq_off[p + 1] == g->seq_off[p]) continue;
+            if (g->q_shards[p] == nullptr || !aligned(g->q_shards[p], 16))
+                return fail(UAA_ERR_INVALID_ARG, "attn: q shard %d is NULL or not 16-byte aligned", p);
+        }
 
     uaa::AttnArgs a{};
     a.q = q;
@@ -319,6 +337,14 @@ static int attn_impl(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, in
     a.H = H;
     a.Sq = Sq;
     a.Sk = Sk;
+    a.row_heads = RH;
+    a.head0 = g != nullptr ? g->head0 : 0;
+    a.n_qsh = 0;
+    if (g != nullptr) {
+        a.n_qsh = g->world;
+        for (int p = 0; p <= g->world; ++p) a.q_row0[p] = (int32_t)g->seq_off[p];
+        for (int p = 0; p < g->world; ++p) a.q_sh[p] = g->q_shards[p];
+    }
     a.scale = scale;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
     a.masked = 0;
@@ -330,7 +356,7 @@ static int attn_impl(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, in
         rc = side_map(*mask, false, Sk, a.kmap);
         if (rc != UAA_OK) return rc;
     }
-    if (dtype == UAA_BF16 && ((double)(Sq > Sk ? Sq : Sk) * H * D * 2 >= 4294967296.0))
+    if (dtype == UAA_BF16 && ((double)(Sq > Sk ? Sq : Sk) * RH * D * 2 >= 4294967296.0))
         return fail(UAA_ERR_UNSUPPORTED, "attn: one batch of q or k/v must stay below 4 GiB");
     // the launcher sets the q-tile count for its tile height; bound the grid here
     if (((Sq + 63) / 64) * H * B >= kMaxIdx32) return fail(UAA_ERR_INVALID_ARG, "attn: grid too large");
@@ -354,7 +380,7 @@ UAA_EXPORT int usp_attn_fwd_lse(int dtype, int64_t B, int64_t H, int64_t Sq, int
                                 const void* q, const void* k, const void* v, void* o, int o_dtype,
                                 float* lse, float scale, const usp_mask* mask, void* stream)
 {
-    return attn_impl(dtype, B, H, Sq, Sk, D, q, k, v, o, o_dtype, lse, scale, mask, nullptr, 0, 0, stream);
+    return attn_impl(dtype, B, H, Sq, Sk, D, q, k, v, o, o_dtype, lse, scale, mask, nullptr, 0, 0, nullptr, stream);
 }
 
 UAA_EXPORT int usp_attn_fwd_lse_ws(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
@@ -363,7 +389,7 @@ UAA_EXPORT int usp_attn_fwd_lse_ws(int dtype, int64_t B, int64_t H, int64_t Sq, 
                                    size_t workspace_bytes, void* stream)
 {
     return attn_impl(dtype, B, H, Sq, Sk, D, q, k, v, o, o_dtype, lse, scale, mask, workspace, workspace_bytes,
-                     0, stream);
+                     0, nullptr, stream);
 }
 
 UAA_EXPORT int usp_attn_fwd_lse_acc(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
@@ -372,7 +398,48 @@ UAA_EXPORT int usp_attn_fwd_lse_acc(int dtype, int64_t B, int64_t H, int64_t Sq,
                                     size_t workspace_bytes, void* stream)
 {
     return attn_impl(dtype, B, H, Sq, Sk, D, q, k, v, o, o_dtype, lse, scale, mask, workspace, workspace_bytes,
-                     1, stream);
+                     1, nullptr, stream);
+}
+
+UAA_EXPORT int usp_attn_fwd_lse_gather(int dtype, int world, int rank, const int64_t* seq_off,
+                                       const int64_t* head_off, int64_t B, int64_t H, int64_t D,
+                                       const void* const* q_shards, const void* const* k_shards,
+                                       const void* const* v_shards, int k_shard, void* o, int o_dtype,
+                                       float* lse, float scale, const usp_mask* mask, void* workspace,
+                                       size_t workspace_bytes, int accumulate, void* stream)
+{
+    if (dtype != UAA_BF16)
+        return fail(dtype == UAA_FP32 ? UAA_ERR_UNSUPPORTED : UAA_ERR_INVALID_ARG,
+                    "attn gather: bf16 input only, got dtype %d", dtype);
+    if (world < 1 || world > UAA_MAX_GATHER_WORLD)
+        return fail(UAA_ERR_INVALID_ARG, "attn gather: world must be in [1, %d], got %d", UAA_MAX_GATHER_WORLD, world);
+    if (rank < 0 || rank >= world) return fail(UAA_ERR_INVALID_ARG, "attn gather: rank %d outside [0, %d)", rank, world);
+    if (k_shard < 0 || k_shard >= world)
+        return fail(UAA_ERR_INVALID_ARG, "attn gather: k_shard %d outside [0, %d)", k_shard, world);
+    if (B < 0 || H < 1) return fail(UAA_ERR_INVALID_ARG, "attn gather: need B >= 0 and H >= 1");
+    if (seq_off == nullptr) return fail(UAA_ERR_INVALID_ARG, "attn gather: seq_off is NULL");
+    if (seq_off[0] != 0) return fail(UAA_ERR_INVALID_ARG, "attn gather: seq_off[0] must be 0");
+    for (int p = 0; p < world; ++p)
+        if (seq_off[p + 1] < seq_off[p])
+            return fail(UAA_ERR_INVALID_ARG, "attn gather: seq_off decreases at rank %d", p);
+    if (seq_off[world] >= kMaxIdx32) return fail(UAA_ERR_INVALID_ARG, "attn gather: sequence too long");
+    int64_t hoff[UAA_MAX_WORLD + 1];
+    if (head_off == nullptr) {
+        even_split(H, world, hoff);
+    } else {
+        for (int p = 0; p <= world; ++p) hoff[p] = head_off[p];
+    }
+    if (hoff[0] != 0 || hoff[world] != H)
+        return fail(UAA_ERR_INVALID_ARG, "attn gather: head_off must run from 0 to H = %lld", (long long)H);
+    for (int p = 0; p < world; ++p)
+        if (hoff[p + 1] <= hoff[p])
+            return fail(UAA_ERR_INVALID_ARG, "attn gather: rank %d gets no heads (head_off must strictly increase)", p);
+    if (q_shards == nullptr || k_shards == nullptr || v_shards == nullptr)
+        return fail(UAA_ERR_INVALID_ARG, "attn gather: a shard array is NULL");
+    const GatherSrc g{world, seq_off, q_shards, H, hoff[rank]};
+    return attn_impl(dtype, B, hoff[rank + 1] - hoff[rank], seq_off[world], seq_off[k_shard + 1] - seq_off[k_shard], D,
+                     nullptr, k_shards[k_shard], v_shards[k_shard], o, o_dtype, lse, scale, mask, workspace,
+                     workspace_bytes, accumulate ? 1 : 0, &g, stream);
 }
 
 UAA_EXPORT int usp_lse_merge(int n_parts, int64_t B, int64_t S, int64_t H, int64_t D,

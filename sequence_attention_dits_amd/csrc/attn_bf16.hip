@@ -162,31 +162,55 @@ __global__ __launch_bounds__(64 * kWaves, D == 64 ? 4 : 2) void attn_bf16_kernel
     const int lane = tid & 63;
     const int l32 = lane & 31, hg = lane >> 5;
     const int64_t H = a.H, Sq = a.Sq, Sk = a.Sk;
-    const uint32_t ld2 = (uint32_t)(H * D * 2);   // bytes between consecutive tokens
+    const int64_t RH = a.row_heads, h_in = a.head0 + hh;   // heads per input token; this head's slot
+    const uint32_t ld2 = (uint32_t)(RH * D * 2);   // bytes between consecutive tokens of the inputs
     const int64_t q0 = qt * kBM;
     const int64_t i = q0 + 32 * wave + l32;       // this lane's query row
 
-    const unsigned char* qbase = static_cast<const unsigned char*>(a.q) + ((b * Sq) * H + hh) * D * 2;
-    const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + ((b * Sk) * H + hh) * D * 2;
-    const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + ((b * Sk) * H + hh) * D * 2;
+    const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + ((b * Sk) * RH + h_in) * D * 2;
+    const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + ((b * Sk) * RH + h_in) * D * 2;
 
     // Q: each wave copies its own 32 rows into its own LDS region with
     // whole-row loads (1 KB, RPD rows, per instruction; 16-byte units
     // swizzled as in the K tile; rows past Sq read as zero) and reads its
     // operands back once the prologue's copies have landed -- instead of
-    // gathering 16-byte pieces of 32 rows per load instruction.
+    // gathering 16-byte pieces of 32 rows per load instruction.  Gathering
+    // from token shards, the rows of one shard are copied per pass (a wave's
+    // rows straddle a shard boundary only when a shard's length is not a
+    // multiple of 32), with the lanes of other rows masked off.
     lds_u8* const qst = (lds_u8*)(smem + 3 * TB + 2 * VTB) + wave * 32 * ROWB;
     {
         constexpr int UPRQ = D / 8, RPD = 1024 / ROWB;
         const int64_t r0 = q0 + 32 * wave;
-        const uint32_t nrec = Sq > r0 ? (uint32_t)((Sq - 1 - r0) * ld2 + D * 2) : 0u;
-        const __amdgpu_buffer_rsrc_t qr =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(qbase + (Sq > r0 ? r0 : 0) * ld2), (short)0, nrec, 0x00020000);
+        auto copy_rows = [&](const unsigned char* base, uint32_t nrec, int lo, int hi, bool all) {
+            // rows [lo, hi) of the wave's 32 (all: every row, the rest reading
+            // as zero) from `base` = the row r0 + lo
+            const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, 0x00020000);
 #pragma unroll
-        for (int n = 0; n < 32 * ROWB / 1024; ++n) {
-            const int row = n * RPD + lane / UPRQ;
-            const uint32_t off = (uint32_t)row * ld2 + (uint32_t)(((lane % UPRQ) ^ (row & (UPRQ - 1))) * 16);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, qst + n * 1024, 16, off, 0, 0, 0);
+            for (int n = 0; n < 32 * ROWB / 1024; ++n) {
+                const int row = n * RPD + lane / UPRQ;
+                const uint32_t off = (uint32_t)(row - lo) * ld2 + (uint32_t)(((lane % UPRQ) ^ (row & (UPRQ - 1))) * 16);
+                if (all || (row >= lo && row < hi)) __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, qst + n * 1024, 16, off, 0, 0, 0);
+            }
+        };
+        if (a.n_qsh == 0) {
+            const unsigned char* qbase = static_cast<const unsigned char*>(a.q) + ((b * Sq) * RH + h_in) * D * 2;
+            const uint32_t nrec = Sq > r0 ? (uint32_t)((Sq - 1 - r0) * ld2 + D * 2) : 0u;
+            copy_rows(qbase + (Sq > r0 ? r0 : 0) * ld2, nrec, 0, 32, true);
+        } else {
+            const int64_t r_end = Sq < r0 + 32 ? Sq : r0 + 32;
+            if (r_end < r0 + 32) copy_rows(static_cast<const unsigned char*>(a.k), 0u, (int)(r_end > r0 ? r_end - r0 : 0), 32, false);
+            int p = 0;
+            for (int64_t rs = r0; rs < r_end;) {   // one pass per shard the rows touch
+                while (a.q_row0[p + 1] <= rs) ++p;
+                const int64_t sp0 = a.q_row0[p], sp = a.q_row0[p + 1] - sp0;
+                const int64_t re = a.q_row0[p + 1] < r_end ? a.q_row0[p + 1] : r_end;
+                const unsigned char* sbase = static_cast<const unsigned char*>(a.q_sh[p]) +
+                                             ((b * sp + (rs - sp0)) * RH + h_in) * D * 2;
+                copy_rows(sbase, (uint32_t)((re - rs - 1) * ld2 + D * 2), (int)(rs - r0), (int)(re - r0),
+                          rs == r0 && re == r0 + 32);
+                rs = re;
+            }
         }
     }
 

@@ -78,13 +78,24 @@ struct PosMap {
     int64_t base0, base1, stride, seg_len;
 };
 
+constexpr int kMaxGather = UAA_MAX_GATHER_WORLD;
+
 struct AttnArgs {
-    const void* q;
-    const void* k;
+    const void* q;        // [B, Sq, row_heads, D]; unused when n_qsh > 0
+    const void* k;        // [B, Sk, row_heads, D]
     const void* v;
     void* o;
     float* lse;
-    int64_t B, H, Sq, Sk;
+    int64_t B, H, Sq, Sk; // H: heads of the output (and of the work grid)
+    // Inputs read head head0 + h of tokens of row_heads heads each (the
+    // plain call: row_heads = H, head0 = 0).  With n_qsh > 0 the queries are
+    // gathered from token shards: query row r is token r of the sequence,
+    // held by shard p (q_row0[p] <= r < q_row0[p+1]) at q_sh[p] as
+    // [B, q_row0[p+1] - q_row0[p], row_heads, D].
+    int64_t row_heads, head0;
+    int32_t n_qsh;
+    int32_t q_row0[kMaxGather + 1];
+    const void* q_sh[kMaxGather];
     float scale;          // softmax scale as given
     float scale_log2;     // scale * log2(e)
     int32_t masked;       // 0: every key allowed; 1: kpos(j) <= qpos(i)

@@ -153,6 +153,27 @@ def test_workspace_call_validates_like_the_plain_call():
     assert rc == -1 and "256-byte" in msg, (rc, msg)
 
 
+def test_gather_validation():
+    lib = uaa.lib()
+    m = uaa.mask_full()
+    so = (ctypes.c_int64 * 3)(0, 4, 8)
+    sh = (ctypes.c_void_p * 2)(FAKE, FAKE)
+
+    def call(dtype=0, world=2, rank=0, seq=so, H=2, D=128, k_shard=0, o=FAKE):
+        rc = lib.usp_attn_fwd_lse_gather(dtype, world, rank, seq, None, 1, H, D, sh, sh, sh, k_shard, o, 0, FAKE,
+                                         0.1, ctypes.byref(m), None, 0, 0, None)
+        return rc, lib.uaa_last_error().decode()
+
+    assert call(dtype=1)[0] == -2                      # fp32: unsupported
+    assert call(world=9)[0] == -1 and "world" in call(world=9)[1]
+    assert call(rank=2)[0] == -1
+    assert call(k_shard=-1)[0] == -1 and "k_shard" in call(k_shard=-1)[1]
+    assert call(seq=(ctypes.c_int64 * 3)(0, 5, 4))[0] == -1
+    assert call(H=1)[0] == -1 and "no heads" in call(H=1)[1]
+    assert call(D=96)[0] == -2
+    assert call(o=FAKE + 8)[0] == -1
+
+
 def test_workspace_bytes_zero_where_no_split_applies():
     lib = uaa.lib()
     full, causal = uaa.mask_full(), uaa.mask_causal(0, 0)
