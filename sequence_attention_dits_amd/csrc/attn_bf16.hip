@@ -170,6 +170,68 @@ __global__ __launch_bounds__(64 * kWaves, D == 64 ? 4 : 2) void attn_bf16_kernel
     const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + ((b * Sk) * RH + h_in) * D * 2;
     const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + ((b * Sk) * RH + h_in) * D * 2;
 
+    // Masking: position ranges of the workgroup's rows and of this wave's,
+    // and for this lane's row the allowed keys as index limits: key j is
+    // allowed iff j < lim0 (first piece of the key map, j < segk) or j < lim1
+    // (second piece).  Each piece of a position map increases, so the allowed
+    // keys of a piece are a prefix of it; without a mask only the ragged end
+    // of the keys counts.
+    int64_t wg_qmax = 0, w_qmin = 0, w_qmax = 0;
+    const bool wave_live = q0 + 32 * wave < Sq;
+    const int32_t sk32 = (int32_t)Sk;
+    int32_t segk = sk32, lim0 = sk32, lim1 = sk32;
+    if (MASKED) {
+        int64_t dummy;
+        const int64_t wg_hi = q0 + kBM < Sq ? q0 + kBM : Sq;
+        pos_range(a.qmap, q0, wg_hi, dummy, wg_qmax);
+        if (wave_live) {
+            const int64_t w_lo = q0 + 32 * wave;
+            const int64_t w_hi = w_lo + 32 < Sq ? w_lo + 32 : Sq;
+            pos_range(a.qmap, w_lo, w_hi, w_qmin, w_qmax);
+        }
+        segk = (int32_t)(a.kmap.seg_len < Sk ? a.kmap.seg_len : Sk);
+        const int64_t qp = pos_of(a.qmap, i);
+        lim0 = (int32_t)allowed_prefix(a.kmap.base0, a.kmap.stride, qp, segk);
+        lim1 = segk + (int32_t)allowed_prefix(a.kmap.base1, a.kmap.stride, qp, Sk - segk);
+    }
+    // key tiles [t_beg, n_tiles) of this workgroup: all of them, or one piece
+    const int n_all = (int)((Sk + kBN - 1) / kBN);
+    const int t_beg = SPLIT ? (int)((int64_t)piece * n_all / np) : 0;
+    const int n_tiles = SPLIT ? (int)((int64_t)(piece + 1) * n_all / np) : n_all;
+    // Key index sets as unions of two intervals, one per piece of the key
+    // map (positions increase within a piece, so the keys a position q may
+    // see are a prefix of each piece), fixed here once so that the tile loop
+    // does a few 32-bit compares per tile:
+    //   live   [0, ln0) u [segk, segk + ln1): keys the workgroup's last row sees
+    //   wave   [0, wa0) u [segk, segk + wa1): keys some row of this wave sees
+    //   full   [0, wf0) u [segk, segk + wf1): keys every row of this wave sees
+    int32_t ln0 = sk32, ln1 = 0, wa0 = sk32, wa1 = 0, wf0 = sk32, wf1 = 0;
+    if (MASKED) {
+        const int64_t n1 = Sk - segk;
+        ln0 = (int32_t)allowed_prefix(a.kmap.base0, a.kmap.stride, wg_qmax, segk);
+        ln1 = (int32_t)allowed_prefix(a.kmap.base1, a.kmap.stride, wg_qmax, n1);
+        wa0 = (int32_t)allowed_prefix(a.kmap.base0, a.kmap.stride, w_qmax, segk);
+        wa1 = (int32_t)allowed_prefix(a.kmap.base1, a.kmap.stride, w_qmax, n1);
+        wf0 = (int32_t)allowed_prefix(a.kmap.base0, a.kmap.stride, w_qmin, segk);
+        wf1 = (int32_t)allowed_prefix(a.kmap.base1, a.kmap.stride, w_qmin, n1);
+    }
+    // does [j0, j1) meet [0, p0) u [segk, segk + p1)?
+    auto meets = [&](int32_t j0, int32_t j1, int32_t p0, int32_t p1) {
+        return j0 < p0 || (j1 > segk && (j0 > segk ? j0 : segk) < segk + p1);
+    };
+    // is [j0, j1) inside it?
+    auto inside = [&](int32_t j0, int32_t j1, int32_t p0, int32_t p1) {
+        return (j0 >= segk || (j1 < segk ? j1 : segk) <= p0) && (j1 <= segk || j1 <= segk + p1);
+    };
+    // live tiles: [0, lt0) and [lt1b, lt1e)
+    const int lt0 = (ln0 + kBN - 1) / kBN;
+    const int lt1b = ln1 > 0 ? segk / kBN : n_all, lt1e = ln1 > 0 ? (segk + ln1 + kBN - 1) / kBN : n_all;
+    auto next_live = [&](int t) -> int {   // first live tile >= t, or n_tiles
+        if (!MASKED || t < lt0) return t < n_tiles ? t : n_tiles;
+        if (t < lt1b) t = lt1b;
+        return t < lt1e && t < n_tiles ? t : n_tiles;
+    };
+
     // Q: each wave copies its own 32 rows into its own LDS region with
     // whole-row loads (1 KB, RPD rows, per instruction; 16-byte units
     // swizzled as in the K tile; rows past Sq read as zero) and reads its
@@ -179,7 +241,7 @@ __global__ __launch_bounds__(64 * kWaves, D == 64 ? 4 : 2) void attn_bf16_kernel
     // rows straddle a shard boundary only when a shard's length is not a
     // multiple of 32), with the lanes of other rows masked off.
     lds_u8* const qst = (lds_u8*)(smem + 3 * TB + 2 * VTB) + wave * 32 * ROWB;
-    {
+    if (next_live(t_beg) < n_tiles) {   // a workgroup without a live key tile needs no Q
         constexpr int UPRQ = D / 8, RPD = 1024 / ROWB;
         const int64_t r0 = q0 + 32 * wave;
         auto copy_rows = [&](const unsigned char* base, uint32_t nrec, int lo, int hi, bool all) {
@@ -213,47 +275,6 @@ __global__ __launch_bounds__(64 * kWaves, D == 64 ? 4 : 2) void attn_bf16_kernel
             }
         }
     }
-
-    // Masking: position ranges of the workgroup's rows and of this wave's,
-    // and for this lane's row the allowed keys as index limits: key j is
-    // allowed iff j < lim0 (first piece of the key map, j < segk) or j < lim1
-    // (second piece).  Each piece of a position map increases, so the allowed
-    // keys of a piece are a prefix of it; without a mask only the ragged end
-    // of the keys counts.
-    int64_t wg_qmax = 0, w_qmin = 0, w_qmax = 0;
-    const bool wave_live = q0 + 32 * wave < Sq;
-    const int32_t sk32 = (int32_t)Sk;
-    int32_t segk = sk32, lim0 = sk32, lim1 = sk32;
-    if (MASKED) {
-        int64_t dummy;
-        const int64_t wg_hi = q0 + kBM < Sq ? q0 + kBM : Sq;
-        pos_range(a.qmap, q0, wg_hi, dummy, wg_qmax);
-        if (wave_live) {
-            const int64_t w_lo = q0 + 32 * wave;
-            const int64_t w_hi = w_lo + 32 < Sq ? w_lo + 32 : Sq;
-            pos_range(a.qmap, w_lo, w_hi, w_qmin, w_qmax);
-        }
-        segk = (int32_t)(a.kmap.seg_len < Sk ? a.kmap.seg_len : Sk);
-        const int64_t qp = pos_of(a.qmap, i);
-        lim0 = (int32_t)allowed_prefix(a.kmap.base0, a.kmap.stride, qp, segk);
-        lim1 = segk + (int32_t)allowed_prefix(a.kmap.base1, a.kmap.stride, qp, Sk - segk);
-    }
-    // key tiles [t_beg, n_tiles) of this workgroup: all of them, or one piece
-    const int n_all = (int)((Sk + kBN - 1) / kBN);
-    const int t_beg = SPLIT ? (int)((int64_t)piece * n_all / np) : 0;
-    const int n_tiles = SPLIT ? (int)((int64_t)(piece + 1) * n_all / np) : n_all;
-    auto tile_live = [&](int t) -> bool {  // may any row of the workgroup see a key of tile t?
-        if (!MASKED) return true;
-        const int64_t j0 = (int64_t)t * kBN;
-        const int64_t j1 = j0 + kBN < Sk ? j0 + kBN : Sk;
-        int64_t kmin, kmax;
-        pos_range(a.kmap, j0, j1, kmin, kmax);
-        return kmin <= wg_qmax;
-    };
-    auto next_live = [&](int t) -> int {
-        while (t < n_tiles && !tile_live(t)) ++t;
-        return t;
-    };
 
     // ---- V staging ---------------------------------------------------------
     // D = 128: wave w stages unit group g = w.  Lane (i, b) = (lane / 16,
@@ -409,11 +430,9 @@ __global__ __launch_bounds__(64 * kWaves, D == 64 ? 4 : 2) void attn_bf16_kernel
         const int64_t j0 = (int64_t)t * kBN;
         bool any = wave_live, per_elem = j0 + kBN > Sk;
         if (MASKED && wave_live) {
-            const int64_t j1 = j0 + kBN < Sk ? j0 + kBN : Sk;
-            int64_t kmin, kmax;
-            pos_range(a.kmap, j0, j1, kmin, kmax);
-            any = kmin <= w_qmax;
-            per_elem = per_elem || kmax > w_qmin;
+            const int32_t j0s = t * kBN, j1s = j0s + kBN < sk32 ? j0s + kBN : sk32;
+            any = meets(j0s, j1s, wa0, wa1);
+            per_elem = per_elem || !inside(j0s, j1s, wf0, wf1);
         }
 
         // With D = 128 every wave computes every live tile (the global loads
