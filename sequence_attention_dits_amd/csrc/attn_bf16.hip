@@ -156,6 +156,10 @@ __global__ __launch_bounds__(64 * kWaves, D == 64 ? 4 : 2) void attn_bf16_kernel
         unit_coords(a, unit, qt, hh, b);
     } else {
         decode_tile(a, qt, hh, b);
+        // Masked: with every mask kind later rows of a head see at least as
+        // many keys, so the q tiles run last-first -- the longest work is
+        // dispatched first and the short tiles fill in at the end.
+        if (MASKED) qt = a.n_qtiles - 1 - qt;
     }
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
