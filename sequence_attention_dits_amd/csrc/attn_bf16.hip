@@ -154,11 +154,18 @@ __global__ __launch_bounds__(64 * kWaves, D == 64 ? 4 : 2) void attn_bf16_kernel
             unit = xcd_logical(L - npc, nw);
         }
         unit_coords(a, unit, qt, hh, b);
+    } else if (MASKED && gridDim.x % 8u == 0u && (gridDim.x / 8u) % (uint32_t)a.n_qtiles == 0u) {
+        // Masked, every XCD holding whole heads: with every mask kind later
+        // rows of a head see at least as many keys, so each XCD's workgroups
+        // (blockIdx = 8 j + x on XCD x) take its heads' q tiles last-first
+        // with the heads interleaved -- the longest units of the XCD are
+        // dispatched first and the short ones fill in at the end.
+        const uint32_t nq = (uint32_t)a.n_qtiles, per = gridDim.x / 8u, hpx = per / nq;
+        const uint32_t x = blockIdx.x % 8u, j = blockIdx.x / 8u;
+        unit_coords(a, x * per + (j % hpx) * nq + (nq - 1u - j / hpx), qt, hh, b);
     } else {
         decode_tile(a, qt, hh, b);
-        // Masked: with every mask kind later rows of a head see at least as
-        // many keys, so the q tiles run last-first -- the longest work is
-        // dispatched first and the short tiles fill in at the end.
+        // masked: q tiles of a head last-first (see above)
         if (MASKED) qt = a.n_qtiles - 1 - qt;
     }
     const int tid = threadIdx.x;
