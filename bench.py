@@ -29,7 +29,7 @@ the stream the kernels run on.
 Other workloads (--workload): flux1008 (the same step on the non-divisible
 4481-token UAA share), and two Ring-only shares whose step is one attention
 launch per K/V chunk plus the merge: qwen1328 (Qwen-Image 1328x1328, 2
-chunks of 3493, Ring-step update) and longctx (32768-token causal zigzag
+chunks of 3493, then usp_lse_merge) and longctx (32768-token causal zigzag
 layout, Q = chunks {1, 6}, 8 chunks of 4096 masked by global position, on
 two streams, then one 8-way merge launch).  There `value` counts only the
 allowed (query, key) pairs.  The per-kernel figures include the standalone
@@ -77,10 +77,11 @@ RING_WORKLOADS = ("qwen1328", "longctx")
 OVERLAP_WORKLOADS = ("longctx",)
 # Workloads whose chunk partials are merged by the Ring-step update inside
 # the attention launches (usp_attn_fwd_lse_acc) rather than by one N-way
-# merge launch: the two-chunk shares, where it saves the merge pass.  The
-# 8-chunk long-context share keeps the N-way merge (its launches overlap on
-# two streams, which a running accumulator would serialise).
-ACC_WORKLOADS = ("flux1024", "flux1008", "qwen1328")
+# merge launch: the FLUX shares, where it saves the merge pass.  The Qwen
+# and long-context workloads are defined with a usp_lse_merge of their
+# partials (N = 2 and N = 8) and keep it (their steps measured within ~3 %
+# and ~1 % of the accumulating form).
+ACC_WORKLOADS = ("flux1024", "flux1008")
 
 
 def parse():
@@ -384,17 +385,33 @@ class RingShare:
             return 1
         raise ValueError(name)
 
-    def attn_chunk(self, s, c, ws, acc=False):
+    def attn_chunk(self, s, c, ws, acc=False, into=None):
+        """Chunk c's attention into its partial buffers, or with acc into the
+        running (O, LSE) `into` (default: the result), merging unless c is
+        the first chunk accumulated there."""
         d = self.sets[s]
         a, b = self.kv[c]
-        o, l = (self.o, self.lse) if acc else (self.o_part[c], self.l_part[c])
+        if acc:
+            o, l = into if into is not None else (self.o, self.lse)
+        else:
+            o, l = self.o_part[c], self.l_part[c]
+        first = c == 0 if into is None else c < 2
         self.uaa.usp_attn_fwd_lse(d["q"], d["k"][:, a:b], d["v"][:, a:b], o, l, self.scale, self.masks[c],
-                                  workspace=ws, accumulate=acc and c > 0)
+                                  workspace=ws, accumulate=acc and not first)
 
     def step(self, s):
         """The attention of every chunk with the merge of the partials (see
         Share.step)."""
         torch = self.torch
+        if self.ring_acc and self.overlap_chunks:
+            # two running results, one per stream (chunks alternate), then
+            # the 2-way merge of the two
+            runs = [(self.o_part[0], self.l_part[0]), (self.o_part[1], self.l_part[1])]
+            chunks = [lambda w, c=c: self.attn_chunk(s, c, w, acc=True, into=runs[c % 2])
+                      for c in range(len(self.kv))]
+            _two_streams(torch, torch.cuda.current_stream(), self.side, chunks, self.ws)
+            self.uaa.usp_lse_merge([r[0] for r in runs], [r[1] for r in runs], self.o, self.lse)
+            return
         if self.ring_acc:
             for c in range(len(self.kv)):
                 self.attn_chunk(s, c, self.ws[0], acc=True)
