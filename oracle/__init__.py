@@ -13,6 +13,7 @@ from .oracle import (  # noqa: F401
     head2seq,
     seq2head_index,
     attention,
+    attention_bwd,
     lse_merge,
     ring_pass,
     uaa_pass,

@@ -7,7 +7,8 @@ library.
 The heavy steps (permute, attention, merge) are plain loops in ``oracle.c``;
 this module builds and loads that file, writes out the split and position
 definitions, and composes the steps into the Ring, Ulysses-Anything and
-Unified passes exactly as the pages describe them.
+Unified passes exactly as the pages describe them.  The attention backward
+is written here with numpy float64 matrix products as its steps.
 
 Pages cited (title, then section):
   [CP]  "Context parallelism" (diffusers documentation): "Ring Attention",
@@ -273,6 +274,72 @@ def lse_merge(o_parts: Sequence[np.ndarray], lse_parts: Sequence[np.ndarray]):
     if rc != 0:
         raise ValueError("orc_lse_merge rejected its arguments")
     return o.reshape(shape), lse.reshape(shape[:-1])
+
+
+# --------------------------------------------------------------------------
+# Backward of attention with LSE.  [USP] (pull request conversation): the
+# Unified / Ring attention carries a backward (a forward + backward test
+# script; the gradient count of the templated Unified attention's backward)
+# without writing it out.  Reading: the gradient of the forward above, by
+# the chain rule -- what any backward of the same forward must return.
+# --------------------------------------------------------------------------
+def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, scale: float,
+                  qpos: Optional[np.ndarray] = None, kpos: Optional[np.ndarray] = None,
+                  dlse: Optional[np.ndarray] = None):
+    """Gradients (dQ, dK, dV) of  L = sum(dout * O) + sum(dlse * LSE)  where
+    (O, LSE) = attention(q, k, v, scale, qpos, kpos).
+
+    q/dout [B,Sq,H,D], k/v [B,Sk,H,D], dlse [B,Sq,H] or None (zero); all
+    widened to float64.  Per (batch, head), with S = scale Q K^T (entries with
+    kpos > qpos removed), P = softmax(S) row by row and O = P V:
+        dV  = P^T dO
+        dP  = dO V^T
+        dS  = P * (dP - Delta + dlse),   Delta_i = sum_d dO_id O_id
+        dQ  = scale dS K,   dK = scale dS^T Q
+    (the softmax Jacobian is diag(P_i) - P_i P_i^T, and d LSE_i / d S_ij =
+    P_ij).  Rows with no allowed key have P = 0 and a constant LSE (-inf):
+    they add nothing, whatever their dout or dlse.
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    do = np.ascontiguousarray(dout, dtype=np.float64)
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if k.shape != (B, Sk, H, D) or v.shape != (B, Sk, H, D) or do.shape != q.shape:
+        raise ValueError("q/k/v/dout shape mismatch")
+    if (qpos is None) != (kpos is None):
+        raise ValueError("causal masking needs both position maps")
+    allowed = np.ones((Sq, Sk), dtype=bool)
+    if qpos is not None:
+        qpos = np.asarray(qpos, dtype=np.int64)
+        kpos = np.asarray(kpos, dtype=np.int64)
+        if qpos.shape != (Sq,) or kpos.shape != (Sk,):
+            raise ValueError("position map length mismatch")
+        allowed = kpos[None, :] <= qpos[:, None]
+    dl = np.zeros((B, Sq, H)) if dlse is None else np.asarray(dlse, dtype=np.float64)
+    if dl.shape != (B, Sq, H):
+        raise ValueError("dlse shape mismatch")
+    live = allowed.any(axis=1)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            Q, K, V, dO = q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h]
+            S = np.where(allowed, scale * (Q @ K.T), -np.inf)
+            m = np.where(live, S.max(axis=1, initial=-np.inf), 0.0)
+            E = np.exp(S - m[:, None])               # exp(-inf) = 0 for removed entries
+            P = E / np.where(live, E.sum(axis=1), 1.0)[:, None]
+            O = P @ V
+            dV = P.T @ dO
+            dP = dO @ V.T
+            delta = (dO * O).sum(axis=1)
+            dS = P * (dP - delta[:, None] + np.where(live, dl[b, :, h], 0.0)[:, None])
+            dq[b, :, h] = scale * (dS @ K)
+            dk[b, :, h] = scale * (dS.T @ Q)
+            dv[b, :, h] = dV
+    return dq, dk, dv
 
 
 # --------------------------------------------------------------------------
