@@ -328,6 +328,63 @@ int usp_lse_merge(int n_parts, int64_t B, int64_t S, int64_t H, int64_t D,
                   void* o_out, int out_dtype, float* lse_out, void* stream);
 
 /*
+ * usp_attn_bwd_delta -- the per-row statistic of the attention backward
+ * ([USP], pull request conversation: the Unified / Ring attention is trained
+ * through a backward of its forward; the backward itself is the chain rule
+ * through softmax):
+ *   delta[b, s, h] = sum_d dout[b, s, h, d] * o[b, s, h, d]  -  dlse[b, s, h]
+ * in fp32, with (o, lse) the forward's result over ALL key blocks of the
+ * rows (after the Ring merge), dout the gradient of o and dlse the gradient
+ * of lse (NULL: zero).
+ *
+ *   o, dout    device [B, S, H, D] dtype (UAA_BF16 or UAA_FP32)
+ *   dlse       device [B, S, H] fp32, or NULL
+ *   delta      device [B, S, H] fp32 (output)
+ * D: 64 or 128 (else UAA_ERR_UNSUPPORTED).  o, dout 16-byte aligned; dlse,
+ * delta 4-byte aligned.  delta must not overlap the inputs.  B, S or H = 0:
+ * no work.
+ * Returns UAA_OK, UAA_ERR_INVALID_ARG, UAA_ERR_UNSUPPORTED or UAA_ERR_HIP.
+ */
+int usp_attn_bwd_delta(int dtype, int64_t B, int64_t S, int64_t H, int64_t D, const void* o,
+                       const void* dout, const float* dlse, float* delta, void* stream);
+
+/*
+ * usp_attn_bwd -- gradients of one attention call (one Ring key block) of
+ * usp_attn_fwd_lse ([USP], as above).  With J the allowed keys of row i (as
+ * in the forward), lse the rows' LSE over all key blocks and delta from
+ * usp_attn_bwd_delta:
+ *   P_ij  = exp(scale <q_i, k_j> - lse_i)   (j in J; 0 otherwise, and 0 for
+ *                                            every j when lse_i = -inf)
+ *   dS_ij = P_ij (<dout_i, v_j> - delta_i)
+ *   dq_i  = scale sum_j dS_ij k_j,   dk_j = scale sum_i dS_ij q_i,
+ *   dv_j  = sum_i P_ij dout_i.
+ * For a single block (lse, o of this call) this is the gradient of
+ * sum(dout * o) + sum(dlse * lse); over the blocks of a Ring pass, dq summed
+ * over the blocks and each block's (dk, dv) are the gradients of the merged
+ * result.
+ *
+ *   q, dout    device [B, Sq, H, D] dtype
+ *   k, v       device [B, Sk, H, D] dtype
+ *   lse, delta device [B, Sq, H] fp32
+ *   dq         device [B, Sq, H, D] grad_dtype (output)
+ *   dk, dv     device [B, Sk, H, D] grad_dtype (output)
+ * accumulate = 0: the gradients are written; 1: added to what dq, dk, dv
+ * hold (in fp32, rounded once when grad_dtype is bf16).  dtype: UAA_BF16
+ * (bf16 matrix-core products, fp32 accumulation; UAA_FP32 input gives
+ * UAA_ERR_UNSUPPORTED).  grad_dtype: UAA_BF16 or UAA_FP32.  D: 64 or 128.
+ * scale: finite, > 0.  mask as in usp_attn_fwd_lse.  q, k, v, dout, dq, dk,
+ * dv 16-byte aligned; lse, delta 4-byte aligned.  Outputs must not overlap
+ * inputs or each other.  B = 0, H = 0 or Sq = Sk = 0: no work; Sq = 0 gives
+ * dk = dv = 0 (nothing added when accumulating); Sk = 0 gives dq = 0.  The
+ * two kernels (dk/dv, then dq) run in order on `stream`; no workspace.
+ * Returns UAA_OK, UAA_ERR_INVALID_ARG, UAA_ERR_UNSUPPORTED or UAA_ERR_HIP.
+ */
+int usp_attn_bwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                 const void* q, const void* k, const void* v, const void* dout,
+                 const float* lse, const float* delta, void* dq, void* dk, void* dv, int grad_dtype,
+                 float scale, const usp_mask* mask, int accumulate, void* stream);
+
+/*
  * uaa_last_error -- text describing the last non-zero status returned on
  * the calling thread ("" if none).  The pointer stays valid until the next
  * call on that thread.

@@ -9,6 +9,7 @@ from .oracle import (  # noqa: F401
     build,
     split_offsets,
     positions,
+    zigzag_chunks,
     seq2head,
     head2seq,
     seq2head_index,

@@ -30,6 +30,8 @@ from .binding import (  # noqa: F401
     attn_workspace,
     usp_attn_fwd_lse,
     usp_attn_fwd_lse_gather,
+    usp_attn_bwd,
+    usp_attn_bwd_delta,
     usp_lse_merge,
     usp_mask,
     uaa_seq2head_permute,

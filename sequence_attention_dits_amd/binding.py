@@ -124,6 +124,12 @@ def lib() -> ctypes.CDLL:
         l.usp_lse_merge.restype = ctypes.c_int
         l.usp_lse_merge.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_int,
                                     _c_p, _c_p, ctypes.c_int, _c_p, _c_p]
+        l.usp_attn_bwd_delta.restype = ctypes.c_int
+        l.usp_attn_bwd_delta.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p]
+        l.usp_attn_bwd.restype = ctypes.c_int
+        l.usp_attn_bwd.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p,
+                                   _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_int, ctypes.c_float,
+                                   ctypes.POINTER(usp_mask), ctypes.c_int, _c_p]
         l.uaa_last_error.restype = ctypes.c_char_p
         l.uaa_last_error.argtypes = []
         l.uaa_abi_version.restype = ctypes.c_int
@@ -372,3 +378,54 @@ def usp_attn_fwd_lse_gather(rank: int, q_shards: Sequence[torch.Tensor], k_shard
                                          ptrs(q_shards), ptrs(k_shards), ptrs(v_shards), k_shard, o.data_ptr(),
                                          _code(o.dtype, "o"), lse.data_ptr(), float(scale), ctypes.byref(m),
                                          ws_ptr, ws_n, 1 if accumulate else 0, _stream(o)))
+
+
+def usp_attn_bwd_delta(o: torch.Tensor, dout: torch.Tensor, delta: torch.Tensor,
+                       dlse: Optional[torch.Tensor] = None) -> None:
+    """delta [B,S,H] fp32 = rowsum(dout * o) - dlse for o, dout [B,S,H,D]."""
+    for t, n in ((o, "o"), (dout, "dout"), (delta, "delta")):
+        _dev(t, n)
+    if o.dim() != 4 or tuple(dout.shape) != tuple(o.shape) or dout.dtype != o.dtype:
+        raise ValueError("o and dout are [B, S, H, D] of one dtype")
+    B, S, H, D = o.shape
+    if tuple(delta.shape) != (B, S, H) or delta.dtype != torch.float32:
+        raise ValueError("delta must be [B, S, H] float32")
+    dl = 0
+    if dlse is not None:
+        _dev(dlse, "dlse")
+        if tuple(dlse.shape) != (B, S, H) or dlse.dtype != torch.float32:
+            raise ValueError("dlse must be [B, S, H] float32")
+        dl = dlse.data_ptr()
+    _check(lib().usp_attn_bwd_delta(_code(o.dtype, "o"), B, S, H, D, o.data_ptr(), dout.data_ptr(), dl,
+                                    delta.data_ptr(), _stream(o)))
+
+
+def usp_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
+                 delta: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, scale: float,
+                 mask: Optional[usp_mask] = None, accumulate: bool = False) -> None:
+    """Gradients of one attention call (one Ring key block) into caller-owned
+    dq [B,Sq,H,D], dk, dv [B,Sk,H,D] (bf16 or float32), from the rows' final
+    lse and delta (usp_attn_bwd_delta); accumulate=True adds into them."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout"), (lse, "lse"), (delta, "delta"), (dq, "dq"),
+                 (dk, "dk"), (dv, "dv")):
+        _dev(t, n)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or dout.shape != q.shape:
+        raise ValueError("q, dout [B, Sq, H, D] and k, v [B, Sk, H, D]")
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
+        raise ValueError("k/v shape %s does not match q %s" % (tuple(k.shape), tuple(q.shape)))
+    if k.dtype != q.dtype or v.dtype != q.dtype or dout.dtype != q.dtype:
+        raise ValueError("q, k, v, dout must share a dtype")
+    for t, n in ((lse, "lse"), (delta, "delta")):
+        if tuple(t.shape) != (B, Sq, H) or t.dtype != torch.float32:
+            raise ValueError("%s must be [B, Sq, H] float32" % n)
+    if tuple(dq.shape) != tuple(q.shape) or tuple(dk.shape) != tuple(k.shape) or tuple(dv.shape) != tuple(k.shape):
+        raise ValueError("dq must be shaped like q and dk, dv like k")
+    if dk.dtype != dq.dtype or dv.dtype != dq.dtype:
+        raise ValueError("dq, dk, dv must share a dtype")
+    m = mask if mask is not None else mask_full()
+    _check(lib().usp_attn_bwd(_code(q.dtype, "q"), B, H, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              dout.data_ptr(), lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), _code(dq.dtype, "dq"), float(scale), ctypes.byref(m),
+                              1 if accumulate else 0, _stream(q)))

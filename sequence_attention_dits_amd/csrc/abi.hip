@@ -481,3 +481,86 @@ UAA_EXPORT int usp_lse_merge(int n_parts, int64_t B, int64_t S, int64_t H, int64
     return hip_status(uaa::launch_merge(part_dtype, out_dtype, a, static_cast<hipStream_t>(stream)),
                       "merge launch");
 }
+
+// --------------------------------------------------------------------------
+// Attention backward.
+// --------------------------------------------------------------------------
+UAA_EXPORT int usp_attn_bwd_delta(int dtype, int64_t B, int64_t S, int64_t H, int64_t D, const void* o,
+                                  const void* dout, const float* dlse, float* delta, void* stream)
+{
+    if (dtype != UAA_BF16 && dtype != UAA_FP32)
+        return fail(UAA_ERR_INVALID_ARG, "bwd delta: dtype must be UAA_BF16 or UAA_FP32, got %d", dtype);
+    if (B < 0 || S < 0 || H < 0 || D < 1) return fail(UAA_ERR_INVALID_ARG, "bwd delta: bad sizes");
+    if (D != 64 && D != 128) return fail(UAA_ERR_UNSUPPORTED, "bwd delta: D must be 64 or 128, got %lld", (long long)D);
+    if ((double)B * S * H * D > (double)kMaxElems) return fail(UAA_ERR_INVALID_ARG, "bwd delta: tensor too large");
+    const int64_t rows = B * S * H;
+    if (rows == 0) return UAA_OK;
+    if (o == nullptr || dout == nullptr || delta == nullptr)
+        return fail(UAA_ERR_INVALID_ARG, "bwd delta: o, dout and delta must not be NULL");
+    if (!aligned(o, 16) || !aligned(dout, 16)) return fail(UAA_ERR_INVALID_ARG, "bwd delta: o and dout must be 16-byte aligned");
+    if (!aligned(delta, 4) || (dlse != nullptr && !aligned(dlse, 4)))
+        return fail(UAA_ERR_INVALID_ARG, "bwd delta: delta and dlse must be 4-byte aligned");
+    uaa::DeltaArgs a{o, dout, dlse, delta, rows};
+    return hip_status(uaa::launch_bwd_delta(dtype, (int)D, a, static_cast<hipStream_t>(stream)), "bwd delta launch");
+}
+
+UAA_EXPORT int usp_attn_bwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, const void* q,
+                            const void* k, const void* v, const void* dout, const float* lse, const float* delta,
+                            void* dq, void* dk, void* dv, int grad_dtype, float scale, const usp_mask* mask,
+                            int accumulate, void* stream)
+{
+    if (dtype != UAA_BF16 && dtype != UAA_FP32)
+        return fail(UAA_ERR_INVALID_ARG, "bwd: dtype must be UAA_BF16 or UAA_FP32, got %d", dtype);
+    if (grad_dtype != UAA_BF16 && grad_dtype != UAA_FP32)
+        return fail(UAA_ERR_INVALID_ARG, "bwd: grad_dtype must be UAA_BF16 or UAA_FP32, got %d", grad_dtype);
+    if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || D < 1) return fail(UAA_ERR_INVALID_ARG, "bwd: negative size");
+    if (!(scale > 0.f) || !isfinite(scale)) return fail(UAA_ERR_INVALID_ARG, "bwd: scale must be finite and > 0");
+    if (mask != nullptr && (mask->kind < USP_MASK_FULL || mask->kind > USP_MASK_STRIPE))
+        return fail(UAA_ERR_INVALID_ARG, "bwd: unknown mask kind %d", mask->kind);
+    if (accumulate != 0 && accumulate != 1) return fail(UAA_ERR_INVALID_ARG, "bwd: accumulate must be 0 or 1");
+    if (D != 64 && D != 128) return fail(UAA_ERR_UNSUPPORTED, "bwd: D must be 64 or 128, got %lld", (long long)D);
+    if (dtype == UAA_FP32) return fail(UAA_ERR_UNSUPPORTED, "bwd: fp32 input is not supported (bf16 only)");
+    if ((double)B * (Sq > Sk ? Sq : Sk) * H * D > (double)kMaxElems) return fail(UAA_ERR_INVALID_ARG, "bwd: tensor too large");
+    if (B == 0 || H == 0 || (Sq == 0 && Sk == 0)) return UAA_OK;
+    if (Sq > 0 && (q == nullptr || dout == nullptr || lse == nullptr || delta == nullptr || dq == nullptr))
+        return fail(UAA_ERR_INVALID_ARG, "bwd: q, dout, lse, delta and dq must not be NULL when Sq > 0");
+    if (Sk > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+        return fail(UAA_ERR_INVALID_ARG, "bwd: k, v, dk and dv must not be NULL when Sk > 0");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
+        !aligned(dk, 16) || !aligned(dv, 16))
+        return fail(UAA_ERR_INVALID_ARG, "bwd: q, k, v, dout, dq, dk and dv must be 16-byte aligned");
+    if (!aligned(lse, 4) || !aligned(delta, 4)) return fail(UAA_ERR_INVALID_ARG, "bwd: lse and delta must be 4-byte aligned");
+    // 32-bit buffer offsets within one (batch) slab, with room for a tile past the end
+    if ((double)((Sq > Sk ? Sq : Sk) + 256) * H * D * 2 >= 4294967296.0)
+        return fail(UAA_ERR_UNSUPPORTED, "bwd: one batch of q or k/v must stay below 4 GiB");
+    if (((Sk + 127) / 128) * H * B >= kMaxIdx32 || ((Sq + 255) / 256) * H * B >= kMaxIdx32)
+        return fail(UAA_ERR_INVALID_ARG, "bwd: grid too large");
+
+    uaa::BwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.lse = lse;
+    a.delta = delta;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.B = B;
+    a.H = H;
+    a.Sq = Sq;
+    a.Sk = Sk;
+    a.scale = scale;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    a.masked = 0;
+    a.accumulate = accumulate;
+    a.grad_bf16 = grad_dtype == UAA_BF16 ? 1 : 0;
+    if (mask != nullptr && mask->kind != USP_MASK_FULL) {
+        a.masked = 1;
+        int rc = side_map(*mask, true, Sq, a.qmap);
+        if (rc != UAA_OK) return rc;
+        rc = side_map(*mask, false, Sk, a.kmap);
+        if (rc != UAA_OK) return rc;
+    }
+    return hip_status(uaa::launch_attn_bwd_bf16((int)D, a, static_cast<hipStream_t>(stream)), "bwd launch");
+}

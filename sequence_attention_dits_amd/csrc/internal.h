@@ -133,4 +133,40 @@ int64_t attn_bf16_units(int64_t B, int64_t H, int64_t Sq);
 hipError_t launch_attn_bf16(int D, int o_dtype, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_fp32(int D, const AttnArgs& a, hipStream_t s);
 
+// --------------------------------------------------------------------------
+// Attention backward.  Tensors as in the forward: q, dout, dq [B, Sq, H, D];
+// k, v, dk, dv [B, Sk, H, D]; lse, delta [B, Sq, H] fp32.
+// --------------------------------------------------------------------------
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    const float* lse;     // natural log, over every key block of the rows
+    const float* delta;   // rowsum(dout * o) - dlse
+    void* dq;
+    void* dk;
+    void* dv;
+    int64_t B, H, Sq, Sk;
+    float scale;          // softmax scale as given
+    float scale_log2;     // scale * log2(e)
+    int32_t masked;       // 0: every key allowed; 1: kpos(j) <= qpos(i)
+    int32_t accumulate;   // 1: add into dq, dk, dv
+    int32_t grad_bf16;    // gradients stored as bf16 (else fp32)
+    int32_t n_tiles;      // work tiles per (batch, head) of the launched kernel, set by the launcher
+    PosMap qmap, kmap;
+};
+
+struct DeltaArgs {
+    const void* o;
+    const void* dout;
+    const float* dlse;    // may be null
+    float* delta;
+    int64_t rows;         // B * S * H
+};
+
+// dK/dV kernel then dQ kernel (bf16 inputs)
+hipError_t launch_attn_bwd_bf16(int D, const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_delta(int dtype, int D, const DeltaArgs& a, hipStream_t s);
+
 }  // namespace uaa

@@ -258,3 +258,58 @@ def test_multi_permute_validation():
     dst0 = _ptrs(FAKE, 0)
     assert lib.uaa_seq2head_permute_multi(2, 0, 0, 2, _i64(0, 2, 4), None, 1, 2, 8, 2, src, dst0, None) == -1
     assert "dst[1]" in lib.uaa_last_error().decode()
+
+
+def _bwd(dtype=0, B=1, H=1, Sq=4, Sk=4, D=128, q=FAKE, k=FAKE, v=FAKE, do=FAKE, lse=FAKE, delta=FAKE,
+         dq=FAKE, dk=FAKE, dv=FAKE, gdt=1, scale=0.1, mask=None, acc=0):
+    lib = uaa.lib()
+    m = mask if mask is not None else uaa.mask_full()
+    rc = lib.usp_attn_bwd(dtype, B, H, Sq, Sk, D, q, k, v, do, lse, delta, dq, dk, dv, gdt, scale,
+                          ctypes.byref(m), acc, None)
+    return rc, lib.uaa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(dtype=5), -1, "dtype"),
+    (dict(gdt=3), -1, "grad_dtype"),
+    (dict(Sk=-1), -1, "negative"),
+    (dict(scale=0.0), -1, "scale"),
+    (dict(scale=float("nan")), -1, "scale"),
+    (dict(acc=2), -1, "accumulate"),
+    (dict(D=96), -2, "D must be"),
+    (dict(dtype=1), -2, "fp32 input"),
+    (dict(delta=0), -1, "NULL"),
+    (dict(dv=0), -1, "NULL"),
+    (dict(dq=FAKE + 8), -1, "16-byte"),
+    (dict(lse=FAKE + 2), -1, "4-byte"),
+    (dict(mask=binding.usp_mask(kind=9)), -1, "mask kind"),
+    (dict(mask=uaa.mask_zigzag(2, [1], [2])), -1, "chunks hold"),
+    (dict(mask=uaa.mask_stripe(4, 1, 4)), -1, "stripe"),
+    (dict(Sq=1 << 26, H=64), -2, "4 GiB"),
+])
+def test_backward_validation(kw, code, text):
+    rc, msg = _bwd(**kw)
+    assert rc == code and text in msg, (rc, msg)
+
+
+def test_backward_empty_work_is_ok():
+    assert _bwd(B=0)[0] == 0
+    assert _bwd(H=0)[0] == 0
+    assert _bwd(Sq=0, Sk=0, q=0, k=0, v=0, do=0, lse=0, delta=0, dq=0, dk=0, dv=0)[0] == 0
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(dtype=4), -1, "dtype"),
+    (dict(D=32), -2, "D must be"),
+    (dict(o=0), -1, "NULL"),
+    (dict(dout=FAKE + 4), -1, "16-byte"),
+    (dict(dlse=FAKE + 1), -1, "4-byte"),
+])
+def test_backward_delta_validation(kw, code, text):
+    a = dict(dtype=0, B=1, S=4, H=2, D=128, o=FAKE, dout=FAKE, dlse=None, delta=FAKE)
+    a.update(kw)
+    lib = uaa.lib()
+    rc = lib.usp_attn_bwd_delta(a["dtype"], a["B"], a["S"], a["H"], a["D"], a["o"], a["dout"], a["dlse"],
+                                a["delta"], None)
+    assert rc == code and text in lib.uaa_last_error().decode(), (rc, lib.uaa_last_error())
+    assert lib.usp_attn_bwd_delta(0, 0, 4, 2, 128, 0, 0, None, 0, None) == 0
