@@ -97,6 +97,7 @@ def parse():
                         "merge launch (auto: per workload)")
     p.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough for 1 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-backward", action="store_true", help="skip the backward variant")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--pmc-probe", action="store_true",
                    help="only enqueue the dispatches that the HBM traffic counters are read on: a plain "
@@ -469,6 +470,58 @@ def ring_cpu_baseline(share: "RingShare", target_s: float):
                       % (n, share.Sq, share.H, len(share.kv), len(share.kv), elapsed)}
 
 
+def backward_variant(share, cfg_id: int, steps: int, warmup: int) -> dict:
+    """The backward of one step's attention: for a seeded output gradient
+    dO of the step's (O, LSE), delta = rowsum(dO * O) once, then
+    usp_attn_bwd per Ring chunk against the final LSE -- the first chunk
+    writes dQ, later chunks add into it, each chunk's dK, dV written fresh
+    (fp32 gradients).  Algorithmic FLOPs: 2.5x the forward's (the five
+    products S, dP, dV, dK, dQ over the allowed pairs)."""
+    import numpy as np
+
+    import synth
+    torch, uaa = share.torch, share.uaa
+    share.step(0)
+    if isinstance(share, RingShare):
+        d = share.sets[0]
+        q = d["q"]
+        chunks = [(d["k"][:, a:b], d["v"][:, a:b], m) for (a, b), m in zip(share.kv, share.masks)]
+    else:
+        q = share.qh["q"]
+        chunks = [(_contig(kc), _contig(vc), None) for kc, vc in share.kc]
+    B, Sq, H, D = q.shape
+    bits, _ = synth.tensor(cfg_id, 11, (B, Sq, H, D), "bf16")
+    dout = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+    delta = torch.empty_like(share.lse)
+    dq = torch.empty(B, Sq, H, D, device="cuda", dtype=torch.float32)
+    dkv = [(torch.empty(k.shape, device="cuda", dtype=torch.float32),
+            torch.empty(k.shape, device="cuda", dtype=torch.float32)) for k, _, _ in chunks]
+
+    def run():
+        uaa.usp_attn_bwd_delta(share.o, dout, delta)
+        for c, ((k, v, m), (dk, dv)) in enumerate(zip(chunks, dkv)):
+            uaa.usp_attn_bwd(q, k, v, dout, share.lse, delta, dq, dk, dv, share.scale, m,
+                             accumulate="dq" if c else False)
+
+    for _ in range(max(warmup, 1)):
+        run()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * 0.02))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2.5 * sum(share.attn_flops(c) for c in range(len(chunks)))
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms_per_step": round(ms, 4), "value": round(tf, 2), "unit": "TFLOP/s",
+            "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_step": flops,
+            "launches_per_step": 1 + len(chunks), "grad_dtype": "fp32"}
+
+
 def _contig(t):
     # a K/V chunk of the head-sharded tensor is a slice along S: with B = 1 it
     # is already contiguous, so no copy is made here
@@ -740,6 +793,10 @@ def main():
             "equals_default_step_bitwise": same,
         }
         del fgraphs
+
+    # the backward of the step's attention (usp_attn_bwd_delta + usp_attn_bwd)
+    if not args.no_backward:
+        variants["backward"] = backward_variant(share, cfg_id, args.steps, args.warmup)
 
     # timed region 2: per-kernel durations.  Each launch of the step is
     # repeated back to back over the rotating input sets between two HIP

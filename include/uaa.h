@@ -368,14 +368,16 @@ int usp_attn_bwd_delta(int dtype, int64_t B, int64_t S, int64_t H, int64_t D, co
  *   lse, delta device [B, Sq, H] fp32
  *   dq         device [B, Sq, H, D] grad_dtype (output)
  *   dk, dv     device [B, Sk, H, D] grad_dtype (output)
- * accumulate = 0: the gradients are written; 1: added to what dq, dk, dv
- * hold (in fp32, rounded once when grad_dtype is bf16).  dtype: UAA_BF16
+ * accumulate: bit 0 set -- dq is added to what dq holds, else written;
+ * bit 1 set -- dk and dv likewise (a Ring backward adds every block into dq,
+ * and each block's dk, dv into the buffers that travel with that block).
+ * Sums run in fp32 and are rounded once when grad_dtype is bf16.  dtype: UAA_BF16
  * (bf16 matrix-core products, fp32 accumulation; UAA_FP32 input gives
  * UAA_ERR_UNSUPPORTED).  grad_dtype: UAA_BF16 or UAA_FP32.  D: 64 or 128.
  * scale: finite, > 0.  mask as in usp_attn_fwd_lse.  q, k, v, dout, dq, dk,
  * dv 16-byte aligned; lse, delta 4-byte aligned.  Outputs must not overlap
  * inputs or each other.  B = 0, H = 0 or Sq = Sk = 0: no work; Sq = 0 gives
- * dk = dv = 0 (nothing added when accumulating); Sk = 0 gives dq = 0.  The
+ * dk = dv = 0 (nothing added with bit 1); Sk = 0 gives dq = 0.  The
  * two kernels (dk/dv, then dq) run in order on `stream`; no workspace.
  * Returns UAA_OK, UAA_ERR_INVALID_ARG, UAA_ERR_UNSUPPORTED or UAA_ERR_HIP.
  */

@@ -402,10 +402,14 @@ def usp_attn_bwd_delta(o: torch.Tensor, dout: torch.Tensor, delta: torch.Tensor,
 
 def usp_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
                  delta: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, scale: float,
-                 mask: Optional[usp_mask] = None, accumulate: bool = False) -> None:
+                 mask: Optional[usp_mask] = None, accumulate=False) -> None:
     """Gradients of one attention call (one Ring key block) into caller-owned
     dq [B,Sq,H,D], dk, dv [B,Sk,H,D] (bf16 or float32), from the rows' final
-    lse and delta (usp_attn_bwd_delta); accumulate=True adds into them."""
+    lse and delta (usp_attn_bwd_delta).  accumulate: False (write all), True
+    (add into all three), "dq" (add into dq only) or "dkdv" (into dk, dv)."""
+    acc_code = {False: 0, True: 3, "dq": 1, "dkdv": 2}.get(accumulate)
+    if acc_code is None:
+        raise ValueError("accumulate must be False, True, 'dq' or 'dkdv'")
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout"), (lse, "lse"), (delta, "delta"), (dq, "dq"),
                  (dk, "dk"), (dv, "dv")):
         _dev(t, n)
@@ -428,4 +432,4 @@ def usp_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.
     _check(lib().usp_attn_bwd(_code(q.dtype, "q"), B, H, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                               dout.data_ptr(), lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                               dv.data_ptr(), _code(dq.dtype, "dq"), float(scale), ctypes.byref(m),
-                              1 if accumulate else 0, _stream(q)))
+                              acc_code, _stream(q)))

@@ -517,7 +517,7 @@ UAA_EXPORT int usp_attn_bwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t
     if (!(scale > 0.f) || !isfinite(scale)) return fail(UAA_ERR_INVALID_ARG, "bwd: scale must be finite and > 0");
     if (mask != nullptr && (mask->kind < USP_MASK_FULL || mask->kind > USP_MASK_STRIPE))
         return fail(UAA_ERR_INVALID_ARG, "bwd: unknown mask kind %d", mask->kind);
-    if (accumulate != 0 && accumulate != 1) return fail(UAA_ERR_INVALID_ARG, "bwd: accumulate must be 0 or 1");
+    if (accumulate < 0 || accumulate > 3) return fail(UAA_ERR_INVALID_ARG, "bwd: accumulate must be in [0, 3]");
     if (D != 64 && D != 128) return fail(UAA_ERR_UNSUPPORTED, "bwd: D must be 64 or 128, got %lld", (long long)D);
     if (dtype == UAA_FP32) return fail(UAA_ERR_UNSUPPORTED, "bwd: fp32 input is not supported (bf16 only)");
     if ((double)B * (Sq > Sk ? Sq : Sk) * H * D > (double)kMaxElems) return fail(UAA_ERR_INVALID_ARG, "bwd: tensor too large");

@@ -448,7 +448,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void attn_bwd_dkdv_kernel(const 
             for (int e = 0; e < 4; ++e) r[e] = ((qh == 0 ? dv[db][4 * g4 + e] : dk[db][4 * g4 + e]) + o[e]) * mul;
             if (a.grad_bf16) {
                 bwd_u32x2* p = reinterpret_cast<bwd_u32x2*>(static_cast<unsigned short*>(out) + orow + f);
-                if (a.accumulate) {
+                if (a.accumulate & 2) {
                     const bwd_u32x2 old = *p;
                     r[0] += bwd_lo(old[0]);
                     r[1] += bwd_hi(old[0]);
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void attn_bwd_dkdv_kernel(const 
             } else {
                 bwd_f32x4* p = reinterpret_cast<bwd_f32x4*>(static_cast<float*>(out) + orow + f);
                 bwd_f32x4 w{r[0], r[1], r[2], r[3]};
-                if (a.accumulate) w += *p;
+                if (a.accumulate & 2) w += *p;
                 *p = w;
             }
         }
@@ -681,7 +681,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void attn_bwd_dq_kernel(const Bw
             for (int e = 0; e < 4; ++e) r[e] = acc[db][4 * g4 + e] * a.scale;
             if (a.grad_bf16) {
                 bwd_u32x2* p = reinterpret_cast<bwd_u32x2*>(static_cast<unsigned short*>(a.dq) + orow + f);
-                if (a.accumulate) {
+                if (a.accumulate & 1) {
                     const bwd_u32x2 old = *p;
                     r[0] += bwd_lo(old[0]);
                     r[1] += bwd_hi(old[0]);
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void attn_bwd_dq_kernel(const Bw
             } else {
                 bwd_f32x4* p = reinterpret_cast<bwd_f32x4*>(static_cast<float*>(a.dq) + orow + f);
                 bwd_f32x4 w{r[0], r[1], r[2], r[3]};
-                if (a.accumulate) w += *p;
+                if (a.accumulate & 1) w += *p;
                 *p = w;
             }
         }
@@ -753,10 +753,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, hipStream_t s)
 hipError_t launch_attn_bwd_bf16(int D, const BwdArgs& a, hipStream_t s)
 {
     if (a.B * a.H == 0 || (a.Sq == 0 && a.Sk == 0)) return hipSuccess;
-    if (a.Sq == 0) {
-        // no query: dK = dV = 0 (nothing to add when accumulating)
-        if (a.accumulate) return hipSuccess;
-    }
+    // no query: dK = dV = 0 (nothing to add when accumulating into them)
+    if (a.Sq == 0 && (a.accumulate & 2)) return hipSuccess;
     if (D == 128) return a.masked ? launch_bwd_d<128, true>(a, s) : launch_bwd_d<128, false>(a, s);
     return a.masked ? launch_bwd_d<64, true>(a, s) : launch_bwd_d<64, false>(a, s);
 }

@@ -151,7 +151,7 @@ struct BwdArgs {
     float scale;          // softmax scale as given
     float scale_log2;     // scale * log2(e)
     int32_t masked;       // 0: every key allowed; 1: kpos(j) <= qpos(i)
-    int32_t accumulate;   // 1: add into dq, dk, dv
+    int32_t accumulate;   // bit 0: add into dq; bit 1: add into dk and dv
     int32_t grad_bf16;    // gradients stored as bf16 (else fp32)
     int32_t n_tiles;      // work tiles per (batch, head) of the launched kernel, set by the launcher
     PosMap qmap, kmap;

@@ -275,7 +275,8 @@ def _bwd(dtype=0, B=1, H=1, Sq=4, Sk=4, D=128, q=FAKE, k=FAKE, v=FAKE, do=FAKE, 
     (dict(Sk=-1), -1, "negative"),
     (dict(scale=0.0), -1, "scale"),
     (dict(scale=float("nan")), -1, "scale"),
-    (dict(acc=2), -1, "accumulate"),
+    (dict(acc=4), -1, "accumulate"),
+    (dict(acc=-1), -1, "accumulate"),
     (dict(D=96), -2, "D must be"),
     (dict(dtype=1), -2, "fp32 input"),
     (dict(delta=0), -1, "NULL"),

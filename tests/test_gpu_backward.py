@@ -206,15 +206,17 @@ def test_ring_pass_gradient(kind):
         uaa.usp_attn_fwd_lse(tq, kr, vr, o, lse, scale, masks[r], accumulate=r > 0)
     delta = torch.empty_like(lse)
     uaa.usp_attn_bwd_delta(o, tdo, delta)
-    dq = torch.zeros((B, Sq, H, D), device="cuda", dtype=torch.float32)
+    dq = torch.empty((B, Sq, H, D), device="cuda", dtype=torch.float32)
     dks, dvs = [], []
     for r in range(R):
         kr = tk[:, offs[r]:offs[r + 1]].contiguous()
         vr = tv[:, offs[r]:offs[r + 1]].contiguous()
-        # accumulate applies to all three: the block's dk / dv start at zero
-        dk = torch.zeros(kr.shape, device="cuda", dtype=torch.float32)
-        dv = torch.zeros(kr.shape, device="cuda", dtype=torch.float32)
-        uaa.usp_attn_bwd(tq, kr, vr, tdo, lse, delta, dq, dk, dv, scale, masks[r], accumulate=True)
+        # block 0 writes dq, later blocks add into it; every block's dk / dv
+        # are written fresh (uninitialised buffers)
+        dk = torch.empty(kr.shape, device="cuda", dtype=torch.float32)
+        dv = torch.empty(kr.shape, device="cuda", dtype=torch.float32)
+        uaa.usp_attn_bwd(tq, kr, vr, tdo, lse, delta, dq, dk, dv, scale, masks[r],
+                         accumulate="dq" if r > 0 else False)
         dks.append(dk)
         dvs.append(dv)
     torch.cuda.synchronize()
@@ -242,9 +244,15 @@ def test_accumulate_adds_and_edges():
     uaa.usp_attn_bwd(q, k, v, do, lse, delta, *g1, scale)
     g2 = [torch.full_like(x, 0.5) for x in g1]
     uaa.usp_attn_bwd(q, k, v, do, lse, delta, *g2, scale, accumulate=True)
+    g3 = [torch.full_like(x, 0.5) for x in g1]
+    uaa.usp_attn_bwd(q, k, v, do, lse, delta, *g3, scale, accumulate="dq")
+    g4 = [torch.full_like(x, 0.5) for x in g1]
+    uaa.usp_attn_bwd(q, k, v, do, lse, delta, *g4, scale, accumulate="dkdv")
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a + 0.5, b)
+    assert torch.equal(g1[0] + 0.5, g3[0]) and torch.equal(g1[1], g3[1]) and torch.equal(g1[2], g3[2])
+    assert torch.equal(g1[0], g4[0]) and torch.equal(g1[1] + 0.5, g4[1]) and torch.equal(g1[2] + 0.5, g4[2])
     # no keys: dq = 0, dk / dv untouched (empty)
     k0 = torch.empty((B, 0, H, D), device="cuda", dtype=torch.bfloat16)
     e = torch.empty((B, 0, H, D), device="cuda", dtype=torch.float32)
