@@ -166,16 +166,26 @@ __device__ __forceinline__ int64_t bwd_below(int64_t base, int64_t stride, int64
 // ==========================================================================
 // dK / dV
 // ==========================================================================
+// The two waves of a SIMD (w and w + 4) own the same 32 keys in two roles:
+//   K side (w < 4): K rows as operands, dK accumulators; S = Q K^T, P
+//   V side (w >= 4): V rows as operands, dV accumulators; dP = dO V^T
+// and exchange P and dS through LDS.  Step i (query tile t_i), two phases:
+//   1. K: S_i, P_i (bf16) -> LDS           V: dP_i - delta
+//   2. V: dV += dO_i^T P_i, dS_i -> LDS     K: dK += Q_{i-1}^T dS_{i-1}
+// so in each phase one wave's vector work runs beside the other's matrix
+// work; dK trails by one step (Q tiles stay for three steps, dS is double
+// buffered).  Operand reads run four matrix instructions ahead.
 template <int D, bool MASKED>
 __global__ __launch_bounds__(64 * kBwdWaves, 2) void attn_bwd_dkdv_kernel(const BwdArgs a)
 {
     constexpr int ROWB = 2 * D, NKC = D / 16, NDB = D / 32, TB = kBwdT * ROWB;
     constexpr int CPT = TB / 1024 / kBwdWaves;        // copy instructions per wave per tensor per tile
-    constexpr int kOps = 2 * CPT;                     // ... for Q and dO (waves 0, 1 add lse / delta)
-    constexpr int STAGES = 6 * TB + 6 * 256;          // Q[3], dO[3], lse[3], delta[3]
-    constexpr int RED = 4 * 64 * NDB * 16 * 4;        // one accumulator set of the 4 key groups
-    constexpr int SMEM = STAGES > 2 * RED ? STAGES : 2 * RED;
+    constexpr int XB = 4 * 4 * 64 * 16;               // an exchange buffer: key group x chunk x lane x 16 bytes
+    // LDS: Q[3] | dO[2] | lse[2] (log2 units) | delta[2] | P | dS[2]
+    constexpr int OFF_Q = 0, OFF_O = 3 * TB, OFF_L = 5 * TB, OFF_D = OFF_L + 512, OFF_P = OFF_D + 512;
+    constexpr int OFF_S = OFF_P + XB, SMEM = OFF_S + 2 * XB;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
+    bwd_lds_u8* const L = (bwd_lds_u8*)smem;
 
     const uint32_t unit = xcd_logical(blockIdx.x, gridDim.x);
     const int64_t kt = unit % (uint32_t)a.n_tiles;
@@ -185,7 +195,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void attn_bwd_dkdv_kernel(const 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hg = lane >> 5;
-    const int kg = wave & 3, qh = wave >> 2;
+    const int kg = wave & 3, role = wave >> 2;       // role 0: K side, 1: V side
     const int64_t H = a.H, Sq = a.Sq, Sk = a.Sk;
     const uint32_t ld2 = (uint32_t)(H * D * 2);
     const int64_t k0 = kt * kBwdKeys;
@@ -193,23 +203,19 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void attn_bwd_dkdv_kernel(const 
     const int64_t j = kw0 + l32;                 // this lane's key
     const bool wave_keys = kw0 < Sk;
 
-    // K and V rows of this lane's key as the B operands of S = Q K^T and
-    // dP = dO V^T: features 16 kc + 8 hg .. +7 (zero past Sk)
-    bwd_bf16x8 kop[NKC], vop[NKC];
+    // this lane's K (K side) or V (V side) row as the B operand of S = Q K^T
+    // or dP = dO V^T: features 16 kc + 8 hg .. +7 (zero past Sk)
+    bwd_bf16x8 kvop[NKC];
     {
         const int64_t hoff = ((b * Sk) * H + hh) * D * 2;
         const uint32_t nrec = (uint32_t)((Sk - 1) * ld2 + D * 2);
-        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(static_cast<const unsigned char*>(a.k) + hoff), (short)0, nrec, 0x00020000);
-        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(static_cast<const unsigned char*>(a.v) + hoff), (short)0, nrec, 0x00020000);
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(static_cast<const unsigned char*>(role == 0 ? a.k : a.v) + hoff), (short)0, nrec, 0x00020000);
         const uint32_t roff = j < Sk ? (uint32_t)j * ld2 : nrec;
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-            const uint32_t off = roff + (uint32_t)((2 * kc + hg) * 16);
-            kop[kc] = __builtin_bit_cast(bwd_bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
-            vop[kc] = __builtin_bit_cast(bwd_bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
-        }
+        for (int kc = 0; kc < NKC; ++kc)
+            kvop[kc] = __builtin_bit_cast(
+                bwd_bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, roff + (uint32_t)((2 * kc + hg) * 16), 0, 0));
     }
 
     // Masking.  Query i may see key j iff qpos(i) >= kpos(j); positions grow
@@ -220,7 +226,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void attn_bwd_dkdv_kernel(const 
     // largest: some key / every key).
     const int32_t sq32 = (int32_t)Sq;
     int32_t segq = sq32;
-    int32_t qs0 = 0, qs1 = sq32;                         // this key
+    int32_t qs0 = 0, qs1 = sq32;
     int32_t g0 = 0, g1 = sq32, wa0 = 0, wa1 = sq32, wf0 = 0, wf1 = sq32;
     if (MASKED) {
         segq = (int32_t)(a.qmap.seg_len < Sq ? a.qmap.seg_len : Sq);
@@ -263,189 +269,210 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void attn_bwd_dkdv_kernel(const 
         return t < e1 ? t : n_qt;
     };
 
-    // ---- staging -----------------------------------------------------------
+    // ---- staging: tile of step i into Q stage qs and dO / lse / delta stage os
     const unsigned char* qbase = static_cast<const unsigned char*>(a.q) + ((b * Sq) * H + hh) * D * 2;
     const unsigned char* obase = static_cast<const unsigned char*>(a.dout) + ((b * Sq) * H + hh) * D * 2;
-    auto issue = [&](int t, int st) {
+    auto issue = [&](int t, int qs, int os) {
         const int64_t r0 = (int64_t)t * kBwdT;
         const int64_t nv = Sq - r0 < kBwdT ? Sq - r0 : kBwdT;
         const uint32_t nrec = (uint32_t)((nv - 1) * ld2 + D * 2);
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            bwd_copy<D>(qbase + r0 * ld2, nrec, ld2, (bwd_lds_u8*)smem + st * TB, wave, lane, i);
-            bwd_copy<D>(obase + r0 * ld2, nrec, ld2, (bwd_lds_u8*)smem + (3 + st) * TB, wave, lane, i);
+            bwd_copy<D>(qbase + r0 * ld2, nrec, ld2, L + OFF_Q + qs * TB, wave, lane, i);
+            bwd_copy<D>(obase + r0 * ld2, nrec, ld2, L + OFF_O + os * TB, wave, lane, i);
         }
         if (wave < 2) {
             const float* src = (wave == 0 ? a.lse : a.delta) + (b * Sq + r0) * H + hh;
             const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)src, (short)0, (uint32_t)((nv - 1) * H * 4 + 4), 0x00020000);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (bwd_lds_u8*)smem + 6 * TB + (3 * wave + st) * 256, 4,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, L + (wave == 0 ? OFF_L : OFF_D) + os * 256, 4,
                                                      (uint32_t)(lane * H * 4), 0, 0, 0);
         }
     };
+    // the lse of stage os to log2 units, +inf for a row with no key (P = 0);
+    // wave 0 copied it and runs this once its copy has landed
+    auto convert_lse = [&](int os) {
+        __attribute__((address_space(3))) float* p = (__attribute__((address_space(3))) float*)(L + OFF_L + os * 256) + lane;
+        const float x = *p;
+        *p = x == -INFINITY ? INFINITY : x * kBwdLog2e;
+    };
 
-    // per-lane LDS addressing: row reads of Q / dO (row 32 qh + l32) and
-    // the transposing reads
-    const int rrow = (32 * qh + l32) * ROWB, rx = (hg ^ bwd_swz<D>(l32)) << 4;
+    const int rrow = l32 * ROWB, rx = (hg ^ bwd_swz<D>(l32)) << 4;
     const BwdTr trs = bwd_tr_setup<D>(lane);
+    // exchange slot of chunk c of this key group
+    auto xslot = [&](int c) { return ((kg * 4 + c) * 64 + lane) * 16; };
 
-    bwd_f32x16 dk[NDB], dv[NDB];
+    bwd_f32x16 acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            dk[db][v] = 0.f;
-            dv[db][v] = 0.f;
-        }
+        for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
     const float c2 = a.scale_log2;
 
+    // S = Q K^T or dP = dO V^T for the tile's two 32-row blocks (rows
+    // 32 qb + l32), the blocks' instructions alternating so that two
+    // accumulations are in flight; operands read four instructions ahead
+    int rxl = rx;            // per-step copies, opaque to the compiler so that the
+    BwdTr trl = trs;         // derived LDS addresses are formed at use, not kept live
+    auto rows_product = [&](const bwd_lds_u8* tile, bwd_f32x16 (&r)[2]) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) r[qb][v] = 0.f;
+        constexpr int N = 2 * NKC;
+        auto rd = [&](int n) { return bwd_row<D>(tile, (n & 1) * 32 * ROWB + rrow, rxl, n >> 1); };
+        bwd_bf16x8 op[4];
+#pragma unroll
+        for (int n = 0; n < 4; ++n) op[n] = rd(n);
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            r[n & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[n & 3], kvop[n >> 1], r[n & 1], 0, 0, 0);
+            if (n + 4 < N) op[n & 3] = rd(n + 4);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // acc^T += tile^T X over the tile's 64 rows: chunk c of X in x[c]
+    auto tr_product = [&](const bwd_lds_u8* tile, const bwd_u32x4 (&x)[4]) {
+        constexpr int N = 4 * NDB;
+        auto rd = [&](int r) { return bwd_tr<D>(tile, 16 * (r / NDB) * ROWB, trl, r % NDB); };
+        bwd_bf16x8 op[2];
+        op[0] = rd(0);
+        op[1] = rd(1);
+#pragma unroll
+        for (int r = 0; r < N; ++r) {
+            acc[r % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[r & 1], __builtin_bit_cast(bwd_bf16x8, x[r / NDB]),
+                                                                  acc[r % NDB], 0, 0, 0);
+            if (r + 2 < N) op[r & 1] = rd(r + 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
     int t = next_live(0);
-    int t1 = t < n_qt ? next_live(t + 1) : n_qt;
-    int st = 0;
-    if (t < n_qt) {
-        issue(t, 0);
-        if (t1 < n_qt) issue(t1, 1);
-    }
-    if (t1 < n_qt)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | kOps);   // the operands and tile t landed
-    else
-        __builtin_amdgcn_s_waitcnt(0x0F70);
+    int qs = 0, os = 0, dsb = 0;           // stages of the current step
+    if (t < n_qt) issue(t, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);    // the operands and tile t landed
+    if (wave == 0 && t < n_qt) convert_lse(0);
     __syncthreads();
 
+    bool prev_any = false;                 // this wave's keys met the previous tile
+    int qprev = 0;                         // Q stage of the previous tile
+    bwd_f32x16 r2[2];                      // S (K side) / dP - delta (V side) of the tile's two blocks
     while (t < n_qt) {
-        const int t2 = t1 < n_qt ? next_live(t1 + 1) : n_qt;
-        if (t2 < n_qt) issue(t2, st == 0 ? 2 : st - 1);
+        rxl = rx;
+        trl = trs;
+        asm volatile("" : "+v"(rxl), "+v"(trl.base[0]), "+v"(trl.base[1]), "+v"(trl.x[0]), "+v"(trl.x[1]));
+        const int t1 = next_live(t + 1);
+        const int qn = qs == 2 ? 0 : qs + 1;
+        if (t1 < n_qt) issue(t1, qn, os ^ 1);
 
-        const int32_t i0 = t * kBwdT + 32 * qh;
-        const int32_t i1 = i0 + 32 < sq32 ? i0 + 32 : sq32;
-        bool any = wave_keys && i0 < sq32, per_elem = false;
+        const int32_t i0 = t * kBwdT, i1 = i0 + kBwdT < sq32 ? i0 + kBwdT : sq32;
+        bool any = wave_keys, per_elem = false;
         if (MASKED && any) {
             any = meets(i0, i1, wa0, wa1);
             per_elem = !inside(i0, i1, wf0, wf1);
         }
+        const bwd_lds_u8* Ol = L + OFF_O + os * TB;
+
+        // ---- phase 1: S = Q K^T (K side) or dP = dO V^T (V side) --------
         if (any) {
-            const bwd_lds_u8* Ql = (const bwd_lds_u8*)smem + st * TB;
-            const bwd_lds_u8* Ol = (const bwd_lds_u8*)smem + (3 + st) * TB;
-            const bwd_lds_u8* Ll = (const bwd_lds_u8*)smem + 6 * TB + st * 256;
-            const bwd_lds_u8* Dl = (const bwd_lds_u8*)smem + 6 * TB + (3 + st) * 256;
-            // S = Q K^T: lane = key, register v = query
-            // 32 qh + 8 (v / 4) + 4 hg + v % 4 of the tile
-            bwd_f32x16 sc;
+            rows_product(role == 0 ? L + OFF_Q + qs * TB : Ol, r2);
+            if (role == 0) {
+                // P in bf16, chunk c = 2 qb + g4 / 2, slots 4 hg + {0..3, 8..11}
+                const bwd_lds_u8* Ll = L + OFF_L + os * 256;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+                for (int qb = 0; qb < 2; ++qb) {
+                    bwd_u32x4 pw[2];
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc)
-                sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(Ql, rrow, rx, kc), kop[kc], sc, 0, 0, 0);
-            // P in bf16, in the operand order of the transposing reads:
-            // chunk c, slot s <-> query 16 c + 4 hg + {0..3, 8..11}[s]
-            bwd_u32x4 pw[2];
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int ql = 32 * qb + 8 * g4 + 4 * hg;   // 4 consecutive tile queries
+                        const bwd_f32x4 l2 = *(const bwd_lds_f32x4*)(Ll + ql * 4);
+                        float p[4];
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int ql = 32 * qh + 8 * g4 + 4 * hg;   // first of 4 consecutive tile queries
-                const bwd_f32x4 lv = *(const bwd_lds_f32x4*)(Ll + ql * 4);
-                float p[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float sv = sc[4 * g4 + e];
-                    if (MASKED && per_elem) {
-                        const int32_t iq = t * kBwdT + ql + e;
-                        const bool ok = iq < segq ? iq >= qs0 : iq >= qs1;
-                        if (!ok) sv = -INFINITY;
+                        for (int e = 0; e < 4; ++e) {
+                            float sv = r2[qb][4 * g4 + e];
+                            if (MASKED && per_elem) {
+                                const int32_t iq = i0 + ql + e;
+                                const bool ok = iq < segq ? iq >= qs0 : iq >= qs1;
+                                if (!ok) sv = -INFINITY;
+                            }
+                            p[e] = __builtin_amdgcn_exp2f(fmaf(sv, c2, -l2[e]));
+                        }
+                        pw[g4 >> 1][2 * (g4 & 1)] = bwd_pack(p[0], p[1]);
+                        pw[g4 >> 1][2 * (g4 & 1) + 1] = bwd_pack(p[2], p[3]);
                     }
-                    // a row with no key at all (lse = -inf) has P = 0
-                    const float l2 = lv[e] == -INFINITY ? INFINITY : lv[e] * kBwdLog2e;
-                    p[e] = __builtin_amdgcn_exp2f(fmaf(sv, c2, -l2));
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) *(bwd_lds_u32x4*)(L + OFF_P + xslot(2 * qb + h)) = pw[h];
                 }
-                const int c = g4 >> 1, h2 = 2 * (g4 & 1);
-                pw[c][h2] = bwd_pack(p[0], p[1]);
-                pw[c][h2 + 1] = bwd_pack(p[2], p[3]);
+            } else {
+                const bwd_lds_u8* Dl = L + OFF_D + os * 256;
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const bwd_f32x4 dl = *(const bwd_lds_f32x4*)(Dl + (32 * qb + 8 * g4 + 4 * hg) * 4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) r2[qb][4 * g4 + e] -= dl[e];
+                    }
             }
-            // dV^T += dO^T P: lane = key, register v = feature
-            // 32 db + 8 (v / 4) + 4 hg + v % 4
+        }
+        bwd_barrier();
+
+        // ---- phase 2: dV^T += dO^T P (V side, this tile) or dK^T += Q^T dS
+        // (K side, previous tile), then the V side's dS -------------------
+        if (role == 0 ? prev_any : any) {
+            bwd_u32x4 x[4];
+            const int xo = role == 0 ? OFF_S + (dsb ^ 1) * XB : OFF_P;
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const bwd_bf16x8 pb = __builtin_bit_cast(bwd_bf16x8, pw[c]);
+            for (int c = 0; c < 4; ++c) x[c] = *(const bwd_lds_u32x4*)(L + xo + xslot(c));
+            tr_product(role == 0 ? L + OFF_Q + qprev * TB : Ol, x);
+            if (role == 1) {
+                // dS = P (dP - delta), chunk c = 2 qb + h: dword e holds
+                // rows 8 h + 2 e, 8 h + 2 e + 1 of block qb
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(Ol, (32 * qh + 16 * c) * ROWB, trs, db),
-                                                                     pb, dv[db], 0, 0, 0);
-            }
-            // dP = dO V^T (same layout as S), dS = P (dP - delta) with the
-            // bf16 P of the dV product
-            bwd_f32x16 dp;
+                for (int c = 0; c < 4; ++c) {
+                    const int qb = c >> 1, h = c & 1;
+                    bwd_u32x4 sw;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) dp[v] = 0.f;
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc)
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(Ol, rrow, rx, kc), vop[kc], dp, 0, 0, 0);
-            bwd_u32x4 sw[2];
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int ql = 32 * qh + 8 * g4 + 4 * hg;
-                const bwd_f32x4 dl = *(const bwd_lds_f32x4*)(Dl + ql * 4);
-                const int c = g4 >> 1, h2 = 2 * (g4 & 1);
-                const unsigned int p01 = pw[c][h2], p23 = pw[c][h2 + 1];
-                sw[c][h2] = bwd_pack(bwd_lo(p01) * (dp[4 * g4] - dl[0]), bwd_hi(p01) * (dp[4 * g4 + 1] - dl[1]));
-                sw[c][h2 + 1] = bwd_pack(bwd_lo(p23) * (dp[4 * g4 + 2] - dl[2]), bwd_hi(p23) * (dp[4 * g4 + 3] - dl[3]));
-            }
-            // dK^T += Q^T dS (scaled at the end)
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const bwd_bf16x8 sb = __builtin_bit_cast(bwd_bf16x8, sw[c]);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(Ql, (32 * qh + 16 * c) * ROWB, trs, db),
-                                                                     sb, dk[db], 0, 0, 0);
+                    for (int e = 0; e < 4; ++e)
+                        sw[e] = bwd_pack(bwd_lo(x[c][e]) * r2[qb][8 * h + 2 * e],
+                                         bwd_hi(x[c][e]) * r2[qb][8 * h + 2 * e + 1]);
+                    *(bwd_lds_u32x4*)(L + OFF_S + dsb * XB + xslot(c)) = sw;
+                }
             }
         }
 
-        // the copies of tile t1 must have landed; those of t2 may still run
-        if (t2 < n_qt)
-            __builtin_amdgcn_s_waitcnt(0x0F70 | kOps);
-        else
-            __builtin_amdgcn_s_waitcnt(0x0F70);
+        // the copies of tile t1 landed; wave 0 converts its lse
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        if (wave == 0 && t1 < n_qt) convert_lse(os ^ 1);
         bwd_barrier();
-        st = st == 2 ? 0 : st + 1;
+        prev_any = any;
+        qprev = qs;
+        qs = qn;
+        os ^= 1;
+        dsb ^= 1;
         t = t1;
-        t1 = t2;
+    }
+    // the last tile's dK
+    if (role == 0 && prev_any) {
+        bwd_u32x4 x[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[c] = *(const bwd_lds_u32x4*)(L + OFF_S + (dsb ^ 1) * XB + xslot(c));
+        tr_product(L + OFF_Q + qprev * TB, x);
     }
 
-    // ---- epilogue: sum the two query halves, write dK (scaled) and dV -----
-    // Waves of half 1 hand their dV to half 0 and half 0 its dK to half 1,
-    // through LDS laid out [key group][quad][lane] (16 bytes per lane).
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    bwd_barrier();
-    bwd_lds_u8* const R0 = (bwd_lds_u8*)smem;         // dV of half 1
-    bwd_lds_u8* const R1 = (bwd_lds_u8*)smem + RED;   // dK of half 0
-    auto slot = [&](int db, int g4) { return ((kg * NDB * 4 + db * 4 + g4) * 64 + lane) * 16; };
-    {
-        bwd_lds_u8* W = qh == 1 ? R0 : R1;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                bwd_f32x4 w;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = qh == 1 ? dv[db][4 * g4 + e] : dk[db][4 * g4 + e];
-                *(bwd_lds_f32x4*)(W + slot(db, g4)) = w;
-            }
-    }
-    bwd_barrier();
+    // ---- epilogue: the K side writes dK (scaled), the V side dV ----------
     if (j >= Sk) return;
-    // half 0 writes dV, half 1 writes dK
-    const bwd_lds_u8* Rd = qh == 0 ? R0 : R1;
-    const float mul = qh == 0 ? 1.f : a.scale;
-    void* out = qh == 0 ? a.dv : a.dk;
+    const float mul = role == 0 ? a.scale : 1.f;
+    void* out = role == 0 ? a.dk : a.dv;
     const int64_t orow = ((b * Sk + j) * H + hh) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-            const bwd_f32x4 o = *(const bwd_lds_f32x4*)(Rd + slot(db, g4));
             const int f = 32 * db + 8 * g4 + 4 * hg;
             float r[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) r[e] = ((qh == 0 ? dv[db][4 * g4 + e] : dk[db][4 * g4 + e]) + o[e]) * mul;
+            for (int e = 0; e < 4; ++e) r[e] = acc[db][4 * g4 + e] * mul;
             if (a.grad_bf16) {
                 bwd_u32x2* p = reinterpret_cast<bwd_u32x2*>(static_cast<unsigned short*>(out) + orow + f);
                 if (a.accumulate & 2) {
@@ -606,56 +633,69 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void attn_bwd_dq_kernel(const Bw
         if (any) {
             const bwd_lds_u8* Kl = (const bwd_lds_u8*)smem + st * TB;
             const bwd_lds_u8* Vl = (const bwd_lds_u8*)smem + (3 + st) * TB;
-            // S^T = K Q^T, dP^T = V dO^T: lane = query, register v of block
-            // jb = key 32 jb + 8 (v / 4) + 4 hg + v % 4 of the tile
-            bwd_f32x16 s[2], dp[2];
+            // One 32-key block at a time: S^T = K Q^T and dP^T = V dO^T
+            // (lane = query, register v = key 32 jb + 8 (v / 4) + 4 hg + v % 4),
+            // dS^T, then dQ^T += K^T dS^T (lane = query, register v = feature
+            // 32 db + 8 (v / 4) + 4 hg + v % 4).  The LDS operands are read
+            // four matrix instructions ahead (two for the transposing reads),
+            // and scheduling barriers keep that order.
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
+            for (int jb = 0; jb < 2; ++jb) {
+                const int rb = jb * 32 * ROWB + rrow;
+                constexpr int NS = 2 * NKC;                 // S and dP instructions, alternating
+                auto rd = [&](int r) { return bwd_row<D>((r & 1) ? Vl : Kl, rb, rx, r >> 1); };
+                bwd_f32x16 sc, dp;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    s[jb][v] = 0.f;
-                    dp[jb][v] = 0.f;
+                    sc[v] = 0.f;
+                    dp[v] = 0.f;
                 }
+                bwd_bf16x8 op[4];
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc)
+                for (int r = 0; r < 4; ++r) op[r] = rd(r);
 #pragma unroll
-                for (int jb = 0; jb < 2; ++jb) {
-                    const int rb = jb * 32 * ROWB + rrow;
-                    s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(Kl, rb, rx, kc), qop[kc], s[jb], 0, 0, 0);
-                    dp[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(Vl, rb, rx, kc), dop[kc], dp[jb], 0, 0, 0);
+                for (int r = 0; r < NS; ++r) {
+                    if (r & 1)
+                        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[r & 3], dop[r >> 1], dp, 0, 0, 0);
+                    else
+                        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[r & 3], qop[r >> 1], sc, 0, 0, 0);
+                    if (r + 4 < NS) op[r & 3] = rd(r + 4);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-            // dS^T in bf16, 16-key chunk c = slots 4 hg + {0..3, 8..11}
-            bwd_u32x4 sw[4];
+                // dS^T in bf16: chunk c = 2 jb + h of the tile, slots 4 hg + {0..3, 8..11}
+                bwd_u32x4 sw[2];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int jb = c >> 1, v0 = 8 * (c & 1);
+                for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float d[2];
+                    for (int e = 0; e < 4; ++e) {
+                        float d[2];
 #pragma unroll
-                    for (int x = 0; x < 2; ++x) {
-                        const int v = v0 + 2 * e + x;
-                        float sv = s[jb][v];
-                        if (per_elem) {
-                            const int32_t jj = j0 + 32 * jb + 8 * (v >> 2) + 4 * hg + (v & 3);
-                            const bool ok = jj < segk ? jj < lim0 : jj < lim1;
-                            if (!ok) sv = -INFINITY;
+                        for (int x = 0; x < 2; ++x) {
+                            const int v = 8 * h + 2 * e + x;
+                            float sv = sc[v];
+                            if (per_elem) {
+                                const int32_t jj = j0 + 32 * jb + 8 * (v >> 2) + 4 * hg + (v & 3);
+                                const bool ok = jj < segk ? jj < lim0 : jj < lim1;
+                                if (!ok) sv = -INFINITY;
+                            }
+                            const float p = __builtin_amdgcn_exp2f(fmaf(sv, c2, -l2));
+                            d[x] = p * (dp[v] - dlt);
                         }
-                        const float p = __builtin_amdgcn_exp2f(fmaf(sv, c2, -l2));
-                        d[x] = p * (dp[jb][v] - dlt);
+                        sw[h][e] = bwd_pack(d[0], d[1]);
                     }
-                    sw[c][e] = bwd_pack(d[0], d[1]);
-                }
-            }
-            // dQ^T += K^T dS^T: lane = query, register v = feature
-            // 32 db + 8 (v / 4) + 4 hg + v % 4
+                constexpr int NQ = 2 * NDB;                 // dQ instructions of the block
+                auto tr = [&](int r) { return bwd_tr<D>(Kl, (32 * jb + 16 * (r / NDB)) * ROWB, trs, r % NDB); };
+                bwd_bf16x8 ta[2];
+                ta[0] = tr(0);
+                ta[1] = tr(1);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const bwd_bf16x8 sb = __builtin_bit_cast(bwd_bf16x8, sw[c]);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(Kl, 16 * c * ROWB, trs, db), sb,
+                for (int r = 0; r < NQ; ++r) {
+                    const int db = r % NDB;
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[r & 1], __builtin_bit_cast(bwd_bf16x8, sw[r / NDB]),
                                                                       acc[db], 0, 0, 0);
+                    if (r + 2 < NQ) ta[r & 1] = tr(r + 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
 
