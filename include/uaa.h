@@ -371,9 +371,9 @@ int usp_attn_bwd_delta(int dtype, int64_t B, int64_t S, int64_t H, int64_t D, co
  * accumulate: bit 0 set -- dq is added to what dq holds, else written;
  * bit 1 set -- dk and dv likewise (a Ring backward adds every block into dq,
  * and each block's dk, dv into the buffers that travel with that block).
- * Sums run in fp32 and are rounded once when grad_dtype is bf16.  dtype: UAA_BF16
- * (bf16 matrix-core products, fp32 accumulation; UAA_FP32 input gives
- * UAA_ERR_UNSUPPORTED).  grad_dtype: UAA_BF16 or UAA_FP32.  D: 64 or 128.
+ * Sums run in fp32 and are rounded once when grad_dtype is bf16.  dtype:
+ * UAA_BF16 (bf16 matrix-core products, fp32 accumulation) or UAA_FP32 (fp32
+ * throughout).  grad_dtype: UAA_BF16 or UAA_FP32.  D: 64 or 128.
  * scale: finite, > 0.  mask as in usp_attn_fwd_lse.  q, k, v, dout, dq, dk,
  * dv 16-byte aligned; lse, delta 4-byte aligned.  Outputs must not overlap
  * inputs or each other.  B = 0, H = 0 or Sq = Sk = 0: no work; Sq = 0 gives

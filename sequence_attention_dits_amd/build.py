@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libuaa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "permute.hip", "merge.hip", "attn_fp32.hip", "attn_bf16.hip", "attn_bwd.hip"]
+SOURCES = ["abi.hip", "permute.hip", "merge.hip", "attn_fp32.hip", "attn_bf16.hip", "attn_bwd.hip", "attn_bwd_fp32.hip"]
 HEADERS = ["internal.h", "attn_common.h"]
 
 CFLAGS = [

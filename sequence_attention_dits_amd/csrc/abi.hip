@@ -519,7 +519,6 @@ UAA_EXPORT int usp_attn_bwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t
         return fail(UAA_ERR_INVALID_ARG, "bwd: unknown mask kind %d", mask->kind);
     if (accumulate < 0 || accumulate > 3) return fail(UAA_ERR_INVALID_ARG, "bwd: accumulate must be in [0, 3]");
     if (D != 64 && D != 128) return fail(UAA_ERR_UNSUPPORTED, "bwd: D must be 64 or 128, got %lld", (long long)D);
-    if (dtype == UAA_FP32) return fail(UAA_ERR_UNSUPPORTED, "bwd: fp32 input is not supported (bf16 only)");
     if ((double)B * (Sq > Sk ? Sq : Sk) * H * D > (double)kMaxElems) return fail(UAA_ERR_INVALID_ARG, "bwd: tensor too large");
     if (B == 0 || H == 0 || (Sq == 0 && Sk == 0)) return UAA_OK;
     if (Sq > 0 && (q == nullptr || dout == nullptr || lse == nullptr || delta == nullptr || dq == nullptr))
@@ -533,7 +532,7 @@ UAA_EXPORT int usp_attn_bwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t
     // 32-bit buffer offsets within one (batch) slab, with room for a tile past the end
     if ((double)((Sq > Sk ? Sq : Sk) + 256) * H * D * 2 >= 4294967296.0)
         return fail(UAA_ERR_UNSUPPORTED, "bwd: one batch of q or k/v must stay below 4 GiB");
-    if (((Sk + 127) / 128) * H * B >= kMaxIdx32 || ((Sq + 255) / 256) * H * B >= kMaxIdx32)
+    if (((Sk + 63) / 64) * H * B >= kMaxIdx32 || ((Sq + 63) / 64) * H * B >= kMaxIdx32)
         return fail(UAA_ERR_INVALID_ARG, "bwd: grid too large");
 
     uaa::BwdArgs a{};
@@ -562,5 +561,7 @@ UAA_EXPORT int usp_attn_bwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t
         rc = side_map(*mask, false, Sk, a.kmap);
         if (rc != UAA_OK) return rc;
     }
-    return hip_status(uaa::launch_attn_bwd_bf16((int)D, a, static_cast<hipStream_t>(stream)), "bwd launch");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == UAA_BF16) return hip_status(uaa::launch_attn_bwd_bf16((int)D, a, s), "bwd launch");
+    return hip_status(uaa::launch_attn_bwd_fp32((int)D, a, s), "bwd launch");
 }

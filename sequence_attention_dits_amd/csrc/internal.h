@@ -165,8 +165,9 @@ struct DeltaArgs {
     int64_t rows;         // B * S * H
 };
 
-// dK/dV kernel then dQ kernel (bf16 inputs)
+// dK/dV kernel then dQ kernel (bf16 inputs; fp32 inputs)
 hipError_t launch_attn_bwd_bf16(int D, const BwdArgs& a, hipStream_t s);
+hipError_t launch_attn_bwd_fp32(int D, const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_delta(int dtype, int D, const DeltaArgs& a, hipStream_t s);
 
 }  // namespace uaa

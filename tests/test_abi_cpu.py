@@ -278,7 +278,6 @@ def _bwd(dtype=0, B=1, H=1, Sq=4, Sk=4, D=128, q=FAKE, k=FAKE, v=FAKE, do=FAKE, 
     (dict(acc=4), -1, "accumulate"),
     (dict(acc=-1), -1, "accumulate"),
     (dict(D=96), -2, "D must be"),
-    (dict(dtype=1), -2, "fp32 input"),
     (dict(delta=0), -1, "NULL"),
     (dict(dv=0), -1, "NULL"),
     (dict(dq=FAKE + 8), -1, "16-byte"),

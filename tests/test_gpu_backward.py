@@ -300,3 +300,81 @@ def test_flux_block_full_size_sampled_heads():
         bnd = _bounds(q[:, :, sl], k[:, :, sl], v[:, :, sl], do[:, :, sl], scale, None, None, None)
         for nm, g, r, bd in zip(("dq", "dk", "dv"), got, ref, bnd):
             _check("%s head %d" % (nm, h), g[:, :, sl], r, bd)
+
+
+FP32 = [
+    ("full_ragged_d64", 1, 257, 129, 2, 64, "full", {}),
+    ("causal_dead_rows", 1, 100, 150, 2, 128, "causal", dict(q_off=0, k_off=40)),
+    ("zigzag_mixed", 2, 96, 96, 1, 64, "zigzag", dict(chunk=48, q_chunks=[1, 2], k_chunks=[0, 3])),
+]
+
+
+def _fp32_inputs(cfg, B, Sq, Sk, H, D):
+    vals = [synth.tensor(cfg, t, shp, "fp32")[1] for t, shp in
+            ((0, (B, Sq, H, D)), (1, (B, Sk, H, D)), (2, (B, Sk, H, D)), (5, (B, Sq, H, D)))]
+    return vals
+
+
+def _check_fp32(name, got, ref, bound):
+    assert np.isfinite(got).all(), name + ": non-finite gradient"
+    err = np.abs(got - ref)
+    lim = 1e-5 * bound + 1e-6 * (np.max(np.abs(ref)) if ref.size else 0.0)
+    worst = float(np.max(err / np.maximum(lim, 1e-30))) if err.size else 0.0
+    say("  %s: max err %.3e, worst err/limit %.3f" % (name, float(err.max()) if err.size else 0.0, worst))
+    assert (err <= lim).all(), "%s: fp32 error above the bound (worst ratio %.3f)" % (name, worst)
+
+
+@pytest.mark.parametrize("case", FP32, ids=[c[0] for c in FP32])
+def test_fp32_against_oracle(case):
+    """fp32 inputs: the full-precision kernels, within 1e-5 of the sum of
+    |terms| of each gradient element (plus 1e-6 of its largest value)."""
+    name, B, Sq, Sk, H, D, kind, kw = case
+    say("backward fp32 %s" % name)
+    q, k, v, do = _fp32_inputs(780 + FP32.index(case), B, Sq, Sk, H, D)
+    scale = 1.0 / math.sqrt(D)
+    mask, qpos, kpos = _masks(kind, Sq, Sk, **kw)
+    tq, tk, tv, tdo = (dev(x, "fp32") for x in (q, k, v, do))
+    o = torch.empty_like(tq)
+    lse = torch.empty((B, Sq, H), device="cuda", dtype=torch.float32)
+    uaa.usp_attn_fwd_lse(tq, tk, tv, o, lse, scale, mask)
+    delta = torch.empty_like(lse)
+    uaa.usp_attn_bwd_delta(o, tdo, delta)
+    dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+    uaa.usp_attn_bwd(tq, tk, tv, tdo, lse, delta, dq, dk, dv, scale, mask)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd(q, k, v, do, scale, qpos, kpos)
+    bnd = _bounds(q, k, v, do, scale, qpos, kpos, None)
+    for nm, g, r, bd in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, bnd):
+        _check_fp32(nm, host_f64(g), r, bd)
+
+
+def test_fp32_ring_share_shape():
+    """The small fp32 share (257 tokens, 2 heads, D = 64) as a two-block
+    Ring pass: forward accumulated over key blocks of 129 and 128 tokens,
+    backward per block against the final (o, lse)."""
+    B, S, H, D = 1, 257, 2, 64
+    say("backward fp32 ring share")
+    q, k, v, do = _fp32_inputs(790, B, S, S, H, D)
+    scale = 1.0 / math.sqrt(D)
+    tq, tk, tv, tdo = (dev(x, "fp32") for x in (q, k, v, do))
+    o = torch.empty_like(tq)
+    lse = torch.empty((B, S, H), device="cuda", dtype=torch.float32)
+    blocks = [(0, 129), (129, 257)]
+    for n, (a, b) in enumerate(blocks):
+        uaa.usp_attn_fwd_lse(tq, tk[:, a:b].contiguous(), tv[:, a:b].contiguous(), o, lse, scale, accumulate=n > 0)
+    delta = torch.empty_like(lse)
+    uaa.usp_attn_bwd_delta(o, tdo, delta)
+    dq = torch.empty_like(tq)
+    dks, dvs = [], []
+    for n, (a, b) in enumerate(blocks):
+        kb, vb = tk[:, a:b].contiguous(), tv[:, a:b].contiguous()
+        dk, dv = torch.empty_like(kb), torch.empty_like(vb)
+        uaa.usp_attn_bwd(tq, kb, vb, tdo, lse, delta, dq, dk, dv, scale, accumulate="dq" if n else False)
+        dks.append(dk)
+        dvs.append(dv)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd(q, k, v, do, scale)
+    bnd = _bounds(q, k, v, do, scale, None, None, None)
+    _check_fp32("dq", host_f64(dq), ref[0], bnd[0])
+    _check_fp32("dk", np.concatenate([host_f64(x) for x in dks], axis=1), ref[1], bnd[1])
+    _check_fp32("dv", np.concatenate([host_f64(x) for x in dvs], axis=1), ref[2], bnd[2])
