@@ -13,13 +13,14 @@
 // gradients summed over the blocks are the gradient of the merged result.
 //
 // How (CDNA4, wave64), two kernels with no atomics:
-//  * dK/dV kernel: a workgroup owns 128 keys of one (batch, head) and keeps
-//    their K and V rows in registers as matrix operands; 8 wavefronts, the
-//    key group of 32 being wave % 4 and the half of each 64-query tile
-//    wave / 4, so both waves of a SIMD work on the same keys and their dK,
-//    dV accumulators are summed once through LDS at the end.  Query tiles of
-//    Q, dO, lse and delta stream through three LDS stages by buffer loads
-//    that write LDS directly, issued two tiles ahead.  Per tile:
+//  * dK/dV kernel: a workgroup owns 128 keys of one (batch, head); 8
+//    wavefronts, the key group of 32 being wave % 4.  The two waves of a
+//    SIMD split the work by role, not by query: wave / 4 = 0 keeps the
+//    group's K rows as matrix operands and accumulates dK, wave / 4 = 1
+//    keeps the V rows and accumulates dV, and they hand P and dS to each
+//    other through LDS, so no accumulator is ever summed across waves.
+//    Query tiles of Q, dO, lse and delta stream through LDS stages by buffer
+//    loads that write LDS directly, issued two tiles ahead.  Per tile:
 //      S = Q K^T, dP = dO V^T           (16-byte row reads of Q, dO)
 //      dV^T += dO^T P, dK^T += Q^T dS   (transposing LDS reads of dO, Q)
 //  * dQ kernel: a workgroup owns 256 query rows (32 per wave) with Q and dO
