@@ -692,7 +692,7 @@ def main():
         return
     if args.gpus != 1:
         print("bench.py measures one rank's share on one GPU; --gpus %d is not supported "
-              "(this build has no multi-GPU path)" % args.gpus, file=sys.stderr)
+              "(the library has no collective or multi-GPU path)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
