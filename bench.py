@@ -105,6 +105,9 @@ def parse():
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="print the traffic summary of two rocprofv3 --pmc runs of --pmc-probe")
     p.add_argument("--stats-summary", metavar="DIR", help="print the summary of a rocprofv3 --stats run")
+    p.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                   help="print the attention kernel's shader counters from rocprofv3 --pmc runs of --pmc-probe "
+                        "(MFMA busy cycles against the active cycles, instruction mix, waits)")
     return p.parse_args()
 
 
@@ -667,6 +670,39 @@ def measured_traffic():
         return None
 
 
+SIMDS = 256 * 4   # MI355X: 256 compute units of 4 SIMDs, in 8 XCDs
+
+
+def counter_summary(dirs):
+    """Means per attention dispatch of every counter in the given rocprofv3
+    --pmc runs, and the matrix-core utilisation they imply: busy cycles of
+    the matrix units over (active cycles of one XCD x all SIMDs), where
+    GRBM_GUI_ACTIVE is summed over the 8 XCDs."""
+    import collections
+    vals = collections.defaultdict(list)
+    for d in dirs:
+        for counter in ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+                        "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES",
+                        "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT"):
+            for k, vs in _pmc_values(d, counter).items():
+                if "attn_bf16_kernel" in k:
+                    vals[counter].extend(vs)
+    if not vals:
+        raise SystemExit("no attention dispatch in " + " ".join(dirs))
+    mean = {k: sum(v) / len(v) for k, v in vals.items()}
+    print("%-28s %10s %16s" % ("counter", "dispatches", "mean per dispatch"))
+    for k in sorted(mean):
+        print("%-28s %10d %16.4g" % (k, len(vals[k]), mean[k]))
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and "GRBM_GUI_ACTIVE" in mean:
+        cyc = mean["GRBM_GUI_ACTIVE"] / 8
+        print("active cycles per XCD: %.4g" % cyc)
+        print("matrix-core busy / (active cycles x %d SIMDs): %.3f" % (SIMDS, mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * SIMDS)))
+        if "SQ_INSTS_MFMA" in mean:
+            print("busy cycles per matrix instruction: %.2f" % (mean["SQ_VALU_MFMA_BUSY_CYCLES"] / mean["SQ_INSTS_MFMA"]))
+    if "SQ_WAIT_INST_ANY" in mean and "SQ_WAVE_CYCLES" in mean:
+        print("wave time waiting on a dependency: %.3f" % (mean["SQ_WAIT_INST_ANY"] / mean["SQ_WAVE_CYCLES"]))
+
+
 def stats_summary(d):
     """Kernel table of a rocprofv3 --kernel-trace --stats run (its *_kernel_stats.csv)."""
     import csv
@@ -689,6 +725,9 @@ def main():
         return
     if args.stats_summary:
         stats_summary(args.stats_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     if args.gpus != 1:
         print("bench.py measures one rank's share on one GPU; --gpus %d is not supported "
