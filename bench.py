@@ -23,8 +23,10 @@ Input sets rotate over more than 4x the 256 MB Infinity Cache so every
 step starts from cold HBM.  Each step is captured once per input set as a
 HIP graph and replayed (a replay is checked bit for bit against the eager
 step first).  Per-kernel times come from HIP events around K back-to-back
-launches of each kernel of the step (same arguments, rotating inputs), on
-the stream the kernels run on.
+launches of each kernel of the step, on the stream the kernels run on; the
+HBM-bound ones (permute, merge, inverse gather) read and write buffers of
+their own per rotating set, so that neither side stays in the Infinity
+Cache.
 
 Other workloads (--workload): flux1008 (the same step on the non-divisible
 4481-token UAA share), and two Ring-only shares whose step is one attention
@@ -164,6 +166,29 @@ class Share:
         self.o_tok = torch.empty(B, S0, H, D, device="cuda", dtype=bf)
         self.l_tok = torch.empty(B, S0, H, 1, device="cuda", dtype=torch.float32)
 
+    def timing_bufs(self, s):
+        """Buffers of set s for the per-kernel timing of the HBM-bound
+        launches (permute, merge, inverse gather): inputs and outputs both
+        rotate with the set, so that those timings read and write HBM and not
+        the Infinity Cache.  Allocated on first use; partials hold finite
+        values."""
+        if not hasattr(self, "_tbufs"):
+            self._tbufs = {}
+        if s not in self._tbufs:
+            torch, bf = self.torch, self.torch.bfloat16
+            B, S, Hr, D, H = self.B, self.S, self.Hr, self.D, self.H
+            S0 = self.seq_off[1]
+            self._tbufs[s] = {
+                "qh": {n: torch.empty(B, S, Hr, D, device="cuda", dtype=bf) for n in "qkv"},
+                "o_part": [torch.randn(B, S, Hr, D, device="cuda").to(bf) for _ in self.ring],
+                "l_part": [8 + torch.randn(B, S, Hr, device="cuda") for _ in self.ring],
+                "o": torch.randn(B, S, Hr, D, device="cuda").to(bf),
+                "lse": 8 + torch.randn(B, S, Hr, device="cuda"),
+                "o_tok": torch.empty(B, S0, H, D, device="cuda", dtype=bf),
+                "l_tok": torch.empty(B, S0, H, 1, device="cuda", dtype=torch.float32),
+            }
+        return self._tbufs[s]
+
     # algorithmic work per launch
     def attn_flops(self, chunk):
         a, b = self.ring[chunk]
@@ -183,16 +208,24 @@ class Share:
     def head2seq_bytes(self):
         return 2.0 * 2 * self.B * self.seq_off[1] * self.H * self.D
 
-    def launch_one(self, name, s):
+    def launch_one(self, name, s, timing=False):
         """Enqueue the launch(es) of one kind that a step makes on set s;
-        returns how many launches were enqueued."""
+        returns how many launches were enqueued.  With timing, the HBM-bound
+        launches use the set's own buffers (timing_bufs) instead of the
+        step's shared intermediates."""
         uaa = self.uaa
         d = self.sets[s]
+        t = self.timing_bufs(s) if timing else None
+        qh = t["qh"] if timing else self.qh
+        o_part, l_part = (t["o_part"], t["l_part"]) if timing else (self.o_part, self.l_part)
+        o, lse = (t["o"], t["lse"]) if timing else (self.o, self.lse)
+        o_tok, l_tok = (t["o_tok"], t["l_tok"]) if timing else (self.o_tok, self.l_tok)
         if name == "permute":
-            uaa.uaa_seq2head_permute(uaa.UAA_SEQ2HEAD, 0, d["q"], self.qh["q"], self.seq_off, self.head_off)
+            uaa.uaa_seq2head_permute(uaa.UAA_SEQ2HEAD, 0, d["q"], qh["q"], self.seq_off, self.head_off)
             return 1
         if name == "permute_qkv":
-            self._seq2head_qkv(s)
+            uaa.uaa_seq2head_permute_multi(uaa.UAA_SEQ2HEAD, 0, [d[n] for n in "qkv"], [qh[n] for n in "qkv"],
+                                           self.seq_off, self.head_off)
             return 1
         if name == "attn":
             for c in range(len(self.kc)):
@@ -203,21 +236,19 @@ class Share:
                 self.attn_chunk(s, c, self.ws[0], acc=True)
             return len(self.kc) - 1
         if name == "merge":
-            uaa.usp_lse_merge(self.o_part, self.l_part, self.o, self.lse)
+            uaa.usp_lse_merge(o_part, l_part, o, lse)
             return 1
         if name == "head2seq":
-            uaa.uaa_seq2head_permute(uaa.UAA_HEAD2SEQ, 0, [self.o, d["o_other"]], self.o_tok, self.seq_off,
-                                     self.head_off)
+            uaa.uaa_seq2head_permute(uaa.UAA_HEAD2SEQ, 0, [o, d["o_other"]], o_tok, self.seq_off, self.head_off)
             return 1
         if name == "head2seq_o_lse":
             # O and its LSE back to the token layout in one launch
-            uaa.uaa_seq2head_permute_multi(uaa.UAA_HEAD2SEQ, 0, [[self.o, d["o_other"]],
-                                                                 [self.lse.unsqueeze(-1), d["l_other"]]],
-                                           [self.o_tok, self.l_tok], self.seq_off, self.head_off)
+            uaa.uaa_seq2head_permute_multi(uaa.UAA_HEAD2SEQ, 0, [[o, d["o_other"]], [lse.unsqueeze(-1), d["l_other"]]],
+                                           [o_tok, l_tok], self.seq_off, self.head_off)
             return 1
         if name == "head2seq_lse":
-            uaa.uaa_seq2head_permute(uaa.UAA_HEAD2SEQ, 0, [self.lse.unsqueeze(-1), d["l_other"]], self.l_tok,
-                                     self.seq_off, self.head_off)
+            uaa.uaa_seq2head_permute(uaa.UAA_HEAD2SEQ, 0, [lse.unsqueeze(-1), d["l_other"]], l_tok, self.seq_off,
+                                     self.head_off)
             return 1
         raise ValueError(name)
 
@@ -373,7 +404,22 @@ class RingShare:
         per = rows * self.D * 2 + rows * 4
         return len(self.kv) * per + per
 
-    def launch_one(self, name, s):
+    def timing_bufs(self, s):
+        """Per-set partials and result for the merge timing (see Share)."""
+        if not hasattr(self, "_tbufs"):
+            self._tbufs = {}
+        if s not in self._tbufs:
+            torch, bf = self.torch, self.torch.bfloat16
+            shp = (self.B, self.Sq, self.H)
+            self._tbufs[s] = {
+                "o_part": [torch.randn(*shp, self.D, device="cuda").to(bf) for _ in self.kv],
+                "l_part": [8 + torch.randn(*shp, device="cuda") for _ in self.kv],
+                "o": torch.empty(*shp, self.D, device="cuda", dtype=bf),
+                "lse": torch.empty(*shp, device="cuda", dtype=torch.float32),
+            }
+        return self._tbufs[s]
+
+    def launch_one(self, name, s, timing=False):
         uaa = self.uaa
         d = self.sets[s]
         if name == "attn":
@@ -385,7 +431,11 @@ class RingShare:
                 self.attn_chunk(s, c, self.ws[0], acc=True)
             return len(self.kv) - 1
         if name == "merge":
-            uaa.usp_lse_merge(self.o_part, self.l_part, self.o, self.lse)
+            if timing:
+                t = self.timing_bufs(s)
+                uaa.usp_lse_merge(t["o_part"], t["l_part"], t["o"], t["lse"])
+            else:
+                uaa.usp_lse_merge(self.o_part, self.l_part, self.o, self.lse)
             return 1
         raise ValueError(name)
 
@@ -842,6 +892,9 @@ def main():
     # events on the launch stream; a spin kernel first gives the host a head
     # start so no launch waits on the host.
     log = {}
+    for s_ in range(n_sets):   # allocated before the timed region
+        share.timing_bufs(s_)
+    torch.cuda.synchronize()
     for name in share.kernel_names:
         a_ev = torch.cuda.Event(enable_timing=True)
         b_ev = torch.cuda.Event(enable_timing=True)
@@ -850,7 +903,7 @@ def main():
         a_ev.record()
         n = 0
         for i in range(args.steps):
-            n += share.launch_one(name, i % n_sets)
+            n += share.launch_one(name, i % n_sets, timing=True)
         b_ev.record()
         torch.cuda.synchronize()
         log[name] = 1e3 * a_ev.elapsed_time(b_ev) / n
