@@ -20,12 +20,12 @@ LIB = os.path.join(HERE, "libuaa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "permute.hip", "merge.hip", "attn_fp32.hip", "attn_bf16.hip", "attn_bwd.hip", "attn_bwd_fp32.hip"]
+SOURCES = ["abi.hip", "permute.hip", "merge.hip", "attn_fp32.hip", "attn_bf16.hip", "attn_p32.hip", "attn_bwd.hip", "attn_bwd_fp32.hip"]
 HEADERS = ["internal.h", "attn_common.h"]
 
 CFLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", "-Wno-inline-asm",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 

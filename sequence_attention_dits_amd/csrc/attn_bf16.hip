@@ -44,6 +44,8 @@
 //    give o = 0, lse = -inf.
 #include "attn_common.h"
 
+#include <stdlib.h>
+
 #include <type_traits>
 
 namespace uaa {
@@ -848,6 +850,15 @@ SplitPlan plan_split(int64_t n_units, int64_t n_tiles, int n_cu)
     return plan;
 }
 
+static bool p32_on()
+{
+    static const bool on = [] {
+        const char* e = getenv("UAA_ATTN_P32");
+        return !(e && e[0] == '0');
+    }();
+    return on;
+}
+
 hipError_t launch_attn_bf16(int D, int o_dtype, const AttnArgs& a0, hipStream_t s)
 {
     AttnArgs a = a0;
@@ -860,6 +871,8 @@ hipError_t launch_attn_bf16(int D, int o_dtype, const AttnArgs& a0, hipStream_t 
     }
     const int64_t blocks = a.split_p > 1 ? a.n_whole + (units - a.n_whole) * a.split_p : units;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (D == 128 && !a.masked && a.split_p <= 1 && a.n_qsh == 0 && attn_p32_fits(a.Sk, a.row_heads) && p32_on())
+        return launch_attn_p32(o_dtype, a0, s);
     const dim3 grid((unsigned)blocks);
     const bool ob = o_dtype == UAA_BF16;
     if (D == 128) return ob ? launch_d<128, true>(a, grid, s) : launch_d<128, false>(a, grid, s);

@@ -1,0 +1,586 @@
+// attn_p32.hip -- blockwise attention forward with LSE, bf16 inputs, D = 128,
+// every key allowed, software-pipelined: the variant the library launches
+// for that case.
+//
+// What it computes is what attn_bf16.hip computes for the unmasked case:
+// for every query row the pair (out, lse) of one Ring step ("Add Unified
+// Sequence Parallel attention", diffusers PR #12693, review thread; "Context
+// parallelism" docs, "Ring Attention"), optionally merged into the running
+// (out, lse) of the pass.
+//
+// Layout as in attn_bf16.hip: a workgroup owns 256 query rows of one
+// (batch, head), 8 wavefronts of 32 rows, two per SIMD.  What differs is the
+// schedule inside each wavefront.  There, a tile step runs
+//   [A] the scores of tile t+1 (16 matrix instructions), each beside the
+//       softmax numerators of two of tile t's scores (vector work), then
+//   [B] O += V_t^T P_t (16 matrix instructions), each beside one step of the
+//       row maximum of tile t+1,
+// so matrix and vector work of one wavefront are independent of each other
+// and issue back to back, and the other wavefront of the SIMD fills the
+// gaps.  The softmax of the last 16-key chunk moves into [B] (its products
+// come last there), so that [A] carries three quarters of the vector work,
+// and [A] runs at raised wave priority; the first V operands of [B] are read
+// during the end of [A].  Each of these measured a few per cent.  What the
+// pipelining itself takes, learnt the hard way:
+//  * the matrix instructions are inline assembly with their register files
+//    fixed (scores in VGPRs, O and Q in AGPRs): left to itself the compiler
+//    puts the scores in AGPRs and copies them every tile.  The compiler does
+//    not see them as matrix instructions, so vector code touching their
+//    results sits behind explicit wait states (fences below) or, inside a
+//    step, at least two matrix instructions later;
+//  * the loop body is one straight block of six steps (two score-register
+//    parities x three LDS stages) with no exit in the middle: exits make the
+//    register allocator move the AGPR accumulators behind the matrix
+//    instructions still writing them.  Steps past the last tile run on fully
+//    masked tiles (nothing added), so the launcher uses this kernel only
+//    where that padding is small;
+//  * the softmax results are pinned with an empty asm before the branch
+//    that follows them; otherwise IR-level sinking moves the softmax below
+//    the branch, away from the matrix instructions it is meant to run beside;
+//  * K and V tiles are copied global -> LDS by buffer loads that write LDS,
+//    issued as inline assembly: as builtins, the compiler would make the next
+//    LDS reads wait for every copy in flight (vmcnt(0)), since it cannot tell
+//    the stage being read from the stage being filled.  Three stages each,
+//    copies two steps ahead, waited for explicitly before the step's barrier.
+// V is stored row-major with the 16-byte units of a row swizzled, and the PV
+// operands are read with ds_read_b64_tr_b16 (two give a lane the 8 keys of
+// one feature in the order the score registers hold them).  Row maximum
+// raised lazily (2^8 threshold), exp2 with the scale folded in, natural-log
+// LSE at the end.
+#include "attn_common.h"
+
+#include <type_traits>
+
+namespace uaa {
+
+typedef __bf16 p_bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 p_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float p_f32x16 __attribute__((ext_vector_type(16)));
+typedef float p_f32x4 __attribute__((ext_vector_type(4)));
+typedef float p_f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int p_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int p_u32x2 __attribute__((ext_vector_type(2)));
+typedef short p_i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char p_lds_u8;
+typedef __attribute__((address_space(3))) p_u32x4 p_lds_u32x4;
+typedef __attribute__((address_space(3))) p_i16x4 p_lds_i16x4;
+
+constexpr int kPWaves = 8;
+constexpr int kPBM = kPWaves * 32;    // query rows per workgroup
+constexpr int kPBN = 64;              // keys per tile
+constexpr int kPD = 128;
+constexpr int kPRowB = 2 * kPD;       // bytes per row
+constexpr int kPTB = kPBN * kPRowB;   // bytes of one K or V tile
+constexpr float kPLn2 = 0.69314718055994530942f;
+constexpr float kPLog2e = 1.44269504088896340736f;
+constexpr float kPRescale = 8.0f;     // lazy rescale threshold, log2 units
+
+__device__ __forceinline__ unsigned int p_pack(float lo, float hi)
+{
+    return __builtin_bit_cast(unsigned int, __builtin_convertvector(p_f32x2{lo, hi}, p_bf16x2));
+}
+__device__ __forceinline__ float p_lo(unsigned int x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float p_hi(unsigned int x) { return __uint_as_float(x & 0xffff0000u); }
+__device__ __forceinline__ float p_max3(float a, float b, float c)
+{
+    return __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
+}
+
+// Physical 16-byte unit of logical unit u of tile row r: u ^ swz(r), swz
+// swapping the two 2-bit halves of r % 16.  Row reads (16 consecutive rows,
+// one unit) and the transposing reads (4 rows x 4 units per 16 lanes) then
+// fall on distinct banks.
+__device__ __forceinline__ int p_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Raw buffer descriptor (stride 0) over nrec bytes from base; reads from
+// nrec on return zero.
+typedef unsigned int p_rsrc __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ p_rsrc p_make_rsrc(const void* base, uint32_t nrec)
+{
+    const uint64_t p = (uint64_t)base;
+    return p_rsrc{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, nrec, 0x00020000u};
+}
+
+// One 16-byte-per-lane copy global -> LDS (buffer_load ... lds): lane s
+// writes bytes [lds + 16 s, lds + 16 s + 16), reading byte voff of r.
+__device__ __forceinline__ void p_dma(const p_rsrc& r, uint32_t voff, uint32_t lds)
+{
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass has no SGPR operand constraint
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(lds)
+                 : "memory", "m0");
+#endif
+}
+
+__device__ __forceinline__ void p_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// S (VGPRs) = K (VGPRs) x Q (AGPRs) [+ S];  O (AGPRs) += V (VGPRs) x P (VGPRs)
+__device__ __forceinline__ void p_mma_s0(p_f32x16& d, const p_bf16x8& k, const p_bf16x8& q)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(k), "a"(q));
+}
+__device__ __forceinline__ void p_mma_s(p_f32x16& d, const p_bf16x8& k, const p_bf16x8& q)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(k), "a"(q));
+}
+__device__ __forceinline__ void p_mma_o(p_f32x16& d, const p_bf16x8& v, const p_u32x4& p)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(v), "v"(p));
+}
+// 32 wait states (more than any matrix result needs) before vector code
+// touches the scores or the O accumulators
+__device__ __forceinline__ void p_fence_s(p_f32x16 (&s)[2])
+{
+    asm volatile("s_nop 15\n\ts_nop 15" : "+v"(s[0]), "+v"(s[1]));
+}
+__device__ __forceinline__ void p_fence_o(p_f32x16 (&o)[4])
+{
+    asm volatile("s_nop 15\n\ts_nop 15" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
+}
+// the O accumulators are in AGPRs here (both sides of a branch that
+// rescales them leave them in the same registers)
+__device__ __forceinline__ void p_pin_o(p_f32x16 (&o)[4])
+{
+    asm volatile("" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
+}
+// values complete at this point (keeps them from being sunk past a branch)
+__device__ __forceinline__ void p_pin_p(p_u32x4 (&p)[4])
+{
+    asm volatile("" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]));
+}
+__device__ __forceinline__ void p_pin_f(float& x) { asm volatile("" : "+v"(x)); }
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArgs a)
+{
+    // V stages, K stages, Q staging: every operand read is a per-lane
+    // register plus an immediate (stage, chunk, block) below 64 KB
+    constexpr int OFF_V = 0, OFF_K = 3 * kPTB, OFF_Q = 6 * kPTB;
+    constexpr int SMEM = OFF_Q + kPBM * kPRowB;   // 160 KB
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
+    p_lds_u8* const L = (p_lds_u8*)smem;
+
+    int64_t qt, hh, b;
+    decode_tile(a, qt, hh, b);
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hg = lane >> 5;
+    const int64_t H = a.H, Sq = a.Sq, Sk = a.Sk;
+    const int64_t RH = a.row_heads, h_in = a.head0 + hh;
+    const uint32_t ld2 = (uint32_t)(RH * kPD * 2);
+    const int64_t r0 = qt * kPBM + 32 * wave;     // first row of this wave
+    const int64_t i = r0 + l32;                    // this lane's row
+    const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + ((b * Sk) * RH + h_in) * kPD * 2;
+    const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + ((b * Sk) * RH + h_in) * kPD * 2;
+    const int n = (int)((Sk + kPBN - 1) / kPBN);
+
+    // One descriptor per tensor over this head's keys (rows from Sk on read
+    // as zero; the launcher checks that the range fits 32 bits) and this
+    // lane's byte offset for each of the wave's 2 copy instructions per tile
+    // (copy c moves tile rows 4 (8 c + wave) .. +3); tile t adds t * 64 rows.
+    const uint32_t nrec_k = Sk > 0 ? (uint32_t)((Sk - 1) * ld2 + kPD * 2) : 0u;
+    const p_rsrc krs = p_make_rsrc(kbase, nrec_k);
+    const p_rsrc vrs = p_make_rsrc(vbase, nrec_k);
+    uint32_t coff[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int row = 4 * (kPWaves * c + wave) + (lane >> 4);
+        coff[c] = (uint32_t)row * ld2 + (uint32_t)(((lane & 15) ^ p_swz(row)) << 4);
+    }
+    const uint32_t tile_bytes = (uint32_t)kPBN * ld2;
+    auto copy_tile = [&](const p_rsrc& rs, int off, int t, int s, int c) {
+        p_dma(rs, coff[c] + (uint32_t)t * tile_bytes,
+              (uint32_t)(uintptr_t)(L + off + s * kPTB + (kPWaves * c + wave) * 1024));
+    };
+
+    // ---- prologue: Q (this wave's 32 rows), K0..K2, V0..V1 ----------------
+    if (n > 0) {
+        const unsigned char* qbase = static_cast<const unsigned char*>(a.q) + ((b * Sq) * RH + h_in) * kPD * 2;
+        const uint32_t nrec = Sq > r0 ? (uint32_t)((Sq - 1 - r0) * ld2 + kPD * 2) : 0u;
+        const p_rsrc qr = p_make_rsrc(qbase + (Sq > r0 ? r0 : 0) * ld2, nrec);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = 4 * j + (lane >> 4);
+            p_dma(qr, (uint32_t)row * ld2 + (uint32_t)(((lane & 15) ^ p_swz(row)) << 4),
+                  (uint32_t)(uintptr_t)(L + OFF_Q + wave * 32 * kPRowB + j * 1024));
+        }
+        // stages past the last tile repeat it: the V a fully masked step
+        // multiplies by zero must be finite
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            const int tt = t < n ? t : n - 1;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) copy_tile(krs, OFF_K, tt, t, c);
+            if (t < 2) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) copy_tile(vrs, OFF_V, tt, t, c);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+
+    // ---- operand addressing ----------------------------------------------
+    // Row read of logical unit 2 kc + hg of row r: byte r * 256 +
+    // ((kc << 5) ^ ((hg ^ swz(r)) << 4)); K rows 32 jb + l32 (swz(l32)).
+    const int kx = (hg ^ p_swz(l32)) << 4;
+    int kaddr[8];   // + ks * tile + jb * 32 rows
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) kaddr[kc] = OFF_K + l32 * kPRowB + ((kc << 5) ^ kx);
+    // Transposing V read k (0, 1): this lane as source lane (g, e, ah) =
+    // (lane / 16, lane / 4 % 4, lane % 4) addresses keys 16 c + 4 (g / 2) + e
+    // + 8 k at features 32 db + 16 (g % 2) + 4 ah; the result lane (feature
+    // 32 db + l32, half hg) holds keys 16 c + 4 hg + {0..3, 8..11}.
+    int vaddr[2][4];   // + vs * tile + c * 16 rows
+    {
+        const int g = lane >> 4, e = (lane >> 2) & 3, ah = lane & 3;
+        const int w = 2 * (g & 1) + (ah >> 1);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int r = 4 * (g >> 1) + e + 8 * k;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                vaddr[k][db] = OFF_V + r * kPRowB + 8 * (ah & 1) + ((db << 6) ^ ((w ^ p_swz(r)) << 4));
+        }
+    }
+    auto vread = [&](int vs, int c, int db) {
+        const p_i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (p_lds_i16x4*)(L + vaddr[0][db] + (vs * kPTB + c * 16 * kPRowB)));
+        const p_i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (p_lds_i16x4*)(L + vaddr[1][db] + (vs * kPTB + c * 16 * kPRowB)));
+        return __builtin_bit_cast(p_bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto kread = [&](int ks, int kc, int jb) {
+        return __builtin_bit_cast(p_bf16x8, *(const p_lds_u32x4*)(L + kaddr[kc] + (ks * kPTB + jb * 32 * kPRowB)));
+    };
+
+    // Q operands: lane holds row l32 of the wave, features 16 kc + 8 hg .. +7
+    p_bf16x8 qop[8];
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc)
+        qop[kc] = __builtin_bit_cast(
+            p_bf16x8, *(const p_lds_u32x4*)(L + OFF_Q + wave * 32 * kPRowB + l32 * kPRowB + ((kc << 5) ^ kx)));
+
+    const float c2 = a.scale_log2;
+    p_f32x16 oacc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
+    p_pin_o(oacc);
+    float m = -INFINITY;    // reference maximum (exp2 units) of this lane's row
+    float lsum = 0.f;       // this lane half's share of the row sum
+    p_f32x16 sacc[2][2];    // [parity][jb]: scores S^T of a tile; register v of
+                            // block jb holds key 32 jb + 8 (v / 4) + 4 hg + v % 4
+
+    // Keys at or past lim of a tile -> -inf (the ragged end, read as zeros;
+    // tiles past the end: lim = 0).  Key 32 jb + 8 (v / 4) + 4 hg + v % 4 is
+    // dead iff its constant part reaches lim - 4 hg.
+    auto mask_keys = [&](p_f32x16 (&s)[2], int lim) {
+        p_fence_s(s);
+        const int ll = lim - 4 * hg;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                if (32 * jb + 8 * (v >> 2) + (v & 3) >= ll) s[jb][v] = -INFINITY;
+    };
+    auto key_lim = [&](int t) {
+        const int64_t r = Sk - (int64_t)t * kPBN;
+        return r <= 0 ? 0 : (r >= kPBN ? kPBN : (int)r);
+    };
+    // Row maximum as 16 single instructions: ten three-way maxima of the
+    // lane's 32 scores, one two-way, then the tree.
+    float rm[11], ra[4], mx = -INFINITY;
+    auto max_op = [&](const p_f32x16 (&s)[2], int j) {
+        if (j < 10) {
+            const int e0 = 3 * j, e1 = 3 * j + 1, e2 = 3 * j + 2;
+            rm[j] = p_max3(s[e0 >> 4][e0 & 15], s[e1 >> 4][e1 & 15], s[e2 >> 4][e2 & 15]);
+        } else if (j == 10) {
+            rm[10] = __builtin_elementwise_maximum(s[1][14], s[1][15]);
+        } else if (j < 14) {
+            const int u = 3 * (j - 11);
+            ra[j - 11] = p_max3(rm[u], rm[u + 1], rm[u + 2]);
+        } else if (j == 14) {
+            ra[3] = __builtin_elementwise_maximum(rm[9], rm[10]);
+        } else {
+            mx = __builtin_elementwise_maximum(p_max3(ra[0], ra[1], ra[2]), ra[3]);
+        }
+    };
+    // both halves of the row; the reference maximum is raised (O and the sum
+    // rescaled) when the tile's maximum exceeds it by more than the threshold
+    auto finish_max = [&]() {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        const float t = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        const float mn = __builtin_elementwise_maximum(m, t * c2);
+        const bool need = mn > m + kPRescale;
+        if (__any(need)) {
+            p_fence_o(oacc);
+            const float alpha = need ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+            m = need ? mn : m;
+            p_pin_o(oacc);
+        }
+    };
+    // softmax numerators, two scores per op k (0..15): key block k / 8,
+    // registers 2 (k % 8), +1; 16-key chunk c of the P operand is pw[c]
+    float ps0 = 0.f, ps1 = 0.f;
+    auto soft_op = [&](const p_f32x16 (&s)[2], p_u32x4 (&pw)[4], float mu, int k) {
+        const int jb = k >> 3, v = 2 * (k & 7);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[jb][v], c2, -mu));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[jb][v + 1], c2, -mu));
+        ps0 += p0;
+        ps1 += p1;
+        pw[2 * jb + (v >> 3)][(v & 7) >> 1] = p_pack(p0, p1);
+    };
+    // score instruction r (0..15): k-chunk r / 2, key block r % 2; its K
+    // operand is read two instructions ahead
+    constexpr int KPF = 2, VPF = 2;
+    auto score_mma = [&](p_f32x16 (&s)[2], p_bf16x8 (&kop)[16], int ks, int r) {
+        const int kc = r >> 1, jb = r & 1;
+        if (r + KPF < 16) kop[r + KPF] = kread(ks, (r + KPF) >> 1, (r + KPF) & 1);
+        if (kc == 0) p_mma_s0(s[jb], kop[r], qop[kc]);
+        else p_mma_s(s[jb], kop[r], qop[kc]);
+    };
+    // PV instruction r (0..15): chunk r / 4, feature block r % 4; its V
+    // operand is read two instructions ahead (the first two during [A])
+    auto pv_mma = [&](p_bf16x8 (&vop)[16], const p_u32x4 (&pw)[4], int vs, int r) {
+        if (r + VPF < 16) vop[r + VPF] = vread(vs, (r + VPF) >> 2, (r + VPF) & 3);
+        p_mma_o(oacc[r & 3], vop[r], pw[r >> 2]);
+    };
+
+    // ---- main loop ---------------------------------------------------------
+    // K tile j and V tile j in stage j % 3.  Step t reads K stage (t+1) % 3
+    // (tile t+1) and V stage t % 3 (tile t), and copies K tile t+3 into stage
+    // t % 3 and V tile t+2 into stage (t+2) % 3 (both read last in step t-1,
+    // before its closing barrier), among its PV instructions; a copy has a
+    // whole step to land.  Copies past the end repeat the last tile.
+    if (n > 0) {
+        p_bf16x8 kop[16];
+#pragma unroll
+        for (int r = 0; r < KPF; ++r) kop[r] = kread(0, r >> 1, r & 1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) score_mma(sacc[0], kop, 0, r);
+        if (key_lim(0) < kPBN) mask_keys(sacc[0], key_lim(0));
+        p_fence_s(sacc[0]);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) max_op(sacc[0], j);
+        finish_max();
+    }
+    // every wave is done with K stage 0 before step 0 copies tile 3 into it
+    p_barrier();
+    auto step = [&](auto parity_tag, auto t3_tag, int t) {
+        constexpr int P = decltype(parity_tag)::value, T3 = decltype(t3_tag)::value;
+        constexpr int KS = (T3 + 1) % 3, VS = T3;
+        const int tk = t + 3 < n ? t + 3 : n - 1, tv = t + 2 < n ? t + 2 : n - 1;
+        const float mu = m == -INFINITY ? 0.f : m;
+        ps0 = 0.f;
+        ps1 = 0.f;
+        p_u32x4 pw[4];
+        p_bf16x8 vop[16];
+        // [A] scores of tile t+1 beside the softmax of tile t
+        {
+            p_bf16x8 kop[16];
+#pragma unroll
+            for (int r = 0; r < KPF; ++r) kop[r] = kread(KS, r >> 1, r & 1);
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                score_mma(sacc[P ^ 1], kop, KS, r);
+                if ((r & 3) != 3) {
+                    const int x = r - (r >> 2), c = x >> 2;
+                    soft_op(sacc[P], pw, mu, (c >> 1) * 8 + (c & 1) * 4 + (x & 3));
+                }
+                if (r >= 16 - VPF) vop[r - (16 - VPF)] = vread(VS, (r - (16 - VPF)) >> 2, (r - (16 - VPF)) & 3);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        __builtin_amdgcn_s_setprio(0);
+        p_pin_p(pw);
+        const int lim = key_lim(t + 1);
+        if (lim < kPBN) mask_keys(sacc[P ^ 1], lim);
+        // [B] O += V_t^T P_t beside the row maximum of tile t+1 (its scores
+        // were written at least two matrix instructions, > 60 cycles,
+        // before), with this step's copies among them
+        {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                pv_mma(vop, pw, VS, r);
+                if (r < 8 && (r & 1) == 0) soft_op(sacc[P], pw, mu, 12 + (r >> 1));
+                max_op(sacc[P ^ 1], r);
+                if ((r & 3) == 1) {
+                    const int c = r >> 2;
+                    if (c < 2) copy_tile(krs, OFF_K, tk, T3, c);
+                    else copy_tile(vrs, OFF_V, tv, (T3 + 2) % 3, c - 2);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        lsum += ps0 + ps1;
+        p_pin_f(lsum);
+        p_pin_f(mx);
+        finish_max();
+        // the copies of step t-1 (K tile t+2, V tile t+1) have landed; this
+        // step's 4 may still run
+        __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
+        p_barrier();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    for (int t = 0; t < n; t += 6) {
+        step(I0{}, I0{}, t);
+        step(I1{}, I1{}, t + 1);
+        step(I0{}, I2{}, t + 2);
+        step(I1{}, I0{}, t + 3);
+        step(I0{}, I1{}, t + 4);
+        step(I1{}, I2{}, t + 5);
+    }
+    // the last copies (into stages nothing reads) have landed and every wave
+    // is done with the stages before the LDS is reused; O is final
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    p_fence_o(oacc);
+
+    // ---- epilogue: O = acc / l, LSE = m + log2 l (natural log stored);
+    // with a.acc merged into the (o, lse) already there, with the weights of
+    // the LSE merge.
+    float lt;
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+        lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lb2 = lt > 0.f ? m + __log2f(lt) : -INFINITY;
+    float wp = 0.f, wb = 1.f, lse_out2 = lb2;
+    if (a.acc) {
+        const float lp2 = i < Sq ? a.lse[(b * Sq + i) * H + hh] * kPLog2e : -INFINITY;
+        const float mm = __builtin_elementwise_maximum(lp2, lb2);
+        if (mm == -INFINITY) {
+            wp = 0.f;
+            wb = 0.f;
+            lse_out2 = -INFINITY;
+        } else {
+            const float ep = __builtin_amdgcn_exp2f(lp2 - mm), eb = __builtin_amdgcn_exp2f(lb2 - mm);
+            const float sum = ep + eb;
+            wp = ep / sum;
+            wb = eb / sum;
+            lse_out2 = mm + __log2f(sum);
+        }
+    }
+    if constexpr (OUT_BF16) {
+        // the wave's 32 x 128 tile through LDS, stored as whole rows (4 rows
+        // of 256 bytes per instruction)
+        constexpr int RS = kPRowB + 16;
+        constexpr int WS = 32 * RS + 32 * 8;
+        p_lds_u8* R = L + wave * WS;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = 32 * db + 8 * g + 4 * hg;
+                const p_u32x2 w{p_pack(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                                p_pack(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+                *(__attribute__((address_space(3))) p_u32x2*)(R + l32 * RS + d0 * 2) = w;
+            }
+        if (a.acc && hg == 0) *(__attribute__((address_space(3))) p_f32x2*)(R + 32 * RS + l32 * 8) = p_f32x2{wp, wb};
+        // this wave's LDS stores are done before its lanes read each other's
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        asm volatile("" ::: "memory");
+        const int rr = lane >> 4, cu = lane & 15;
+        auto dst_of = [&](int k) {
+            const int64_t row = r0 + 4 * k + rr;
+            return reinterpret_cast<p_u32x4*>(static_cast<unsigned char*>(a.o) + ((b * Sq + row) * H + hh) * kPD * 2 +
+                                              cu * 16);
+        };
+        auto row_ok = [&](int k) { return r0 + 4 * k + rr < Sq; };
+        // the previous result's rows, all loaded before any store (a store
+        // to o could alias a later load and serialise each pair)
+        p_u32x4 pvv[8];
+        if (a.acc) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) pvv[k] = row_ok(k) ? *dst_of(k) : p_u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int r = 4 * k + rr;
+            p_u32x4 w = *(const p_lds_u32x4*)(R + r * RS + cu * 16);
+            if (a.acc) {
+                const p_f32x2 wr = *(const __attribute__((address_space(3))) p_f32x2*)(R + 32 * RS + r * 8);
+                const bool use = wr[0] != 0.f;   // a previous result of weight 0 is not read
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = fmaf(wr[0], use ? p_lo(pvv[k][e]) : 0.f, wr[1] * p_lo(w[e]));
+                    const float hi = fmaf(wr[0], use ? p_hi(pvv[k][e]) : 0.f, wr[1] * p_hi(w[e]));
+                    w[e] = p_pack(lo, hi);
+                }
+            }
+            if (row_ok(k)) *dst_of(k) = w;
+        }
+    } else {
+        if (i < Sq) {
+            const int64_t orow = ((b * Sq + i) * H + hh) * kPD;
+            const float sb = wb * inv;
+            auto dst_of = [&](int db, int g) {
+                return reinterpret_cast<p_f32x4*>(static_cast<float*>(a.o) + orow + 32 * db + 8 * g + 4 * hg);
+            };
+            p_f32x4 pvv[4][4];
+            const bool use = a.acc && wp != 0.f;
+            if (use) {
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) pvv[db][g] = *dst_of(db, g);
+            }
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    p_f32x4 x{oacc[db][4 * g] * sb, oacc[db][4 * g + 1] * sb, oacc[db][4 * g + 2] * sb,
+                              oacc[db][4 * g + 3] * sb};
+                    if (use) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = fmaf(wp, pvv[db][g][e], x[e]);
+                    }
+                    *dst_of(db, g) = x;
+                }
+        }
+    }
+    if (hg == 0 && i < Sq) a.lse[(b * Sq + i) * H + hh] = lse_out2 * kPLn2;
+}
+
+bool attn_p32_fits(int64_t Sk, int64_t row_heads)
+{
+    // the key range of one head must fit the 32-bit buffer range, and the
+    // fully masked steps that pad the tile count to a multiple of six must
+    // be at most a tenth of the work
+    const int64_t n = (Sk + kPBN - 1) / kPBN;
+    const int64_t pad = (6 - n % 6) % 6;
+    return n > 0 && Sk * row_heads * kPD * 2 < (int64_t)0xF0000000 && pad * 10 <= n;
+}
+
+hipError_t launch_attn_p32(int o_dtype, const AttnArgs& a0, hipStream_t s)
+{
+    AttnArgs a = a0;
+    a.n_qtiles = (int32_t)((a.Sq + kPBM - 1) / kPBM);
+    const int64_t units = (int64_t)a.n_qtiles * a.H * a.B;
+    if (units <= 0) return hipSuccess;
+    if (units > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)units), block(64 * kPWaves);
+    if (o_dtype == UAA_BF16) return launch_kernel(attn_p32_kernel<true>, grid, block, 0, s, a);
+    return launch_kernel(attn_p32_kernel<false>, grid, block, 0, s, a);
+}
+
+}  // namespace uaa
