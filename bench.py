@@ -623,7 +623,7 @@ def cpu_baseline(share: "Share", target_s: float):
 # ---- HBM traffic of the attention kernel (rocprofv3 counters) ---------------
 PMC_COPY_BYTES = 1 << 30              # calibration copy: a plain device-to-device copy of 1 GiB
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_flux1024_hbm_traffic.txt")
-ATTN_SOURCES = ["attn_bf16.hip", "attn_common.h", "internal.h"]
+ATTN_SOURCES = ["attn_bf16.hip", "attn_p32.hip", "attn_common.h", "internal.h"]
 
 
 def attn_source_hash():
@@ -635,6 +635,23 @@ def attn_source_hash():
         with open(os.path.join(ROOT, "sequence_attention_dits_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def _is_attn_fwd(kernel_name):
+    """A bf16 attention forward kernel: the pipelined one or the general one."""
+    return "attn_p32_kernel" in kernel_name or "attn_bf16_kernel" in kernel_name
+
+
+def attn_kernel_name(masked, split, sk):
+    """The forward kernel the library launches for a bf16 D=128 call: the
+    software-pipelined one for unmasked launches without a key split whose
+    key tiles pad to a multiple of six by at most a tenth (unless
+    UAA_ATTN_P32=0), else the general one."""
+    n = (sk + 63) // 64
+    pad = (6 - n % 6) % 6
+    if not masked and not split and n > 0 and pad * 10 <= n and os.environ.get("UAA_ATTN_P32", "1")[:1] != "0":
+        return "attn_p32_kernel<true>"
+    return "attn_bf16_kernel<128,%s,true,%s>" % ("true" if masked else "false", "true" if split else "false")
 
 
 def pmc_probe(args):
@@ -673,7 +690,7 @@ def pmc_summary(fetch_dir, write_dir, workload):
         vals = _pmc_values(d, counter)
         copy = sorted(v for k, vs in vals.items() if "copyBuffer" in k or "copy" in k.lower() for v in vs)
         copy = [v for v in copy if v * 1024 > PMC_COPY_BYTES / 4]
-        attn = [v for k, vs in vals.items() if "attn_bf16_kernel" in k for v in vs]
+        attn = [v for k, vs in vals.items() if _is_attn_fwd(k) for v in vs]
         if not copy or not attn:
             raise SystemExit("no calibration copy or attention dispatch in " + d)
         scale = PMC_COPY_BYTES / (1024 * sum(copy) / len(copy))
@@ -724,7 +741,7 @@ SIMDS = 256 * 4   # MI355X: 256 compute units of 4 SIMDs, in 8 XCDs
 
 
 def counter_summary(dirs):
-    """Means per attention dispatch of every counter in the given rocprofv3
+    """Means per attention-forward dispatch of every counter in the given rocprofv3
     --pmc runs, and the matrix-core utilisation they imply: busy cycles of
     the matrix units over (active cycles of one XCD x all SIMDs), where
     GRBM_GUI_ACTIVE is summed over the 8 XCDs."""
@@ -735,7 +752,7 @@ def counter_summary(dirs):
                         "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES",
                         "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT"):
             for k, vs in _pmc_values(d, counter).items():
-                if "attn_bf16_kernel" in k:
+                if _is_attn_fwd(k):
                     vals[counter].extend(vs)
     if not vals:
         raise SystemExit("no attention dispatch in " + " ".join(dirs))
@@ -966,10 +983,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic() if args.workload == "flux1024" else None,
-                     # template arguments: D, masked, bf16 output, key split
-                     "kernel": "attn_bf16_kernel<128,%s,true,%s>" % (
-                         "true" if ring and share.masks[0] is not None else "false",
-                         "true" if share.ws[0] is not None else "false"),
+                     "kernel": attn_kernel_name(ring and share.masks[0] is not None, share.ws[0] is not None,
+                                                (share.kv[0][1] - share.kv[0][0]) if ring else
+                                                (share.ring[0][1] - share.ring[0][0])),
                      "launch_us": round(attn_us, 2), "flops_per_launch": attn_flops_launch},
         "kernels": kernels,
     }

@@ -1,0 +1,97 @@
+"""GPU parity of the software-pipelined attention kernel (unmasked, D = 128,
+bf16 inputs, no key split) against the fp64 oracle, every row.
+
+The library launches that kernel when the key tiles of a call (64 keys
+each) pad to a multiple of six by at most a tenth, so these shapes are
+chosen to reach it: 6, 11 and 12 key tiles, with and without a ragged last
+tile, ragged query rows (a partial last 256-row workgroup and waves past the
+end), several heads and batches, bf16 and fp32 output, a two-block Ring pass
+accumulated in place, and scores large enough to make the running maximum
+rise mid-row (the rescale path).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import sequence_attention_dits_amd as uaa
+from gpu_common import check_pair, dev_bf16, host_f64, say
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, B, Sq, Sk, H
+    ("tiles6_exact", 1, 256, 384, 2),
+    ("tiles6_ragged_keys_rows", 2, 300, 367, 3),
+    ("tiles11_pad1", 1, 513, 700, 1),
+    ("tiles12_tail63", 1, 100, 767, 2),
+]
+
+
+def _inputs(cfg, B, Sq, Sk, H, D=128):
+    qb, qv = synth.tensor(cfg, 0, (B, Sq, H, D), "bf16", rms_norm=True)
+    kb, kv = synth.tensor(cfg, 1, (B, Sk, H, D), "bf16", rms_norm=True)
+    vb, vv = synth.tensor(cfg, 2, (B, Sk, H, D), "bf16")
+    return (qb, qv), (kb, kv), (vb, vv)
+
+
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_pipelined_all_rows(case, out):
+    name, B, Sq, Sk, H = case
+    say("attn pipelined", name, out)
+    (qb, qv), (kb, kv), (vb, vv) = _inputs(1100 + CASES.index(case), B, Sq, Sk, H)
+    scale = 1.0 / math.sqrt(128)
+    o = torch.empty(B, Sq, H, 128, device="cuda", dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+    lse = torch.empty(B, Sq, H, device="cuda", dtype=torch.float32)
+    uaa.usp_attn_fwd_lse(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), o, lse, scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(qv, kv, vv, np.float32(scale))
+    check_pair(host_f64(o), host_f64(lse), o_ref, l_ref, "bf16", name)
+
+
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_pipelined_ring_pass_accumulates(out):
+    # two key blocks of 384 and 367 keys (6 tiles each), the second merged
+    # into the first's (O, LSE) in place: equals attention over all keys
+    B, Sq, H = 1, 300, 2
+    say("attn pipelined ring pass", out)
+    (qb, qv), (kb, kv), (vb, vv) = _inputs(1150, B, Sq, 751, H)
+    scale = 1.0 / math.sqrt(128)
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    o = torch.empty(B, Sq, H, 128, device="cuda", dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+    lse = torch.empty(B, Sq, H, device="cuda", dtype=torch.float32)
+    uaa.usp_attn_fwd_lse(q, k[:, :384].contiguous(), v[:, :384].contiguous(), o, lse, scale)
+    uaa.usp_attn_fwd_lse(q, k[:, 384:].contiguous(), v[:, 384:].contiguous(), o, lse, scale, accumulate=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(qv, kv, vv, np.float32(scale))
+    check_pair(host_f64(o), host_f64(lse), o_ref, l_ref, "bf16", "ring pass " + out)
+
+
+def test_pipelined_rising_maximum():
+    # large queries and a key block whose scores grow along the keys, so the
+    # running maximum of a row rises by far more than the lazy-rescale
+    # threshold several times along the row
+    B, Sq, Sk, H = 1, 256, 384, 1
+    say("attn pipelined rising maximum")
+    rng = np.random.default_rng(11)
+    q = 2.0 * rng.standard_normal((B, Sq, H, 128))
+    k = 2.0 * rng.standard_normal((B, Sk, H, 128)) * np.linspace(0.2, 3.0, Sk)[None, :, None, None]
+    v = rng.standard_normal((B, Sk, H, 128))
+    bits = [synth.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v)]
+    q, k, v = (synth.bf16_bits_to_f32(b) for b in bits)
+    scale = 1.0 / math.sqrt(128)
+    # the maximum of a row over all keys exceeds its maximum over the first
+    # tile by far more than the lazy-rescale threshold (8 in log2 units)
+    s = np.einsum("qd,kd->qk", q[0, :, 0].astype(np.float64), k[0, :, 0].astype(np.float64)) * scale / math.log(2)
+    assert np.median(s.max(axis=1) - s[:, :64].max(axis=1)) > 16.0
+    o = torch.empty(B, Sq, H, 128, device="cuda", dtype=torch.float32)
+    lse = torch.empty(B, Sq, H, device="cuda", dtype=torch.float32)
+    uaa.usp_attn_fwd_lse(dev_bf16(bits[0]), dev_bf16(bits[1]), dev_bf16(bits[2]), o, lse, scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(q, k, v, np.float32(scale))
+    check_pair(host_f64(o), host_f64(lse), o_ref, l_ref, "bf16", "rising maximum")
