@@ -20,7 +20,10 @@
 // gaps.  The softmax of the last 16-key chunk moves into [B] (its products
 // come last there), so that [A] carries three quarters of the vector work,
 // and [A] runs at raised wave priority; the first V operands of [B] are read
-// during the end of [A].  Each of these measured a few per cent.  What the
+// during the end of [A].  The step's barrier sits right after [B]'s last V
+// read, so the first K operands of the next step's [A] are read during the
+// last two slots of [B] instead of after the barrier.  Each of these
+// measured a few per cent.  What the
 // pipelining itself takes, learnt the hard way:
 //  * the matrix instructions are inline assembly with their register files
 //    fixed (scores in VGPRs, O and Q in AGPRs): left to itself the compiler
@@ -346,7 +349,8 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
     };
     // score instruction r (0..15): k-chunk r / 2, key block r % 2; its K
     // operand is read two instructions ahead
-    constexpr int KPF = 2, VPF = 2;
+    constexpr int KPF = 2, VPF = 2;   // the barrier placement in [B] assumes KPF == VPF
+    static_assert(KPF == VPF, "[B] reads its last V operand in slot 15 - VPF and the next K operands after it");
     auto score_mma = [&](p_f32x16 (&s)[2], p_bf16x8 (&kop)[16], int ks, int r) {
         const int kc = r >> 1, jb = r & 1;
         if (r + KPF < 16) kop[r + KPF] = kread(ks, (r + KPF) >> 1, (r + KPF) & 1);
@@ -380,6 +384,11 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
     }
     // every wave is done with K stage 0 before step 0 copies tile 3 into it
     p_barrier();
+    // the first K operands of each step's [A] are read at the end of the
+    // step before (after its barrier): step 0's here
+    p_bf16x8 knext[KPF];
+#pragma unroll
+    for (int r = 0; r < KPF; ++r) knext[r] = kread(1, r >> 1, r & 1);
     auto step = [&](auto parity_tag, auto t3_tag, int t) {
         constexpr int P = decltype(parity_tag)::value, T3 = decltype(t3_tag)::value;
         constexpr int KS = (T3 + 1) % 3, VS = T3;
@@ -393,7 +402,7 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
         {
             p_bf16x8 kop[16];
 #pragma unroll
-            for (int r = 0; r < KPF; ++r) kop[r] = kread(KS, r >> 1, r & 1);
+            for (int r = 0; r < KPF; ++r) kop[r] = knext[r];
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -424,6 +433,18 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
                     if (c < 2) copy_tile(krs, OFF_K, tk, T3, c);
                     else copy_tile(vrs, OFF_V, tv, (T3 + 2) % 3, c - 2);
                 }
+                if (r == 15 - KPF) {
+                    // this wave's last V read of the step is done: the copies
+                    // of step t-1 (K tile t+2, V tile t+1) have landed (this
+                    // step's 4 may still run), and after the barrier every
+                    // wave is done with the stages the next step's copies fill
+                    __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
+                    p_barrier();
+                }
+                if (r > 15 - KPF) {
+                    const int x = r - (16 - KPF);
+                    knext[x] = kread((T3 + 2) % 3, x >> 1, x & 1);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -431,10 +452,6 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
         p_pin_f(lsum);
         p_pin_f(mx);
         finish_max();
-        // the copies of step t-1 (K tile t+2, V tile t+1) have landed; this
-        // step's 4 may still run
-        __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
-        p_barrier();
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
