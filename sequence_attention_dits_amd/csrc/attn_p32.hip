@@ -23,7 +23,8 @@
 // during the end of [A].  The step's barrier sits right after [B]'s last V
 // read, so the first K operands of the next step's [A] are read during the
 // last two slots of [B] instead of after the barrier.  Each of these
-// measured a few per cent.  What the
+// measured a few per cent, as did copying a Ring pass's previous O rows
+// into the free Q staging region by DMA at the start.  What the
 // pipelining itself takes, learnt the hard way:
 //  * the matrix instructions are inline assembly with their register files
 //    fixed (scores in VGPRs, O and Q in AGPRs): left to itself the compiler
@@ -389,6 +390,25 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
     p_bf16x8 knext[KPF];
 #pragma unroll
     for (int r = 0; r < KPF; ++r) knext[r] = kread(1, r >> 1, r & 1);
+    // Continuing a Ring pass with bf16 output: the previous result's rows of
+    // this wave are copied now into its Q staging region (free once Q is in
+    // registers), and its LSE loaded, so that the epilogue's merge does not
+    // wait for them.  The copies land before step 0 ends (its vmcnt wait).
+    float lse_prev = -INFINITY;
+    if (a.acc) {
+        if (i < Sq) lse_prev = a.lse[(b * Sq + i) * H + hh];
+        if constexpr (OUT_BF16) {
+            const uint32_t ldo = (uint32_t)(H * kPD * 2);
+            const int64_t rows = Sq > r0 ? (Sq - r0 < 32 ? Sq - r0 : 32) : 0;
+            const p_rsrc orr = p_make_rsrc(static_cast<const unsigned char*>(a.o) +
+                                               ((b * Sq + (rows > 0 ? r0 : 0)) * H + hh) * kPD * 2,
+                                           rows > 0 ? (uint32_t)((rows - 1) * ldo + kPD * 2) : 0u);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                p_dma(orr, (uint32_t)(4 * j + (lane >> 4)) * ldo + (uint32_t)((lane & 15) << 4),
+                      (uint32_t)(uintptr_t)(L + OFF_Q + wave * 32 * kPRowB + j * 1024));
+        }
+    }
     auto step = [&](auto parity_tag, auto t3_tag, int t) {
         constexpr int P = decltype(parity_tag)::value, T3 = decltype(t3_tag)::value;
         constexpr int KS = (T3 + 1) % 3, VS = T3;
@@ -482,7 +502,7 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
     const float lb2 = lt > 0.f ? m + __log2f(lt) : -INFINITY;
     float wp = 0.f, wb = 1.f, lse_out2 = lb2;
     if (a.acc) {
-        const float lp2 = i < Sq ? a.lse[(b * Sq + i) * H + hh] * kPLog2e : -INFINITY;
+        const float lp2 = lse_prev * kPLog2e;
         const float mm = __builtin_elementwise_maximum(lp2, lb2);
         if (mm == -INFINITY) {
             wp = 0.f;
@@ -523,12 +543,12 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
                                               cu * 16);
         };
         auto row_ok = [&](int k) { return r0 + 4 * k + rr < Sq; };
-        // the previous result's rows, all loaded before any store (a store
-        // to o could alias a later load and serialise each pair)
+        // the previous result's rows, copied into LDS at the start
         p_u32x4 pvv[8];
         if (a.acc) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) pvv[k] = row_ok(k) ? *dst_of(k) : p_u32x4{0u, 0u, 0u, 0u};
+            for (int k = 0; k < 8; ++k)
+                pvv[k] = *(const p_lds_u32x4*)(L + OFF_Q + wave * 32 * kPRowB + (4 * k + rr) * kPRowB + cu * 16);
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
