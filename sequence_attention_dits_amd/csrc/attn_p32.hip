@@ -99,10 +99,14 @@ __device__ __forceinline__ int p_swz(int r) { return ((r & 3) << 2) | ((r >> 2) 
 // Raw buffer descriptor (stride 0) over nrec bytes from base; reads from
 // nrec on return zero.
 typedef unsigned int p_rsrc __attribute__((ext_vector_type(4)));
+// The values are uniform by construction; readfirstlane keeps them in
+// scalar registers where the compiler cannot prove it.
 __device__ __forceinline__ p_rsrc p_make_rsrc(const void* base, uint32_t nrec)
 {
     const uint64_t p = (uint64_t)base;
-    return p_rsrc{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, nrec, 0x00020000u};
+    return p_rsrc{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
+                  (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xffffu)),
+                  (uint32_t)__builtin_amdgcn_readfirstlane((int)nrec), 0x00020000u};
 }
 
 // One 16-byte-per-lane copy global -> LDS (buffer_load ... lds): lane s
@@ -112,7 +116,7 @@ __device__ __forceinline__ void p_dma(const p_rsrc& r, uint32_t voff, uint32_t l
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass has no SGPR operand constraint
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
-                 : "v"(voff), "s"(r), "s"(lds)
+                 : "v"(voff), "s"(r), "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds))
                  : "memory", "m0");
 #endif
 }
@@ -206,14 +210,40 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
 
     // ---- prologue: Q (this wave's 32 rows), K0..K2, V0..V1 ----------------
     if (n > 0) {
-        const unsigned char* qbase = static_cast<const unsigned char*>(a.q) + ((b * Sq) * RH + h_in) * kPD * 2;
-        const uint32_t nrec = Sq > r0 ? (uint32_t)((Sq - 1 - r0) * ld2 + kPD * 2) : 0u;
-        const p_rsrc qr = p_make_rsrc(qbase + (Sq > r0 ? r0 : 0) * ld2, nrec);
+        // rows [lo, hi) of the wave's 32 (all: every row, the rest reading as
+        // zero) from base = row r0 + lo, nrec bytes of it valid
+        auto copy_q = [&](const unsigned char* base, uint32_t nrec, int lo, int hi, bool all) {
+            const p_rsrc qr = p_make_rsrc(base, nrec);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = 4 * j + (lane >> 4);
-            p_dma(qr, (uint32_t)row * ld2 + (uint32_t)(((lane & 15) ^ p_swz(row)) << 4),
-                  (uint32_t)(uintptr_t)(L + OFF_Q + wave * 32 * kPRowB + j * 1024));
+            for (int j = 0; j < 8; ++j) {
+                const int row = 4 * j + (lane >> 4);
+                if (all || (row >= lo && row < hi))
+                    p_dma(qr, (uint32_t)(row - lo) * ld2 + (uint32_t)(((lane & 15) ^ p_swz(row)) << 4),
+                          (uint32_t)(uintptr_t)(L + OFF_Q + wave * 32 * kPRowB + j * 1024));
+            }
+        };
+        if (a.n_qsh == 0) {
+            const unsigned char* qbase = static_cast<const unsigned char*>(a.q) + ((b * Sq) * RH + h_in) * kPD * 2;
+            const uint32_t nrec = Sq > r0 ? (uint32_t)((Sq - 1 - r0) * ld2 + kPD * 2) : 0u;
+            copy_q(qbase + (Sq > r0 ? r0 : 0) * ld2, nrec, 0, 32, true);
+        } else {
+            // queries gathered from the token shards: one pass per shard the
+            // wave's rows touch (two only when a shard length is not a
+            // multiple of 32), rows past Sq read as zero
+            const int64_t r_end = Sq < r0 + 32 ? Sq : r0 + 32;
+            if (r_end < r0 + 32)
+                copy_q(static_cast<const unsigned char*>(a.k), 0u, (int)(r_end > r0 ? r_end - r0 : 0), 32, false);
+            int p = 0;
+            for (int64_t rs = r0; rs < r_end;) {
+                while (a.q_row0[p + 1] <= rs) ++p;
+                const int64_t sp0 = a.q_row0[p], sp = a.q_row0[p + 1] - sp0;
+                const int64_t re = a.q_row0[p + 1] < r_end ? a.q_row0[p + 1] : r_end;
+                const unsigned char* sbase = static_cast<const unsigned char*>(a.q_sh[p]) +
+                                             ((b * sp + (rs - sp0)) * RH + h_in) * kPD * 2;
+                copy_q(sbase, (uint32_t)((re - rs - 1) * ld2 + kPD * 2), (int)(rs - r0), (int)(re - r0),
+                       rs == r0 && re == r0 + 32);
+                rs = re;
+            }
         }
         // stages past the last tile repeat it: the V a fully masked step
         // multiplies by zero must be finite

@@ -131,8 +131,7 @@ SplitPlan plan_split(int64_t n_units, int64_t n_tiles, int n_cu);
 int64_t attn_bf16_units(int64_t B, int64_t H, int64_t Sq);
 
 hipError_t launch_attn_bf16(int D, int o_dtype, const AttnArgs& a, hipStream_t s);
-// D = 128, unmasked, no key split, queries not gathered: the software-pipelined
-// kernel, where its padding to a multiple of six key tiles is small
+// D = 128, unmasked, no key split: the software-pipelined kernel, where its padding to a multiple of six key tiles is small
 bool attn_p32_fits(int64_t Sk, int64_t row_heads);
 hipError_t launch_attn_p32(int o_dtype, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_fp32(int D, const AttnArgs& a, hipStream_t s);
