@@ -654,6 +654,22 @@ def attn_kernel_name(masked, split, sk):
     return "attn_bf16_kernel<128,%s,true,%s>" % ("true" if masked else "false", "true" if split else "false")
 
 
+def attn_kernel_label(share, ring):
+    """The forward kernel(s) the timed attention launches run.  A zigzag
+    chunk whose keys all precede the rank's queries (chunk id below both of
+    its Q chunks) allows every pair, and the library runs it unmasked; the
+    label then counts the launches of each kernel."""
+    if not ring:
+        return attn_kernel_name(False, False, share.ring[0][1] - share.ring[0][0])
+    names = []
+    for c, (a, b) in enumerate(share.kv):
+        masked = share.masks[c] is not None and not (share.chunk is not None and c < min(share.qc))
+        names.append(attn_kernel_name(masked, share.ws[0] is not None and not masked, b - a))
+    if len(set(names)) == 1:
+        return names[0]
+    return " + ".join("%s x%d" % (n, names.count(n)) for n in sorted(set(names), key=names.index))
+
+
 def pmc_probe(args):
     import torch
     torch.cuda.set_device(0)
@@ -983,9 +999,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic() if args.workload == "flux1024" else None,
-                     "kernel": attn_kernel_name(ring and share.masks[0] is not None, share.ws[0] is not None,
-                                                (share.kv[0][1] - share.kv[0][0]) if ring else
-                                                (share.ring[0][1] - share.ring[0][0])),
+                     "kernel": attn_kernel_label(share, ring),
                      "launch_us": round(attn_us, 2), "flops_per_launch": attn_flops_launch},
         "kernels": kernels,
     }

@@ -190,7 +190,9 @@ int uaa_seq2head_permute_multi_ex(int n_tensors, int dir, int rank, int world,
  *   s_j = scale * <q_i, k_j>,  lse = log(sum_{j in J} exp(s_j)),
  *   o   = sum_{j in J} exp(s_j - lse) * v_j,
  * and o = 0, lse = -inf when J is empty (a row with no allowed key, or
- * Sk = 0), so that such a partial drops out of usp_lse_merge.
+ * Sk = 0), so that such a partial drops out of usp_lse_merge.  A mask under
+ * which no key lies after any query in position allows every pair; such a
+ * call runs as the unmasked one, with the same result bit for bit.
  *
  * dtype: UAA_BF16 (bf16 matrix-core products, fp32 accumulation and
  * softmax) or UAA_FP32 (fp32 throughout).  o_dtype: UAA_BF16 or UAA_FP32 for

@@ -7,6 +7,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "internal.h"
@@ -257,6 +258,32 @@ static int device_cu_count()
 
 // Key split the bf16 kernel would use for this problem on the current
 // device with a workspace (p = 1: unsplit).
+// [lo, hi] of the positions of rows [0, n), n >= 1, of a map whose pieces
+// each increase.
+static void host_pos_range(const uaa::PosMap& m, int64_t n, int64_t& lo, int64_t& hi)
+{
+    auto pos = [&](int64_t i) { return i < m.seg_len ? m.base0 + m.stride * i : m.base1 + m.stride * (i - m.seg_len); };
+    if (n <= m.seg_len) {
+        lo = pos(0);
+        hi = pos(n - 1);
+    } else {
+        lo = std::min(pos(0), pos(m.seg_len));
+        hi = std::max(pos(m.seg_len - 1), pos(n - 1));
+    }
+}
+
+// No key of the block lies after any query in position: the mask allows
+// every pair, and the call is an unmasked one (a Ring step over a block
+// wholly in the past of the rank's queries).
+static bool all_pairs_allowed(const uaa::PosMap& q, int64_t Sq, const uaa::PosMap& k, int64_t Sk)
+{
+    if (Sq <= 0 || Sk <= 0) return false;
+    int64_t qlo, qhi, klo, khi;
+    host_pos_range(q, Sq, qlo, qhi);
+    host_pos_range(k, Sk, klo, khi);
+    return khi <= qlo;
+}
+
 static uaa::SplitPlan attn_split_plan(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
                                       const usp_mask* mask)
 {
@@ -355,6 +382,7 @@ static int attn_impl(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, in
         if (rc != UAA_OK) return rc;
         rc = side_map(*mask, false, Sk, a.kmap);
         if (rc != UAA_OK) return rc;
+        if (all_pairs_allowed(a.qmap, Sq, a.kmap, Sk)) a.masked = 0;
     }
     if (dtype == UAA_BF16 && ((double)(Sq > Sk ? Sq : Sk) * RH * D * 2 >= 4294967296.0))
         return fail(UAA_ERR_UNSUPPORTED, "attn: one batch of q or k/v must stay below 4 GiB");
@@ -560,6 +588,7 @@ UAA_EXPORT int usp_attn_bwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t
         if (rc != UAA_OK) return rc;
         rc = side_map(*mask, false, Sk, a.kmap);
         if (rc != UAA_OK) return rc;
+        if (all_pairs_allowed(a.qmap, Sq, a.kmap, Sk)) a.masked = 0;
     }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == UAA_BF16) return hip_status(uaa::launch_attn_bwd_bf16((int)D, a, s), "bwd launch");

@@ -95,3 +95,36 @@ def test_pipelined_rising_maximum():
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.attention(q, k, v, np.float32(scale))
     check_pair(host_f64(o), host_f64(lse), o_ref, l_ref, "bf16", "rising maximum")
+
+
+# A masked call whose keys all precede (or equal) every query in position
+# allows every pair and runs as an unmasked call: bit-identical output.  With
+# one key past the first query (or a plain causal block) the mask stays.
+ALL_ALLOWED = [
+    # name, mask builder, qpos, kpos (Sq = 300, Sk = 384), every pair allowed
+    ("causal_past_block", lambda: uaa.mask_causal(1000, 616), 1000 + np.arange(300), 616 + np.arange(384), True),
+    ("zigzag_past_chunks", lambda: uaa.mask_zigzag(192, [2, 5], [0, 1]),
+     np.concatenate([2 * 192 + np.arange(192), 5 * 192 + np.arange(108)]), np.arange(384), True),
+    ("causal_one_pair_out", lambda: uaa.mask_causal(1000, 618), 1000 + np.arange(300), 618 + np.arange(384), False),
+    ("stripe_world1_causal", lambda: uaa.mask_stripe(1, 0, 0), np.arange(300), np.arange(384), False),
+]
+
+
+@pytest.mark.parametrize("case", ALL_ALLOWED, ids=[c[0] for c in ALL_ALLOWED])
+def test_mask_allowing_every_pair_runs_unmasked(case):
+    name, mk, qpos, kpos, every = case
+    assert every == bool(kpos.max() <= qpos.min())
+    say("attn every pair allowed", name)
+    B, Sq, Sk, H = 1, 300, 384, 2
+    (qb, qv), (kb, kv), (vb, vv) = _inputs(1170, B, Sq, Sk, H)
+    scale = 1.0 / math.sqrt(128)
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    o = torch.empty(B, Sq, H, 128, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty(B, Sq, H, device="cuda", dtype=torch.float32)
+    o_u, lse_u = torch.empty_like(o), torch.empty_like(lse)
+    uaa.usp_attn_fwd_lse(q, k, v, o, lse, scale, mask=mk())
+    uaa.usp_attn_fwd_lse(q, k, v, o_u, lse_u, scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(qv, kv, vv, np.float32(scale), qpos=qpos, kpos=kpos)
+    check_pair(host_f64(o), host_f64(lse), o_ref, l_ref, "bf16", name)
+    assert (torch.equal(o, o_u) and torch.equal(lse, lse_u)) == every, name
