@@ -656,14 +656,16 @@ def attn_kernel_name(masked, split, sk):
 
 def attn_kernel_label(share, ring):
     """The forward kernel(s) the timed attention launches run.  A zigzag
-    chunk whose keys all precede the rank's queries (chunk id below both of
-    its Q chunks) allows every pair, and the library runs it unmasked; the
-    label then counts the launches of each kernel."""
+    K chunk other than the rank's own Q chunks lies wholly in the past or
+    the future of every 256-row unit (the chunk length is a multiple of
+    256), which the pipelined kernel handles; the label then counts the
+    launches of each kernel."""
     if not ring:
         return attn_kernel_name(False, False, share.ring[0][1] - share.ring[0][0])
     names = []
     for c, (a, b) in enumerate(share.kv):
-        masked = share.masks[c] is not None and not (share.chunk is not None and c < min(share.qc))
+        masked = share.masks[c] is not None and not (share.chunk is not None and share.chunk % 256 == 0
+                                                     and c not in share.qc)
         names.append(attn_kernel_name(masked, share.ws[0] is not None and not masked, b - a))
     if len(set(names)) == 1:
         return names[0]

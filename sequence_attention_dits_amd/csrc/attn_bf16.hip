@@ -871,7 +871,7 @@ hipError_t launch_attn_bf16(int D, int o_dtype, const AttnArgs& a0, hipStream_t 
     }
     const int64_t blocks = a.split_p > 1 ? a.n_whole + (units - a.n_whole) * a.split_p : units;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    if (D == 128 && !a.masked && a.split_p <= 1 && attn_p32_fits(a.Sk, a.row_heads) && p32_on())
+    if (D == 128 && a.split_p <= 1 && attn_p32_fits(a.Sk, a.row_heads) && p32_on() && attn_p32_mask_ok(a))
         return launch_attn_p32(o_dtype, a0, s);
     const dim3 grid((unsigned)blocks);
     const bool ob = o_dtype == UAA_BF16;

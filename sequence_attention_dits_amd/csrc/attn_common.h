@@ -12,13 +12,13 @@
 
 namespace uaa {
 
-__device__ __forceinline__ int64_t pos_of(const PosMap& m, int64_t idx)
+__host__ __device__ inline int64_t pos_of(const PosMap& m, int64_t idx)
 {
     return idx < m.seg_len ? m.base0 + m.stride * idx : m.base1 + m.stride * (idx - m.seg_len);
 }
 
 // [min, max] of pos_of over idx in [lo, hi), hi > lo.  Each piece increases.
-__device__ __forceinline__ void pos_range(const PosMap& m, int64_t lo, int64_t hi, int64_t& pmin,
+__host__ __device__ inline void pos_range(const PosMap& m, int64_t lo, int64_t hi, int64_t& pmin,
                                           int64_t& pmax)
 {
     if (hi <= m.seg_len || lo >= m.seg_len) {

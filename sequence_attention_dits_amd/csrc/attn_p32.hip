@@ -208,6 +208,31 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
               (uint32_t)(uintptr_t)(L + off + s * kPTB + (kPWaves * c + wave) * 1024));
     };
 
+    // A masked call runs here only when the rows of every unit see either
+    // every key of the block or none (the block lies wholly in their past or
+    // their future).  A unit that sees none gives O = 0, LSE = -inf, and
+    // continuing a Ring pass leaves (o, lse) as they are.
+    if (a.masked) {
+        const int64_t t0 = qt * kPBM, t1 = t0 + kPBM < Sq ? t0 + kPBM : Sq;
+        int64_t qlo, qhi, klo, khi;
+        pos_range(a.qmap, t0, t1, qlo, qhi);
+        pos_range(a.kmap, 0, Sk, klo, khi);
+        if (klo > qhi) {
+            if (!a.acc) {
+                constexpr int C = (OUT_BF16 ? 2 : 4) * kPD / 16;   // 16-byte pieces per output row
+                for (int j = lane; j < 32 * C; j += 64) {
+                    const int64_t row = r0 + j / C;
+                    if (row < Sq)
+                        *reinterpret_cast<p_u32x4*>(static_cast<unsigned char*>(a.o) +
+                                                    ((b * Sq + row) * H + hh) * (C * 16) + (j % C) * 16) =
+                            p_u32x4{0u, 0u, 0u, 0u};
+                }
+                if (hg == 0 && i < Sq) a.lse[(b * Sq + i) * H + hh] = -INFINITY;
+            }
+            return;
+        }
+    }
+
     // ---- prologue: Q (this wave's 32 rows), K0..K2, V0..V1 ----------------
     if (n > 0) {
         // rows [lo, hi) of the wave's 32 (all: every row, the rest reading as
@@ -636,6 +661,20 @@ bool attn_p32_fits(int64_t Sk, int64_t row_heads)
     const int64_t n = (Sk + kPBN - 1) / kPBN;
     const int64_t pad = (6 - n % 6) % 6;
     return n > 0 && Sk * row_heads * kPD * 2 < (int64_t)0xF0000000 && pad * 10 <= n;
+}
+
+bool attn_p32_mask_ok(const AttnArgs& a)
+{
+    if (!a.masked) return true;
+    if (a.Sq <= 0 || a.Sk <= 0) return false;
+    int64_t klo, khi;
+    pos_range(a.kmap, 0, a.Sk, klo, khi);
+    for (int64_t t0 = 0; t0 < a.Sq; t0 += kPBM) {
+        int64_t qlo, qhi;
+        pos_range(a.qmap, t0, t0 + kPBM < a.Sq ? t0 + kPBM : a.Sq, qlo, qhi);
+        if (!(khi <= qlo || klo > qhi)) return false;   // this unit holds a diagonal
+    }
+    return true;
 }
 
 hipError_t launch_attn_p32(int o_dtype, const AttnArgs& a0, hipStream_t s)

@@ -128,3 +128,41 @@ def test_mask_allowing_every_pair_runs_unmasked(case):
     o_ref, l_ref = oracle.attention(qv, kv, vv, np.float32(scale), qpos=qpos, kpos=kpos)
     check_pair(host_f64(o), host_f64(lse), o_ref, l_ref, "bf16", name)
     assert (torch.equal(o, o_u) and torch.equal(lse, lse_u)) == every, name
+
+
+def _zigzag_pos(C, ids, n):
+    return np.concatenate([c * C + np.arange(C) for c in ids])[:n]
+
+
+# Masked calls in which every 256-row unit sees every key of the block or
+# none: zigzag chunks of 768 rows (three units each), K chunk 2 in the future
+# of Q chunk 1 and in the past of Q chunk 4.  Units that see nothing give
+# (0, -inf); a Ring pass continued over such a block keeps its rows.
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_units_all_or_nothing(out):
+    C, H = 768, 2
+    say("attn units all or nothing", out)
+    (qb, qv), (kb, kv), (vb, vv) = _inputs(1180, 1, 2 * C, 2 * C, H)
+    scale = 1.0 / math.sqrt(128)
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    qpos = _zigzag_pos(C, [1, 4], 2 * C)
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    o = torch.full((1, 2 * C, H, 128), 7.0, device="cuda", dtype=dt)
+    lse = torch.full((1, 2 * C, H), 7.0, device="cuda", dtype=torch.float32)
+    # K chunk 2 alone: rows of Q chunk 1 see nothing, rows of Q chunk 4 all
+    uaa.usp_attn_fwd_lse(q, k[:, :C].contiguous(), v[:, :C].contiguous(), o, lse, scale,
+                         mask=uaa.mask_zigzag(C, [1, 4], [2]))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(qv, kv[:, :C], vv[:, :C], np.float32(scale), qpos=qpos,
+                                    kpos=_zigzag_pos(C, [2], C))
+    assert np.isneginf(l_ref[0, :C]).all() and np.isfinite(l_ref[0, C:]).all()
+    check_pair(host_f64(o), host_f64(lse), o_ref, l_ref, "bf16", "chunk 2 " + out)
+    # a Ring pass: K chunk 0 (every pair allowed), then K chunk 2 merged in
+    uaa.usp_attn_fwd_lse(q, k[:, C:].contiguous(), v[:, C:].contiguous(), o, lse, scale,
+                         mask=uaa.mask_zigzag(C, [1, 4], [0]))
+    uaa.usp_attn_fwd_lse(q, k[:, :C].contiguous(), v[:, :C].contiguous(), o, lse, scale,
+                         mask=uaa.mask_zigzag(C, [1, 4], [2]), accumulate=True)
+    torch.cuda.synchronize()
+    kpos = np.concatenate([_zigzag_pos(C, [2], C), _zigzag_pos(C, [0], C)])
+    o_ref, l_ref = oracle.attention(qv, kv, vv, np.float32(scale), qpos=qpos, kpos=kpos)
+    check_pair(host_f64(o), host_f64(lse), o_ref, l_ref, "bf16", "ring pass " + out)
