@@ -725,9 +725,9 @@ def pmc_summary(fetch_dir, write_dir, workload):
         "%s step (Sq=%d, Sk=%d, %d heads, D=%d)" % (workload, sq, sk, Hr, c["D"]),
         "",
         "commands (run from the repository root on one MI355X):",
-        "  rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o pmc --output-format csv -- python3 bench.py --pmc-probe",
-        "  rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o pmc --output-format csv -- python3 bench.py --pmc-probe",
-        "  python3 bench.py --pmc-summary gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        "  rocprofv3 --pmc FETCH_SIZE -d %s -o pmc --output-format csv -- python3 bench.py --pmc-probe" % fetch_dir,
+        "  rocprofv3 --pmc WRITE_SIZE -d %s -o pmc --output-format csv -- python3 bench.py --pmc-probe" % write_dir,
+        "  python3 bench.py --pmc-summary %s %s" % (fetch_dir, write_dir),
         "",
         "calibration: plain device copy of %d bytes" % PMC_COPY_BYTES,
         "  FETCH_SIZE %.1f KiB per copy -> scale %.4f;  WRITE_SIZE %.1f KiB per copy -> scale %.4f"
