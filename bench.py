@@ -86,6 +86,16 @@ OVERLAP_WORKLOADS = ("longctx",)
 ACC_WORKLOADS = ("flux1024", "flux1008")
 
 
+def make_share(workload: str, n_sets: int, overlap_chunks: str = "auto", ring_update: str = "auto"):
+    """The device buffers and launches of one workload's step, in the launch
+    configuration the bench times by default ("auto": the per-workload
+    stream overlap and Ring-step update above)."""
+    cfg_id, _ = WORKLOADS[workload]
+    overlap = {"on": True, "off": False}.get(overlap_chunks, workload in OVERLAP_WORKLOADS)
+    ring_acc = {"acc": True, "merge": False}.get(ring_update, workload in ACC_WORKLOADS)
+    return (RingShare if workload in RING_WORKLOADS else Share)(cfg_id, n_sets, overlap, ring_acc)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -178,8 +188,14 @@ class Share:
             torch, bf = self.torch, self.torch.bfloat16
             B, S, Hr, D, H = self.B, self.S, self.Hr, self.D, self.H
             S0 = self.seq_off[1]
+            qh = {n: torch.empty(B, S, Hr, D, device="cuda", dtype=bf) for n in "qkv"}
+            # the set's gathered Q, K, V hold the real gathered inputs: the
+            # attention timing reads them (cold, like the HBM-bound timings)
+            d = self.sets[s]
+            self.uaa.uaa_seq2head_permute_multi(self.uaa.UAA_SEQ2HEAD, 0, [d[n] for n in "qkv"],
+                                                [qh[n] for n in "qkv"], self.seq_off, self.head_off)
             self._tbufs[s] = {
-                "qh": {n: torch.empty(B, S, Hr, D, device="cuda", dtype=bf) for n in "qkv"},
+                "qh": qh,
                 "o_part": [torch.randn(B, S, Hr, D, device="cuda").to(bf) for _ in self.ring],
                 "l_part": [8 + torch.randn(B, S, Hr, device="cuda") for _ in self.ring],
                 "o": torch.randn(B, S, Hr, D, device="cuda").to(bf),
@@ -229,11 +245,11 @@ class Share:
             return 1
         if name == "attn":
             for c in range(len(self.kc)):
-                self.attn_chunk(s, c, self.ws[0])
+                self.attn_chunk(s, c, self.ws[0], bufs=t)
             return len(self.kc)
         if name == "attn_acc":   # the accumulating launches of a Ring-step-update pass
             for c in range(1, len(self.kc)):
-                self.attn_chunk(s, c, self.ws[0], acc=True)
+                self.attn_chunk(s, c, self.ws[0], acc=True, bufs=t)
             return len(self.kc) - 1
         if name == "merge":
             uaa.usp_lse_merge(o_part, l_part, o, lse)
@@ -255,12 +271,19 @@ class Share:
     kernel_names = ("permute", "permute_qkv", "attn", "attn_acc", "merge", "head2seq", "head2seq_lse",
                     "head2seq_o_lse")
 
-    def attn_chunk(self, s, c, ws, acc=False):
+    def attn_chunk(self, s, c, ws, acc=False, bufs=None):
         """Chunk c's attention into its partial buffers, or with acc into the
-        running (o, lse): chunk 0 writes it, later chunks merge into it."""
-        kc, vc = self.kc[c]
-        o, l = (self.o, self.lse) if acc else (self.o_part[c], self.l_part[c])
-        self.uaa.usp_attn_fwd_lse(self.qh["q"], _contig(kc), _contig(vc), o, l, self.scale, workspace=ws,
+        running (o, lse): chunk 0 writes it, later chunks merge into it.
+        With bufs (timing_bufs of set s) every tensor is the set's own."""
+        if bufs is None:
+            qh, (kc, vc) = self.qh, self.kc[c]
+            o, l = (self.o, self.lse) if acc else (self.o_part[c], self.l_part[c])
+        else:
+            a, b = self.ring[c]
+            qh = bufs["qh"]
+            kc, vc = qh["k"][:, a:b], qh["v"][:, a:b]
+            o, l = (bufs["o"], bufs["lse"]) if acc else (bufs["o_part"][c], bufs["l_part"][c])
+        self.uaa.usp_attn_fwd_lse(qh["q"], _contig(kc), _contig(vc), o, l, self.scale, workspace=ws,
                                   accumulate=acc and c > 0)
 
     def result(self):
@@ -421,14 +444,14 @@ class RingShare:
 
     def launch_one(self, name, s, timing=False):
         uaa = self.uaa
-        d = self.sets[s]
+        t = self.timing_bufs(s) if timing else None
         if name == "attn":
             for c in range(len(self.kv)):
-                self.attn_chunk(s, c, self.ws[0])
+                self.attn_chunk(s, c, self.ws[0], into=(t["o_part"][c], t["l_part"][c]) if timing else None)
             return len(self.kv)
         if name == "attn_acc":
             for c in range(1, len(self.kv)):
-                self.attn_chunk(s, c, self.ws[0], acc=True)
+                self.attn_chunk(s, c, self.ws[0], acc=True, into=(t["o"], t["lse"]) if timing else None)
             return len(self.kv) - 1
         if name == "merge":
             if timing:
@@ -439,17 +462,19 @@ class RingShare:
             return 1
         raise ValueError(name)
 
-    def attn_chunk(self, s, c, ws, acc=False, into=None):
-        """Chunk c's attention into its partial buffers, or with acc into the
-        running (O, LSE) `into` (default: the result), merging unless c is
-        the first chunk accumulated there."""
+    def attn_chunk(self, s, c, ws, acc=False, into=None, first=None):
+        """Chunk c's attention into (O, LSE) `into` (default: its partial
+        buffers, or with acc the result); with acc it is merged into what
+        `into` holds unless this is the first chunk accumulated there (first;
+        default: c == 0)."""
         d = self.sets[s]
         a, b = self.kv[c]
-        if acc:
-            o, l = into if into is not None else (self.o, self.lse)
+        if into is not None:
+            o, l = into
         else:
-            o, l = self.o_part[c], self.l_part[c]
-        first = c == 0 if into is None else c < 2
+            o, l = (self.o, self.lse) if acc else (self.o_part[c], self.l_part[c])
+        if first is None:
+            first = c == 0
         self.uaa.usp_attn_fwd_lse(d["q"], d["k"][:, a:b], d["v"][:, a:b], o, l, self.scale, self.masks[c],
                                   workspace=ws, accumulate=acc and not first)
 
@@ -461,7 +486,7 @@ class RingShare:
             # two running results, one per stream (chunks alternate), then
             # the 2-way merge of the two
             runs = [(self.o_part[0], self.l_part[0]), (self.o_part[1], self.l_part[1])]
-            chunks = [lambda w, c=c: self.attn_chunk(s, c, w, acc=True, into=runs[c % 2])
+            chunks = [lambda w, c=c: self.attn_chunk(s, c, w, acc=True, into=runs[c % 2], first=c < 2)
                       for c in range(len(self.kv))]
             _two_streams(torch, torch.cuda.current_stream(), self.side, chunks, self.ws)
             self.uaa.usp_lse_merge([r[0] for r in runs], [r[1] for r in runs], self.o, self.lse)
@@ -491,6 +516,8 @@ def ring_cpu_baseline(share: "RingShare", target_s: float):
     oracle.build(force=False)
     h = share.host
 
+    res = {}
+
     def run(rows):
         t = time.perf_counter()
         parts = []
@@ -500,7 +527,7 @@ def ring_cpu_baseline(share: "RingShare", target_s: float):
                 qpos, kpos = h["q_rows"], np.arange(a, b)
             parts.append(oracle.attention(h["q"], h["k"][:, a:b], h["v"][:, a:b], share.scale, qpos=qpos,
                                           kpos=kpos, rows=rows))
-        oracle.lse_merge([p[0] for p in parts], [p[1] for p in parts])
+        res["o"], res["lse"] = oracle.lse_merge([p[0] for p in parts], [p[1] for p in parts])
         return time.perf_counter() - t
 
     n = 8
@@ -511,6 +538,7 @@ def ring_cpu_baseline(share: "RingShare", target_s: float):
         n = min(share.Sq, int(n * max(2.0, min(8.0, target_s / max(elapsed, 1e-3) / 2))))
         rows = np.sort(rng.choice(share.Sq, n, replace=False))
         elapsed = run(rows)
+    o_gpu, l_gpu = _step_result_rows(share, share.o, share.lse, rows)
     # the sample's share of the allowed pairs
     if share.masks[0] is None:
         pairs = float(n) * sum(b - a for a, b in share.kv)
@@ -518,9 +546,35 @@ def ring_cpu_baseline(share: "RingShare", target_s: float):
         qpos = h["q_rows"][rows]
         pairs = float(sum(np.searchsorted(np.arange(a, b), qpos, side="right").sum() for a, b in share.kv))
     flops = 4.0 * share.D * share.H * pairs
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d of %d query rows x %d heads against all %d K/V chunks + %d-way merge, fp64; %.1f s"
-                      % (n, share.Sq, share.H, len(share.kv), len(share.kv), elapsed)}
+    out = {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": "%d of %d query rows x %d heads against all %d K/V chunks + %d-way merge, fp64; %.1f s"
+                     % (n, share.Sq, share.H, len(share.kv), len(share.kv), elapsed)}
+    out.update(_parity(o_gpu, l_gpu, res["o"], res["lse"], n))
+    return out
+
+
+def _step_result_rows(share, o, lse, rows):
+    """Rows `rows` (flat tokens of batch 0) of one fresh eager step's (O, LSE)
+    on input set 0, as float64 host arrays [n, H, D] and [n, H]."""
+    torch = share.torch
+    share.step(0)
+    torch.cuda.synchronize()
+    idx = torch.as_tensor(rows, device=o.device)
+    return (o[0].index_select(0, idx).float().cpu().numpy().astype("float64"),
+            lse[0].index_select(0, idx).cpu().numpy().astype("float64"))
+
+
+def _parity(o_gpu, l_gpu, o_ref, l_ref, n_rows):
+    """Largest errors of the GPU step's rows against the oracle's, and
+    whether they are inside the bf16 tolerances (O 2e-2, LSE 1e-3 max-abs;
+    rows without a key exactly (0, -inf))."""
+    import numpy as np
+    empty = np.isneginf(l_ref)
+    same_empty = bool(np.array_equal(np.isneginf(l_gpu), empty) and (o_gpu[empty] == 0).all())
+    o_err = float(np.abs(o_gpu - o_ref).max())
+    l_err = float(np.abs(l_gpu[~empty] - l_ref[~empty]).max()) if (~empty).any() else 0.0
+    return {"parity_rows": int(n_rows), "max_abs_err_o": o_err, "max_abs_err_lse": l_err,
+            "parity_ok": bool(same_empty and o_err <= 2e-2 and l_err <= 1e-3)}
 
 
 def backward_variant(share, cfg_id: int, steps: int, warmup: int) -> dict:
@@ -599,25 +653,32 @@ def cpu_baseline(share: "Share", target_s: float):
         heads[name] = oracle.seq2head(shards, 0, share.seq_off, share.head_off)
     t_perm = time.perf_counter() - t0
 
+    res = {}
+
     def run(rows):
         t = time.perf_counter()
         parts = [oracle.attention(heads["q"], heads["k"][:, a:b], heads["v"][:, a:b], share.scale, rows=rows)
                  for a, b in share.ring]
-        oracle.lse_merge([p[0] for p in parts], [p[1] for p in parts])
+        res["o"], res["lse"] = oracle.lse_merge([p[0] for p in parts], [p[1] for p in parts])
         return time.perf_counter() - t
 
     n = 16
     rng = np.random.default_rng(0)
-    elapsed = run(np.sort(rng.choice(S, n, replace=False)))
+    rows = np.sort(rng.choice(S, n, replace=False))
+    elapsed = run(rows)
     while elapsed < target_s / 4 and n < S:
         n = min(S, int(n * max(2.0, min(8.0, target_s / max(elapsed, 1e-3) / 2))))
-        elapsed = run(np.sort(rng.choice(S, n, replace=False)))
+        rows = np.sort(rng.choice(S, n, replace=False))
+        elapsed = run(rows)
     # the gather of the whole tensors is pro-rated to the sampled rows
     t_total = elapsed + t_perm * (n / S)
     flops = 4.0 * D * Hr * n * S
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d of %d query rows x %d heads over all %d keys (2 Ring chunks + merge), fp64, "
-                      "plus the Ulysses gather of Q/K/V pro-rated; %.1f s" % (n, S, Hr, S, t_total)}
+    o_gpu, l_gpu = _step_result_rows(share, share.o, share.lse, rows)
+    out = {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": "%d of %d query rows x %d heads over all %d keys (2 Ring chunks + merge), fp64, "
+                     "plus the Ulysses gather of Q/K/V pro-rated; %.1f s" % (n, S, Hr, S, t_total)}
+    out.update(_parity(o_gpu, l_gpu, res["o"], res["lse"], n))
+    return out
 
 
 # ---- HBM traffic of the attention kernel (rocprofv3 counters) ---------------
@@ -837,9 +898,7 @@ def main():
     else:
         per_set = 3 * c["B"] * c["S"] * c["H"] * c["D"] * 2 + c["B"] * c["S"] * (c["H"] // 2) * c["D"] * 2
     n_sets = args.sets or max(2, int(math.ceil((1 << 30) / per_set)))
-    overlap = {"on": True, "off": False}.get(args.overlap_chunks, args.workload in OVERLAP_WORKLOADS)
-    ring_acc = {"acc": True, "merge": False}.get(args.ring_update, args.workload in ACC_WORKLOADS)
-    share = (RingShare if ring else Share)(cfg_id, n_sets, overlap, ring_acc)
+    share = make_share(args.workload, n_sets, args.overlap_chunks, args.ring_update)
 
     for i in range(max(args.warmup, 1)):
         share.step(i % n_sets)

@@ -99,6 +99,23 @@ typedef struct usp_mask {
 } usp_mask;
 
 /*
+ * uaa_split_offsets -- the default split of `total` items (tokens or heads)
+ * over `parts` ranks as exclusive prefix sums: off[0] = 0, off[p+1] =
+ * off[p] + n_p with n_p = ceil(total / parts) for the first total mod parts
+ * ranks and floor(total / parts) for the rest ([UAA] and [CP] "Ulysses
+ * Anything Attention": any length is split without padding; the first
+ * ranks take the extra token, so 257 -> 129 / 128 and 4481 -> 2241 / 2240).
+ * The permute and gathering-attention calls use this split for the heads
+ * when they are given head_off = NULL.
+ *
+ *   off  host array of parts + 1 entries, written (owned by the caller).
+ * parts >= 1, total >= 0 (else UAA_ERR_INVALID_ARG, off untouched).  Host
+ * only: no device work, callable without a GPU.
+ * Returns UAA_OK or UAA_ERR_INVALID_ARG.
+ */
+int uaa_split_offsets(int64_t total, int parts, int64_t* off);
+
+/*
  * uaa_seq2head_permute -- the local data movement of the Ulysses all-to-all
  * for one rank, run as a gather ([CP] "Ulysses Attention": the first
  * exchange leaves every GPU all tokens of a subset of heads, the second
@@ -290,6 +307,24 @@ int usp_attn_fwd_lse_gather(int dtype, int world, int rank, const int64_t* seq_o
                             const void* const* k_shards, const void* const* v_shards, int k_shard, void* o,
                             int o_dtype, float* lse, float scale, const usp_mask* mask, void* workspace,
                             size_t workspace_bytes, int accumulate, void* stream);
+
+/*
+ * usp_attn_kernel -- which forward kernel usp_attn_fwd_lse(_ws, _acc) would
+ * run for this problem on the current device, for profiling and for tests
+ * that must know the kernel they cover.  Host only: nothing is launched and
+ * no pointer is needed; a workspace counts as given when workspace_bytes >
+ * 0 (enough bytes: see usp_attn_workspace_bytes).  Returns one of the codes
+ * below, or UAA_ERR_INVALID_ARG / UAA_ERR_UNSUPPORTED for arguments the
+ * call itself would reject (as usp_attn_fwd_lse, pointers aside).
+ */
+#define USP_KERNEL_NONE 0            /* no work (B, H or Sq = 0) */
+#define USP_KERNEL_FP32 1            /* fp32 input: the fp32 kernel */
+#define USP_KERNEL_GENERAL 2         /* bf16, every key allowed: the general kernel */
+#define USP_KERNEL_GENERAL_MASKED 3  /* bf16, a mask with units on its diagonal: the general kernel */
+#define USP_KERNEL_GENERAL_SPLIT 4   /* bf16, keys of the last round's units split: the general kernel */
+#define USP_KERNEL_PIPELINED 5       /* bf16, D = 128: the software-pipelined kernel */
+int usp_attn_kernel(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, int o_dtype,
+                    const usp_mask* mask, size_t workspace_bytes);
 
 /*
  * usp_attn_workspace_bytes -- device workspace usp_attn_fwd_lse_ws uses for

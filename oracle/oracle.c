@@ -238,12 +238,12 @@ int orc_attention(int64_t B, int64_t Sq, int64_t Sk, int64_t H, int64_t D,
 /*
  * Merge of N partial (O, LSE) pairs of the same query rows, each computed
  * over a disjoint set of keys ([USP] review thread: the Ring loop folds each
- * step's (out, lse) into the running pair, in fp32).  The pages' pairwise
- * update, with sigma the logistic function,
- *     out = prev_out - sigma(lse - prev_lse) * (prev_out - out)
- *     lse = prev_lse - logsigma(prev_lse - lse)
- * is, for finite inputs, the softmax-weighted mean of the partials with
- * lse = log(exp(prev_lse) + exp(lse)).  Written out for N partials, with the
+ * step's (out, lse) into the running pair, in fp32).  Each such pairwise
+ * update weights the running output and the new one by the logistic
+ * function of their LSE difference, and sets the LSE to the log of the sum
+ * of the two exponentials: for finite inputs, the softmax-weighted mean of
+ * the partials with lse = log(exp(prev_lse) + exp(lse)).  Written out for N
+ * partials, with the
  * maximum shifted out so that -inf partials (rows with no allowed key) add
  * nothing instead of producing NaN:
  *     M   = max_n LSE_n

@@ -35,6 +35,12 @@ USP_MASK_FULL = 0
 USP_MASK_CAUSAL = 1
 USP_MASK_ZIGZAG = 2
 USP_MASK_STRIPE = 3
+USP_KERNEL_NONE = 0
+USP_KERNEL_FP32 = 1
+USP_KERNEL_GENERAL = 2
+USP_KERNEL_GENERAL_MASKED = 3
+USP_KERNEL_GENERAL_SPLIT = 4
+USP_KERNEL_PIPELINED = 5
 
 _c_i64 = ctypes.c_int64
 _c_p = ctypes.c_void_p
@@ -130,6 +136,11 @@ def lib() -> ctypes.CDLL:
         l.usp_attn_bwd.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p,
                                    _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_int, ctypes.c_float,
                                    ctypes.POINTER(usp_mask), ctypes.c_int, _c_p]
+        l.usp_attn_kernel.restype = ctypes.c_int
+        l.usp_attn_kernel.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int,
+                                      ctypes.POINTER(usp_mask), ctypes.c_size_t]
+        l.uaa_split_offsets.restype = ctypes.c_int
+        l.uaa_split_offsets.argtypes = [_c_i64, ctypes.c_int, _c_p]
         l.uaa_last_error.restype = ctypes.c_char_p
         l.uaa_last_error.argtypes = []
         l.uaa_abi_version.restype = ctypes.c_int
@@ -166,6 +177,24 @@ def _i64_array(vals):
     return (ctypes.c_int64 * len(vals))(*[int(x) for x in vals])
 
 
+def uaa_split_offsets(total: int, parts: int) -> list:
+    """The library's default split of `total` items over `parts` ranks, as
+    exclusive prefix sums (uaa_split_offsets): what the permute and the
+    gathering attention use for the heads when head_off is None."""
+    off = (ctypes.c_int64 * (parts + 1))() if parts >= 1 else None
+    _check(lib().uaa_split_offsets(int(total), int(parts), off))
+    return [int(x) for x in off]
+
+
+def _head_offsets(head_off, H, world):
+    """(offsets used for the shape checks, array handed to the library):
+    with head_off None the library splits the heads itself (NULL is passed),
+    and the checks use the split it reports."""
+    if head_off is None:
+        return uaa_split_offsets(H, world), None
+    return [int(x) for x in head_off], _i64_array(head_off)
+
+
 def _permute_shapes(direction, rank, src, dst, seq_off, head_off):
     """Check one tensor's shard shapes against the offsets; returns (B, H, D, head offsets)."""
     world = len(src)
@@ -186,13 +215,7 @@ def _permute_shapes(direction, rank, src, dst, seq_off, head_off):
         H = dst.shape[2]
     else:
         raise ValueError("direction must be UAA_SEQ2HEAD or UAA_HEAD2SEQ")
-    if head_off is None:
-        base, extra = divmod(H, world)
-        hoff = [0]
-        for p in range(world):
-            hoff.append(hoff[-1] + base + (1 if p < extra else 0))
-    else:
-        hoff = [int(x) for x in head_off]
+    hoff, harg = _head_offsets(head_off, H, world)
     if len(hoff) != world + 1:
         raise ValueError("head_off needs world+1 entries")
     if direction == UAA_SEQ2HEAD:
@@ -207,7 +230,7 @@ def _permute_shapes(direction, rank, src, dst, seq_off, head_off):
                 raise ValueError("src[%d] shape %s does not match the offsets" % (r, tuple(x.shape)))
         if tuple(dst.shape) != (B, seq_off[rank + 1] - seq_off[rank], H, D):
             raise ValueError("dst shape %s does not match the offsets" % (tuple(dst.shape),))
-    return B, H, D, hoff
+    return B, H, D, harg
 
 
 def uaa_seq2head_permute(direction: int, rank: int, src: Sequence[torch.Tensor], dst: torch.Tensor,
@@ -218,10 +241,10 @@ def uaa_seq2head_permute(direction: int, rank: int, src: Sequence[torch.Tensor],
     HEAD2SEQ: src[r] [B,S,H_r,D] -> dst [B,S_p,H,D] for token rank `rank`.
     Any element dtype; bits are copied unchanged.
     """
-    B, H, D, hoff = _permute_shapes(direction, rank, src, dst, seq_off, head_off)
+    B, H, D, harg = _permute_shapes(direction, rank, src, dst, seq_off, head_off)
     ptrs = (ctypes.c_void_p * len(src))(*[x.data_ptr() if x.numel() else 0 for x in src])
     _check(lib().uaa_seq2head_permute(direction, rank, len(src), _i64_array(seq_off),
-                                      _i64_array(hoff), B, H, D, dst.element_size(), ptrs,
+                                      harg, B, H, D, dst.element_size(), ptrs,
                                       dst.data_ptr() if dst.numel() else 0, _stream(dst)))
 
 
@@ -240,19 +263,19 @@ def uaa_seq2head_permute_multi(direction: int, rank: int, srcs: Sequence[Sequenc
         shapes.append(_permute_shapes(direction, rank, src, dst, seq_off, head_off))
         if (shapes[-1][0], shapes[-1][1], shapes[-1][3]) != (shapes[0][0], shapes[0][1], shapes[0][3]):
             raise ValueError("all tensors of one call must share B, H and the offsets")
-    B, H, D, hoff = shapes[0]
+    B, H, D, harg = shapes[0]
     flat = [x for src in srcs for x in src]
     ptrs = (ctypes.c_void_p * len(flat))(*[x.data_ptr() if x.numel() else 0 for x in flat])
     dptrs = (ctypes.c_void_p * len(dsts))(*[d.data_ptr() if d.numel() else 0 for d in dsts])
     if all(sh[2] == D for sh in shapes) and all(d.dtype == dsts[0].dtype for d in dsts):
         _check(lib().uaa_seq2head_permute_multi(len(dsts), direction, rank, len(srcs[0]), _i64_array(seq_off),
-                                                _i64_array(hoff), B, H, D, dsts[0].element_size(), ptrs, dptrs,
+                                                harg, B, H, D, dsts[0].element_size(), ptrs, dptrs,
                                                 _stream(dsts[0])))
         return
     Ds = _i64_array([sh[2] for sh in shapes])
     elems = (ctypes.c_int * len(dsts))(*[d.element_size() for d in dsts])
     _check(lib().uaa_seq2head_permute_multi_ex(len(dsts), direction, rank, len(srcs[0]), _i64_array(seq_off),
-                                               _i64_array(hoff), B, H, Ds, elems, ptrs, dptrs, _stream(dsts[0])))
+                                               harg, B, H, Ds, elems, ptrs, dptrs, _stream(dsts[0])))
 
 
 def attn_workspace(q: torch.Tensor, k: torch.Tensor, mask: Optional[usp_mask] = None) -> Optional[torch.Tensor]:
@@ -267,6 +290,19 @@ def attn_workspace(q: torch.Tensor, k: torch.Tensor, mask: Optional[usp_mask] = 
     if n == 0:
         return None
     return torch.zeros(n, dtype=torch.uint8, device=q.device)
+
+
+def usp_attn_kernel(q_shape, sk: int, dtype: torch.dtype = torch.bfloat16, o_dtype: Optional[torch.dtype] = None,
+                    mask: Optional[usp_mask] = None, workspace_bytes: int = 0) -> int:
+    """USP_KERNEL_* code of the forward kernel a usp_attn_fwd_lse call with
+    queries of shape q_shape [B, Sq, H, D] and sk keys would run (host only)."""
+    B, Sq, H, D = (int(x) for x in q_shape)
+    m = mask if mask is not None else mask_full()
+    r = lib().usp_attn_kernel(_code(dtype, "dtype"), B, H, Sq, int(sk), D, _code(o_dtype or dtype, "o_dtype"),
+                              ctypes.byref(m), int(workspace_bytes))
+    if r < 0:
+        _check(r)
+    return r
 
 
 def usp_attn_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
@@ -356,13 +392,9 @@ def usp_attn_fwd_lse_gather(rank: int, q_shards: Sequence[torch.Tensor], k_shard
         for t in (q_shards[p], k_shards[p], v_shards[p]):
             if tuple(t.shape) != (B, Sp, H, D):
                 raise ValueError("shard %d shape %s does not match the offsets" % (p, tuple(t.shape)))
-    if head_off is None:
-        base, extra = divmod(H, world)
-        hoff = [0]
-        for p in range(world):
-            hoff.append(hoff[-1] + base + (1 if p < extra else 0))
-    else:
-        hoff = [int(x) for x in head_off]
+    hoff, harg = _head_offsets(head_off, H, world)
+    if len(hoff) != world + 1:
+        raise ValueError("head_off needs world+1 entries")
     Hr = hoff[rank + 1] - hoff[rank]
     _dev(o, "o")
     _dev(lse, "lse")
@@ -374,7 +406,7 @@ def usp_attn_fwd_lse_gather(rank: int, q_shards: Sequence[torch.Tensor], k_shard
         _dev(workspace, "workspace")
         ws_ptr, ws_n = workspace.data_ptr(), workspace.numel()
     ptrs = lambda ts: (ctypes.c_void_p * world)(*[t.data_ptr() if t.numel() else 0 for t in ts])
-    _check(lib().usp_attn_fwd_lse_gather(UAA_BF16, world, rank, _i64_array(seq_off), _i64_array(hoff), B, H, D,
+    _check(lib().usp_attn_fwd_lse_gather(UAA_BF16, world, rank, _i64_array(seq_off), harg, B, H, D,
                                          ptrs(q_shards), ptrs(k_shards), ptrs(v_shards), k_shard, o.data_ptr(),
                                          _code(o.dtype, "o"), lse.data_ptr(), float(scale), ctypes.byref(m),
                                          ws_ptr, ws_n, 1 if accumulate else 0, _stream(o)))

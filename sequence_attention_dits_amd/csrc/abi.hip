@@ -52,6 +52,15 @@ UAA_EXPORT const char* uaa_last_error(void) { return g_err; }
 
 UAA_EXPORT int uaa_abi_version(void) { return 1; }
 
+UAA_EXPORT int uaa_split_offsets(int64_t total, int parts, int64_t* off)
+{
+    if (parts < 1) return fail(UAA_ERR_INVALID_ARG, "split: parts must be >= 1, got %d", parts);
+    if (total < 0) return fail(UAA_ERR_INVALID_ARG, "split: total must be >= 0, got %lld", (long long)total);
+    if (off == nullptr) return fail(UAA_ERR_INVALID_ARG, "split: off is NULL");
+    even_split(total, parts, off);
+    return UAA_OK;
+}
+
 namespace {
 
 // Shared by the permute entry points; Ds[t], elems[t]: features and element
@@ -318,10 +327,14 @@ struct GatherSrc {
     int64_t row_heads, head0;
 };
 
+// Validates the call, builds the kernel arguments and launches.  With
+// `kernel` non-null nothing is launched and the pointers are not checked:
+// the USP_KERNEL_* code of the kernel the call would run is stored there (a
+// workspace counts as given when workspace_bytes > 0).
 static int attn_impl(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, const void* q,
                      const void* k, const void* v, void* o, int o_dtype, float* lse, float scale,
                      const usp_mask* mask, void* workspace, size_t workspace_bytes, int acc, const GatherSrc* g,
-                     void* stream)
+                     void* stream, int* kernel = nullptr)
 {
     if (dtype != UAA_BF16 && dtype != UAA_FP32)
         return fail(UAA_ERR_INVALID_ARG, "attn: dtype must be UAA_BF16 or UAA_FP32, got %d", dtype);
@@ -339,15 +352,20 @@ static int attn_impl(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, in
     const int64_t RH = g != nullptr ? g->row_heads : H;   // heads per input token
     if ((double)B * (Sq > Sk ? Sq : Sk) * RH * D > (double)kMaxElems)
         return fail(UAA_ERR_INVALID_ARG, "attn: tensor too large");
-    if (B == 0 || H == 0 || Sq == 0) return UAA_OK;
-    if ((g == nullptr && q == nullptr) || o == nullptr || lse == nullptr)
+    if (B == 0 || H == 0 || Sq == 0) {
+        if (kernel != nullptr) *kernel = USP_KERNEL_NONE;
+        return UAA_OK;
+    }
+    const bool query = kernel != nullptr;   // the plan only looks at sizes, dtypes and the mask
+    if (!query && ((g == nullptr && q == nullptr) || o == nullptr || lse == nullptr))
         return fail(UAA_ERR_INVALID_ARG, "attn: q, o and lse must not be NULL");
-    if (Sk > 0 && (k == nullptr || v == nullptr))
+    if (!query && Sk > 0 && (k == nullptr || v == nullptr))
         return fail(UAA_ERR_INVALID_ARG, "attn: k and v must not be NULL when Sk > 0");
-    if ((g == nullptr && !aligned(q, 16)) || !aligned(o, 16) || (Sk > 0 && (!aligned(k, 16) || !aligned(v, 16))))
+    if (!query &&
+        ((g == nullptr && !aligned(q, 16)) || !aligned(o, 16) || (Sk > 0 && (!aligned(k, 16) || !aligned(v, 16)))))
         return fail(UAA_ERR_INVALID_ARG, "attn: q, k, v and o must be 16-byte aligned");
-    if (!aligned(lse, 4)) return fail(UAA_ERR_INVALID_ARG, "attn: lse must be 4-byte aligned");
-    if (g != nullptr)
+    if (!query && !aligned(lse, 4)) return fail(UAA_ERR_INVALID_ARG, "attn: lse must be 4-byte aligned");
+    if (g != nullptr && !query)
         for (int p = 0; p < g->world; ++p) {
             if (g->seq_off[p + 1] == g->seq_off[p]) continue;
             if (g->q_shards[p] == nullptr || !aligned(g->q_shards[p], 16))
@@ -390,14 +408,19 @@ static int attn_impl(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, in
     if (((Sq + 63) / 64) * H * B >= kMaxIdx32) return fail(UAA_ERR_INVALID_ARG, "attn: grid too large");
     a.split_p = 1;
     a.n_whole = 0;
-    if (workspace != nullptr) {
-        if (!aligned(workspace, 256)) return fail(UAA_ERR_INVALID_ARG, "attn: workspace must be 256-byte aligned");
+    if (query ? workspace_bytes > 0 : workspace != nullptr) {
+        if (!query && !aligned(workspace, 256))
+            return fail(UAA_ERR_INVALID_ARG, "attn: workspace must be 256-byte aligned");
         const uaa::SplitPlan plan = attn_split_plan(dtype, B, H, Sq, Sk, D, mask);
         if (plan.p > 1 && workspace_bytes >= (size_t)plan_ws_bytes(plan, B, H, Sq)) {
             a.split_p = plan.p;
             a.n_whole = plan.n_whole;
             a.ws = workspace;
         }
+    }
+    if (query) {
+        *kernel = dtype == UAA_BF16 ? uaa::attn_bf16_kernel_choice((int)D, a) : USP_KERNEL_FP32;
+        return UAA_OK;
     }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == UAA_BF16) return hip_status(uaa::launch_attn_bf16((int)D, o_dtype, a, s), "attn launch");
@@ -427,6 +450,15 @@ UAA_EXPORT int usp_attn_fwd_lse_acc(int dtype, int64_t B, int64_t H, int64_t Sq,
 {
     return attn_impl(dtype, B, H, Sq, Sk, D, q, k, v, o, o_dtype, lse, scale, mask, workspace, workspace_bytes,
                      1, nullptr, stream);
+}
+
+UAA_EXPORT int usp_attn_kernel(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, int o_dtype,
+                               const usp_mask* mask, size_t workspace_bytes)
+{
+    int k = USP_KERNEL_NONE;
+    const int rc = attn_impl(dtype, B, H, Sq, Sk, D, nullptr, nullptr, nullptr, nullptr, o_dtype, nullptr, 1.0f,
+                             mask, nullptr, workspace_bytes, 0, nullptr, nullptr, &k);
+    return rc != UAA_OK ? rc : k;
 }
 
 UAA_EXPORT int usp_attn_fwd_lse_gather(int dtype, int world, int rank, const int64_t* seq_off,

@@ -859,20 +859,43 @@ static bool p32_on()
     return on;
 }
 
-hipError_t launch_attn_bf16(int D, int o_dtype, const AttnArgs& a0, hipStream_t s)
+// The general kernel's arguments with its q-tile count set and a key split
+// kept only where it applies; false when there is no work.
+static bool general_args(const AttnArgs& a0, AttnArgs& a)
 {
-    AttnArgs a = a0;
+    a = a0;
     a.n_qtiles = (int32_t)((a.Sq + kBM - 1) / kBM);
     const int64_t units = (int64_t)a.n_qtiles * a.H * a.B;
-    if (units <= 0) return hipSuccess;
+    if (units <= 0) return false;
     if (a.masked || a.ws == nullptr || a.split_p <= 1 || a.n_whole < 0 || a.n_whole >= units) {
         a.split_p = 1;
         a.n_whole = 0;
     }
+    return true;
+}
+
+static bool use_p32(int D, const AttnArgs& a)
+{
+    return D == 128 && a.split_p <= 1 && attn_p32_fits(a.Sk, a.row_heads) && p32_on() && attn_p32_mask_ok(a);
+}
+
+int attn_bf16_kernel_choice(int D, const AttnArgs& a0)
+{
+    AttnArgs a;
+    if (!general_args(a0, a)) return USP_KERNEL_NONE;
+    if (use_p32(D, a)) return USP_KERNEL_PIPELINED;
+    if (a.masked) return USP_KERNEL_GENERAL_MASKED;
+    return a.split_p > 1 ? USP_KERNEL_GENERAL_SPLIT : USP_KERNEL_GENERAL;
+}
+
+hipError_t launch_attn_bf16(int D, int o_dtype, const AttnArgs& a0, hipStream_t s)
+{
+    AttnArgs a;
+    if (!general_args(a0, a)) return hipSuccess;
+    const int64_t units = (int64_t)a.n_qtiles * a.H * a.B;
     const int64_t blocks = a.split_p > 1 ? a.n_whole + (units - a.n_whole) * a.split_p : units;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    if (D == 128 && a.split_p <= 1 && attn_p32_fits(a.Sk, a.row_heads) && p32_on() && attn_p32_mask_ok(a))
-        return launch_attn_p32(o_dtype, a0, s);
+    if (use_p32(D, a)) return launch_attn_p32(o_dtype, a0, s);
     const dim3 grid((unsigned)blocks);
     const bool ob = o_dtype == UAA_BF16;
     if (D == 128) return ob ? launch_d<128, true>(a, grid, s) : launch_d<128, false>(a, grid, s);

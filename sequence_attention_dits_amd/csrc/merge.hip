@@ -156,7 +156,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a, int lpr_l
             }
             const int64_t elem = row * a.D + (int64_t)seg * VEC;
             Slice<TOut, VEC>::store(reinterpret_cast<TOut*>(a.o_out) + elem, acc);
-            if (seg == 0) a.lse_out[row] = L;
+            // lse_out may be one of the partials' LSE arrays: it is written
+            // only in the pass after which no lane of the row reads the
+            // partial LSEs again (the lane of slice 0 makes the most passes,
+            // and the row's lanes are one wavefront, in step)
+            if ((seg & (lpr - 1)) == 0 && seg + lpr >= slices) a.lse_out[row] = L;
         }
     }
 }

@@ -313,3 +313,53 @@ def test_backward_delta_validation(kw, code, text):
                                 a["delta"], None)
     assert rc == code and text in lib.uaa_last_error().decode(), (rc, lib.uaa_last_error())
     assert lib.usp_attn_bwd_delta(0, 0, 4, 2, 128, 0, 0, None, 0, None) == 0
+
+
+def test_split_offsets_matches_the_oracle_split():
+    """The library's default split (used for heads when head_off is NULL)
+    against the oracle's, which is written independently from the pages'
+    worked lengths (257 -> 129 / 128, 4481 -> 2241 / 2240)."""
+    import oracle
+    assert uaa.uaa_split_offsets(257, 2) == [0, 129, 257]
+    assert uaa.uaa_split_offsets(4481, 2) == [0, 2241, 4481]
+    for total in (0, 1, 5, 7, 24, 31, 4608, 6986):
+        for parts in (1, 2, 3, 4, 7, 8, 64):
+            assert uaa.uaa_split_offsets(total, parts) == oracle.split_offsets(total, parts), (total, parts)
+
+
+@pytest.mark.parametrize("total,parts,text", [(5, 0, "parts"), (-1, 2, "total")])
+def test_split_offsets_validation(total, parts, text):
+    lib = uaa.lib()
+    off = (ctypes.c_int64 * 4)(7, 7, 7, 7)
+    assert lib.uaa_split_offsets(total, parts, off) == -1
+    assert text in lib.uaa_last_error().decode()
+    assert list(off) == [7, 7, 7, 7]
+    assert lib.uaa_split_offsets(5, 2, None) == -1
+
+
+def test_kernel_query_names_the_kernel_of_each_case():
+    """usp_attn_kernel: the workloads' launches and the selection rules
+    (pipelined for unmasked D = 128 bf16 whose key tiles pad to a multiple
+    of six by at most a tenth, and for masks whose 256-row units see every
+    key of the block or none; the general kernel otherwise).  Host only."""
+    K = uaa
+    bf, f32 = __import__("torch").bfloat16, __import__("torch").float32
+    flux = (1, 4608, 12, 128)
+    assert K.usp_attn_kernel(flux, 2304) == K.USP_KERNEL_PIPELINED
+    assert K.usp_attn_kernel((1, 4481, 12, 128), 2241) == K.USP_KERNEL_PIPELINED
+    assert K.usp_attn_kernel(flux, 2304, f32) == K.USP_KERNEL_FP32
+    assert K.usp_attn_kernel(flux, 2304, bf, f32) == K.USP_KERNEL_PIPELINED
+    assert K.usp_attn_kernel((1, 4608, 12, 64), 2304) == K.USP_KERNEL_GENERAL
+    assert K.usp_attn_kernel((1, 300, 2, 128), 64 * 7) == K.USP_KERNEL_GENERAL   # 7 tiles pad by 5 > 0.7
+    assert K.usp_attn_kernel((0, 300, 2, 128), 64) == K.USP_KERNEL_NONE
+    lc = (1, 8192, 32, 128)
+    zz = lambda c: K.mask_zigzag(4096, [1, 6], [c])
+    assert K.usp_attn_kernel(lc, 4096, mask=zz(0)) == K.USP_KERNEL_PIPELINED      # wholly in the past
+    assert K.usp_attn_kernel(lc, 4096, mask=zz(3)) == K.USP_KERNEL_PIPELINED      # units see all or none
+    assert K.usp_attn_kernel((1, 300, 2, 128), 300, mask=K.mask_causal()) == K.USP_KERNEL_GENERAL_MASKED
+    with pytest.raises(uaa.UaaError) as e:
+        K.usp_attn_kernel(flux, 2304, mask=K.usp_mask(kind=7))
+    assert e.value.status == K.UAA_ERR_INVALID_ARG
+    with pytest.raises(uaa.UaaError) as e:
+        K.usp_attn_kernel((1, 30, 2, 96), 30)
+    assert e.value.status == K.UAA_ERR_UNSUPPORTED

@@ -3,8 +3,11 @@ partials) against the fp64 oracle.
 
 * small shapes that span several tiles and ragged tails, every mask kind,
   bf16 (both output dtypes) and fp32, all rows checked;
-* the five workloads at full size, in the launch configuration the bench
-  times, checked on sampled rows the oracle computes one by one;
+* the workloads' attention calls at full size (one call over all keys of
+  the FLUX shares, the Qwen chunks, the long-context chunks with their
+  8-way merge), checked on sampled rows the oracle computes one by one; the
+  exact step the bench times (its launches, kernels and streams) is checked
+  on every row in test_gpu_step.py;
 * edge cases: empty key set, rows with no allowed key, a key chunk after
   every query (O = 0, LSE = -inf), single rows, large scores.
 """

@@ -133,3 +133,23 @@ def test_gather_rejects_fp32_and_bad_shard_index():
     with pytest.raises(uaa.UaaError) as e:
         uaa.usp_attn_fwd_lse_gather(0, [x, x], [x, x], [x, x], 2, o, lse, 0.1, [0, 4, 8])
     assert e.value.status == uaa.UAA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("H,rank", [(5, 0), (5, 1)])
+def test_gather_default_head_split_against_oracle(H, rank):
+    """head_off = None goes to the library as NULL; the rank's heads are the
+    oracle's own split (3 / 2 of 5), and the Ring pass over both token shards
+    must equal the oracle's attention of those heads over every key."""
+    B, seq_off, D = 1, [0, 197, 389], 128
+    shards, (qv, kv_, vv) = _shards(998, B, seq_off, H, D)
+    scale = 1.0 / math.sqrt(D)
+    hoff = oracle.split_offsets(H, 2)
+    h0, h1 = hoff[rank], hoff[rank + 1]
+    o = torch.empty(B, 389, h1 - h0, D, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty(B, 389, h1 - h0, device="cuda")
+    say("attn gather default head split H=%d rank %d" % (H, rank))
+    for ks in range(2):
+        uaa.usp_attn_fwd_lse_gather(rank, *shards, ks, o, lse, scale, seq_off, None, accumulate=ks > 0)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(qv[:, :, h0:h1], kv_[:, :, h0:h1], vv[:, :, h0:h1], np.float32(scale))
+    check_pair(host_f64(o), host_f64(lse), o_ref, l_ref, "bf16", "gather, default head split")

@@ -44,6 +44,7 @@ def _inputs(cfg, B, Sq, Sk, H, D=128):
 def test_pipelined_all_rows(case, out):
     name, B, Sq, Sk, H = case
     say("attn pipelined", name, out)
+    assert uaa.usp_attn_kernel((B, Sq, H, 128), Sk) == uaa.USP_KERNEL_PIPELINED
     (qb, qv), (kb, kv), (vb, vv) = _inputs(1100 + CASES.index(case), B, Sq, Sk, H)
     scale = 1.0 / math.sqrt(128)
     o = torch.empty(B, Sq, H, 128, device="cuda", dtype=torch.bfloat16 if out == "bf16" else torch.float32)
@@ -63,6 +64,8 @@ def test_pipelined_ring_pass_accumulates(out):
     (qb, qv), (kb, kv), (vb, vv) = _inputs(1150, B, Sq, 751, H)
     scale = 1.0 / math.sqrt(128)
     q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    assert uaa.usp_attn_kernel((B, Sq, H, 128), 384) == uaa.USP_KERNEL_PIPELINED
+    assert uaa.usp_attn_kernel((B, Sq, H, 128), 367) == uaa.USP_KERNEL_PIPELINED
     o = torch.empty(B, Sq, H, 128, device="cuda", dtype=torch.bfloat16 if out == "bf16" else torch.float32)
     lse = torch.empty(B, Sq, H, device="cuda", dtype=torch.float32)
     uaa.usp_attn_fwd_lse(q, k[:, :384].contiguous(), v[:, :384].contiguous(), o, lse, scale)
@@ -89,6 +92,7 @@ def test_pipelined_rising_maximum():
     # tile by far more than the lazy-rescale threshold (8 in log2 units)
     s = np.einsum("qd,kd->qk", q[0, :, 0].astype(np.float64), k[0, :, 0].astype(np.float64)) * scale / math.log(2)
     assert np.median(s.max(axis=1) - s[:, :64].max(axis=1)) > 16.0
+    assert uaa.usp_attn_kernel((B, Sq, H, 128), Sk) == uaa.USP_KERNEL_PIPELINED
     o = torch.empty(B, Sq, H, 128, device="cuda", dtype=torch.float32)
     lse = torch.empty(B, Sq, H, device="cuda", dtype=torch.float32)
     uaa.usp_attn_fwd_lse(dev_bf16(bits[0]), dev_bf16(bits[1]), dev_bf16(bits[2]), o, lse, scale)
@@ -149,6 +153,9 @@ def test_units_all_or_nothing(out):
     dt = torch.bfloat16 if out == "bf16" else torch.float32
     o = torch.full((1, 2 * C, H, 128), 7.0, device="cuda", dtype=dt)
     lse = torch.full((1, 2 * C, H), 7.0, device="cuda", dtype=torch.float32)
+    for kc in ([2], [0]):
+        assert uaa.usp_attn_kernel((1, 2 * C, H, 128), C, mask=uaa.mask_zigzag(C, [1, 4], kc)) == \
+            uaa.USP_KERNEL_PIPELINED
     # K chunk 2 alone: rows of Q chunk 1 see nothing, rows of Q chunk 4 all
     uaa.usp_attn_fwd_lse(q, k[:, :C].contiguous(), v[:, :C].contiguous(), o, lse, scale,
                          mask=uaa.mask_zigzag(C, [1, 4], [2]))

@@ -107,6 +107,31 @@ def test_merge_in_place_into_first_partial():
     check_pair(host_f64(o_parts[0]), host_f64(l_parts[0]), o_ref, l_ref, "bf16", "in place")
 
 
+@pytest.mark.parametrize("din,dout,D,into", [
+    ("bf16", "fp32", 128, 0),    # one element per lane: two passes over the row's 128 slices
+    ("bf16", "bf16", 130, 1),    # D not a multiple of the vector: 130 slices, three passes
+    ("fp32", "fp32", 301, 2),    # one element per lane: 301 slices, five passes
+    ("bf16", "bf16", 1024, 0),   # 16-byte slices, two passes
+])
+def test_merge_lse_in_place_with_several_passes_per_row(din, dout, D, into):
+    """lse_out aliasing one partial's LSE (allowed for any dtype pair) when a
+    row's slices outnumber the 64 lanes, so the row is merged in several
+    passes: the later passes must still see the partials' own LSEs."""
+    say("merge in place, several passes", din, dout, D)
+    shape = (1, 37, 3, D)
+    o_bits, o_vals, l_vals = _partials(6, 3, shape, din, neg_inf_frac=0.05)
+    o_parts = [dev(b, din) for b in o_bits]
+    l_parts = [torch.from_numpy(x).cuda() for x in l_vals]
+    same = din == dout
+    o_out = o_parts[into] if same else torch.empty(shape, device="cuda",
+                                                   dtype=torch.bfloat16 if dout == "bf16" else torch.float32)
+    uaa.usp_lse_merge(o_parts, l_parts, o_out, l_parts[into])
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.lse_merge(o_vals, [x.astype(np.float64) for x in l_vals])
+    check_pair(host_f64(o_out), host_f64(l_parts[into]), o_ref, l_ref,
+               "bf16" if "bf16" in (din, dout) else "fp32", "in place D=%d" % D)
+
+
 @pytest.mark.parametrize("din,dout", [("bf16", "fp32"), ("fp32", "bf16")])
 def test_merge_mixed_dtypes(din, dout):
     shape = (2, 70, 3, 128)

@@ -222,3 +222,54 @@ def test_multi_tensor_mixed_row_sizes_equal_separate_calls(direction, seq_off, h
     torch.cuda.synchronize()
     assert torch.equal(refs[0].view(torch.int16), d2[0].view(torch.int16))
     assert torch.equal(refs[1].view(torch.int32), d2[1].view(torch.int32))
+
+
+@pytest.mark.parametrize("S,H,world,seq_split", [
+    (389, 5, 2, None),               # uneven heads: 3 / 2
+    (4481, 24, 2, [0, 2241, 4481]),  # the non-divisible FLUX share: 12 / 12 heads, 2241 / 2240 tokens
+    (100, 7, 3, [0, 40, 40, 100]),   # 3 / 2 / 2 heads, an empty token shard
+])
+def test_default_head_split_inside_the_library(S, H, world, seq_split):
+    """head_off = None is passed to the library as NULL: the heads are split
+    there, and the result must equal the oracle's gather with the oracle's
+    own split (first H mod world ranks take one extra head)."""
+    B, D = 1, 64
+    seq_off = seq_split or oracle.split_offsets(S, world)
+    head_off = oracle.split_offsets(H, world)
+    assert uaa.uaa_split_offsets(H, world) == head_off
+    x = (np.arange(B * S * H * D, dtype=np.int64) * 2654435761 % (1 << 31)).astype(np.int32).reshape(B, S, H, D)
+    shards = [x[:, seq_off[p]:seq_off[p + 1]] for p in range(world)]
+    dev_shards = [torch.from_numpy(np.ascontiguousarray(s)).cuda() for s in shards]
+    heads = []
+    for r in range(world):
+        say("permute default head split S=%d H=%d world=%d SEQ2HEAD rank %d" % (S, H, world, r))
+        dst = torch.empty(B, S, head_off[r + 1] - head_off[r], D, dtype=torch.int32, device="cuda")
+        uaa.uaa_seq2head_permute(uaa.UAA_SEQ2HEAD, r, dev_shards, dst, seq_off, None)
+        torch.cuda.synchronize()
+        ref = oracle.seq2head(shards, r, seq_off, head_off)
+        assert dst.cpu().numpy().tobytes() == ref.tobytes()
+        heads.append(dst)
+    for p in range(world):
+        say("permute default head split HEAD2SEQ rank %d" % p)
+        out = torch.empty(B, seq_off[p + 1] - seq_off[p], H, D, dtype=torch.int32, device="cuda")
+        uaa.uaa_seq2head_permute(uaa.UAA_HEAD2SEQ, p, heads, out, seq_off, None)
+        torch.cuda.synchronize()
+        assert out.cpu().numpy().tobytes() == np.ascontiguousarray(shards[p]).tobytes()
+    # the multi-tensor entry with its NULL head split: O and its LSE together
+    lse_heads = [h[..., :1].contiguous() for h in heads]
+    out_o = torch.empty(B, seq_off[1], H, D, dtype=torch.int32, device="cuda")
+    out_l = torch.empty(B, seq_off[1], H, 1, dtype=torch.int32, device="cuda")
+    uaa.uaa_seq2head_permute_multi(uaa.UAA_HEAD2SEQ, 0, [heads, lse_heads], [out_o, out_l], seq_off, None)
+    torch.cuda.synchronize()
+    assert out_o.cpu().numpy().tobytes() == np.ascontiguousarray(shards[0]).tobytes()
+    assert out_l.cpu().numpy().tobytes() == np.ascontiguousarray(shards[0][..., :1]).tobytes()
+
+
+def test_default_head_split_rejects_mismatched_destination():
+    """With head_off None the binding checks the destination against the
+    library's split, so a tensor sized for another split is refused before
+    any launch."""
+    src = [torch.zeros(1, 4, 5, 8, device="cuda"), torch.zeros(1, 4, 5, 8, device="cuda")]
+    wrong = torch.empty(1, 8, 2, 8, device="cuda")    # rank 0 gets 3 of 5 heads
+    with pytest.raises(ValueError):
+        uaa.uaa_seq2head_permute(uaa.UAA_SEQ2HEAD, 0, src, wrong, [0, 4, 8], None)

@@ -1,10 +1,11 @@
 """Pins of the oracle's LSE merge (O5).
 
-P5  * equals the pages' own pairwise update on finite inputs ("Add Unified
-      Sequence Parallel attention", review thread: the Ring loop's
-      out = prev_out - sigmoid(lse - prev_lse) * (prev_out - out),
-      lse = prev_lse - logsigmoid(prev_lse - lse), in fp32 there, fp64 here),
-      folded left to right over N partials;
+P5  * equals the pages' own way of merging ("Add Unified Sequence Parallel
+      attention", review thread: the Ring loop folds each step's (out, lse)
+      into the running pair, in fp32 there): two partials at a time, the
+      result is the mean of the two outputs weighted by e^lse of each, and
+      its LSE is log(e^lse_a + e^lse_b); folded left to right over N
+      partials, in fp64 here;
     * commutative and associative;
     * a partial with LSE = -inf is the identity; all -inf gives (0, -inf);
     * merging the halves of an attention equals the whole (see P4 too).
@@ -14,42 +15,45 @@ import math
 
 import numpy as np
 import pytest
-import torch
 
 import oracle
 
 
-def _pairwise_pages_form(o_parts, lse_parts):
-    out = torch.from_numpy(o_parts[0].copy())
-    lse = torch.from_numpy(lse_parts[0].copy())[..., None]
+def _pairwise_fold(o_parts, lse_parts):
+    """Fold the partials two at a time: (a, la) and (b, lb) become the mean
+    of a and b weighted e^la : e^lb -- b's weight is the logistic function of
+    lb - la -- with LSE log(e^la + e^lb).  Valid for finite LSEs."""
+    out = np.array(o_parts[0], dtype=np.float64)
+    lse = np.array(lse_parts[0], dtype=np.float64)
     for o_n, l_n in zip(o_parts[1:], lse_parts[1:]):
-        o_n = torch.from_numpy(o_n)
-        l_n = torch.from_numpy(l_n)[..., None]
-        prev_out, prev_lse = out, lse
-        out = prev_out - torch.sigmoid(l_n - prev_lse) * (prev_out - o_n)
-        lse = prev_lse - torch.nn.functional.logsigmoid(prev_lse - l_n)
-    return out.numpy(), lse[..., 0].numpy()
+        w = 1.0 / (1.0 + np.exp(lse - l_n))
+        out = out + w[..., None] * (o_n - out)
+        lse = np.logaddexp(lse, l_n)
+    return out, lse
 
 
 @pytest.mark.parametrize("n", [2, 3, 8, 16])
-def test_p5_equals_pages_pairwise_update(n):
+def test_p5_equals_pairwise_fold(n):
     rng = np.random.default_rng(n)
     o = [rng.standard_normal((5, 7, 3, 16)) for _ in range(n)]
     l = [rng.standard_normal((5, 7, 3)) * 4 + 8 for _ in range(n)]
     got_o, got_l = oracle.lse_merge(o, l)
-    ref_o, ref_l = _pairwise_pages_form(o, l)
+    ref_o, ref_l = _pairwise_fold(o, l)
     np.testing.assert_allclose(got_o, ref_o, rtol=0, atol=1e-13)
     np.testing.assert_allclose(got_l, ref_l, rtol=0, atol=1e-13)
 
 
-def test_p5_pages_form_gives_nan_on_empty_first_partial():
-    # The reading replaces the pages' pairwise form where it breaks down: a
-    # first partial with no allowed key (LSE = -inf) makes it NaN, the
-    # max-shifted form returns the other partial unchanged.
+def test_p5_pairwise_lse_update_breaks_on_an_empty_partial():
+    # Why the merge is written max-shifted (reading 6): the pages fold the
+    # new LSE in as the running LSE plus log(1 + e^(new - running)).  With
+    # no key seen so far the running LSE is -inf, the exponent +inf, and the
+    # sum -inf + inf is NaN in IEEE arithmetic; the max-shifted merge gives
+    # the other partial unchanged.
+    with np.errstate(over="ignore", invalid="ignore"):
+        run, new = np.float64(-np.inf), np.float64(1.5)
+        assert np.isnan(run + np.log1p(np.exp(new - run)))
     o = [np.zeros((1, 4)), np.arange(4.0)[None]]
     l = [np.array([-math.inf]), np.array([1.5])]
-    ref_o, ref_l = _pairwise_pages_form(o, l)
-    assert np.isnan(ref_l).all() or np.isnan(ref_o).any()
     got_o, got_l = oracle.lse_merge(o, l)
     np.testing.assert_array_equal(got_o, o[1])
     np.testing.assert_array_equal(got_l, l[1])
