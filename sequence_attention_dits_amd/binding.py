@@ -196,7 +196,8 @@ def _head_offsets(head_off, H, world):
 
 
 def _permute_shapes(direction, rank, src, dst, seq_off, head_off):
-    """Check one tensor's shard shapes against the offsets; returns (B, H, D, head offsets)."""
+    """Check one tensor's shard shapes against the offsets; returns (B, H, D, head offsets,
+    the head_off argument of the library call: NULL when the caller gave none)."""
     world = len(src)
     if len(seq_off) != world + 1:
         raise ValueError("seq_off needs world+1 entries")
@@ -230,7 +231,7 @@ def _permute_shapes(direction, rank, src, dst, seq_off, head_off):
                 raise ValueError("src[%d] shape %s does not match the offsets" % (r, tuple(x.shape)))
         if tuple(dst.shape) != (B, seq_off[rank + 1] - seq_off[rank], H, D):
             raise ValueError("dst shape %s does not match the offsets" % (tuple(dst.shape),))
-    return B, H, D, harg
+    return B, H, D, hoff, harg
 
 
 def uaa_seq2head_permute(direction: int, rank: int, src: Sequence[torch.Tensor], dst: torch.Tensor,
@@ -241,7 +242,7 @@ def uaa_seq2head_permute(direction: int, rank: int, src: Sequence[torch.Tensor],
     HEAD2SEQ: src[r] [B,S,H_r,D] -> dst [B,S_p,H,D] for token rank `rank`.
     Any element dtype; bits are copied unchanged.
     """
-    B, H, D, harg = _permute_shapes(direction, rank, src, dst, seq_off, head_off)
+    B, H, D, _, harg = _permute_shapes(direction, rank, src, dst, seq_off, head_off)
     ptrs = (ctypes.c_void_p * len(src))(*[x.data_ptr() if x.numel() else 0 for x in src])
     _check(lib().uaa_seq2head_permute(direction, rank, len(src), _i64_array(seq_off),
                                       harg, B, H, D, dst.element_size(), ptrs,
@@ -263,7 +264,7 @@ def uaa_seq2head_permute_multi(direction: int, rank: int, srcs: Sequence[Sequenc
         shapes.append(_permute_shapes(direction, rank, src, dst, seq_off, head_off))
         if (shapes[-1][0], shapes[-1][1], shapes[-1][3]) != (shapes[0][0], shapes[0][1], shapes[0][3]):
             raise ValueError("all tensors of one call must share B, H and the offsets")
-    B, H, D, harg = shapes[0]
+    B, H, D, _, harg = shapes[0]
     flat = [x for src in srcs for x in src]
     ptrs = (ctypes.c_void_p * len(flat))(*[x.data_ptr() if x.numel() else 0 for x in flat])
     dptrs = (ctypes.c_void_p * len(dsts))(*[d.data_ptr() if d.numel() else 0 for d in dsts])
