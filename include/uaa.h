@@ -254,6 +254,32 @@ int usp_attn_fwd_lse_ws(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
                         size_t workspace_bytes, void* stream);
 
 /*
+ * usp_attn_fwd_lse_static -- usp_attn_fwd_lse_ws for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid hipMalloc.  It takes no workspace
+ * and allocates nothing (no hipMalloc, hipFree or allocating library call):
+ * the key split's workspace is a device array inside the library,
+ * USP_STATIC_SCRATCH_BYTES per GPU, which every GPU the library runs on
+ * holds from the library's loading until the process ends.  Its device
+ * address is looked up once per device on the first call there.  The split's
+ * arrival counters are cleared by a small kernel on `stream` ahead of each
+ * launch that uses them (a kernel, not a memset, so graph replays repeat
+ * it).  Every call on one GPU shares that GPU's array and it keeps the last
+ * call's contents: calls that may overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller.
+ *
+ * A problem whose key split would need more than USP_STATIC_SCRATCH_BYTES
+ * (a device with more than 256 compute units) returns UAA_ERR_UNSUPPORTED
+ * and enqueues nothing.  Results equal usp_attn_fwd_lse_ws given a large
+ * enough workspace, bit for bit; every argument is that call's.
+ * Returns UAA_OK, UAA_ERR_INVALID_ARG, UAA_ERR_UNSUPPORTED or UAA_ERR_HIP.
+ */
+#define USP_STATIC_SCRATCH_BYTES (36u << 20)   /* 256 piece slots of 136 KiB and their counters */
+int usp_attn_fwd_lse_static(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                            const void* q, const void* k, const void* v, void* o, int o_dtype,
+                            float* lse, float scale, const usp_mask* mask, void* stream);
+
+/*
  * usp_attn_fwd_lse_acc -- one step of a Ring pass in one call: the
  * attention of this key/value block merged into the running result ([USP]:
  * each Ring step's (out, lse) is folded into the accumulated one by the LSE

@@ -117,6 +117,8 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_float, ctypes.POINTER(usp_mask), _c_p]
         l.usp_attn_fwd_lse_ws.restype = ctypes.c_int
         l.usp_attn_fwd_lse_ws.argtypes = l.usp_attn_fwd_lse.argtypes[:-1] + [_c_p, ctypes.c_size_t, _c_p]
+        l.usp_attn_fwd_lse_static.restype = ctypes.c_int
+        l.usp_attn_fwd_lse_static.argtypes = l.usp_attn_fwd_lse.argtypes
         l.usp_attn_fwd_lse_acc.restype = ctypes.c_int
         l.usp_attn_fwd_lse_acc.argtypes = l.usp_attn_fwd_lse_ws.argtypes
         l.usp_attn_fwd_lse_gather.restype = ctypes.c_int
@@ -342,6 +344,25 @@ def usp_attn_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch
     fn = lib().usp_attn_fwd_lse_acc if accumulate else lib().usp_attn_fwd_lse_ws
     _check(fn(dt, B, H, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), odt, lse.data_ptr(),
               float(scale), ctypes.byref(m), ws_ptr, ws_n, _stream(q)))
+
+
+def usp_attn_fwd_lse_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                            lse: torch.Tensor, scale: float, mask: Optional[usp_mask] = None) -> None:
+    """usp_attn_fwd_lse_static: usp_attn_fwd_lse with the key split's
+    workspace inside the library (nothing is allocated by the call)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse")):
+        _dev(t, n)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q, k, v are [B, S, H, D] and k, v share a shape")
+    B, Sq, H, D = q.shape
+    if k.shape[0] != B or k.shape[2] != H or k.shape[3] != D or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k/v must match q in batch, heads, features and dtype")
+    if tuple(o.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Sq, H) or lse.dtype != torch.float32:
+        raise ValueError("o must be shaped like q and lse [B, Sq, H] float32")
+    m = mask if mask is not None else mask_full()
+    _check(lib().usp_attn_fwd_lse_static(_code(q.dtype, "q"), B, H, Sq, k.shape[1], D, q.data_ptr(), k.data_ptr(),
+                                         v.data_ptr(), o.data_ptr(), _code(o.dtype, "o"), lse.data_ptr(),
+                                         float(scale), ctypes.byref(m), _stream(q)))
 
 
 def usp_lse_merge(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor],

@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "internal.h"
 
@@ -331,10 +332,14 @@ struct GatherSrc {
 // `kernel` non-null nothing is launched and the pointers are not checked:
 // the USP_KERNEL_* code of the kernel the call would run is stored there (a
 // workspace counts as given when workspace_bytes > 0).
+// With clear_counters the key split's arrival counters in the workspace are
+// zeroed on the stream (a small fill kernel) before the attention launch.
+static hipError_t clear_split_counters(const uaa::AttnArgs& a, hipStream_t s);
+
 static int attn_impl(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, const void* q,
                      const void* k, const void* v, void* o, int o_dtype, float* lse, float scale,
                      const usp_mask* mask, void* workspace, size_t workspace_bytes, int acc, const GatherSrc* g,
-                     void* stream, int* kernel = nullptr)
+                     void* stream, int* kernel = nullptr, bool clear_counters = false)
 {
     if (dtype != UAA_BF16 && dtype != UAA_FP32)
         return fail(UAA_ERR_INVALID_ARG, "attn: dtype must be UAA_BF16 or UAA_FP32, got %d", dtype);
@@ -423,6 +428,10 @@ static int attn_impl(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, in
         return UAA_OK;
     }
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (clear_counters && a.split_p > 1) {
+        const int rc = hip_status(clear_split_counters(a, s), "scratch counter clear");
+        if (rc != UAA_OK) return rc;
+    }
     if (dtype == UAA_BF16) return hip_status(uaa::launch_attn_bf16((int)D, o_dtype, a, s), "attn launch");
     return hip_status(uaa::launch_attn_fp32((int)D, a, s), "attn launch");
 }
@@ -625,4 +634,79 @@ UAA_EXPORT int usp_attn_bwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == UAA_BF16) return hip_status(uaa::launch_attn_bwd_bf16((int)D, a, s), "bwd launch");
     return hip_status(uaa::launch_attn_bwd_fp32((int)D, a, s), "bwd launch");
+}
+
+// --------------------------------------------------------------------------
+// Attention without allocation (usp_attn_fwd_lse_static): the key split's
+// workspace is this file-scope device array, one copy per GPU, held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (there
+// it is a host-side stand-in): its device address is taken once per device
+// with hipGetSymbolAddress, with that device current, and that pointer is
+// what the kernels get.
+// --------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[USP_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+// n 32-bit words from p set to zero (a kernel, not a memset, so that a
+// captured graph replays it faithfully)
+__global__ void zero_words_kernel(uint32_t* p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];   // device address of `scratch` per device, once known
+
+int scratch_address(void** out)
+{
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "static attn: hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(UAA_ERR_UNSUPPORTED, "static attn: device %d above the 64 this library tracks", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        const hipError_t g = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (g != hipSuccess) return hip_status(g, "static attn: hipGetSymbolAddress(scratch)");
+        if (p == nullptr) return fail(UAA_ERR_HIP, "static attn: scratch has no device address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return UAA_OK;
+}
+
+}  // namespace
+
+static hipError_t clear_split_counters(const uaa::AttnArgs& a, hipStream_t s)
+{
+    const int64_t units = uaa::attn_bf16_units(a.B, a.H, a.Sq);
+    const int64_t n_split = units - a.n_whole;
+    if (n_split <= 0) return hipSuccess;
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(a.ws) +
+                                                n_split * a.split_p * uaa::kSplitSlotBytes);
+    const unsigned blocks = (unsigned)std::min<int64_t>((n_split + 255) / 256, 64);
+    void* params[] = {&cnt, const_cast<int64_t*>(&n_split)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(zero_words_kernel), dim3(blocks), dim3(256), params, 0, s);
+}
+
+UAA_EXPORT int usp_attn_fwd_lse_static(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                       const void* q, const void* k, const void* v, void* o, int o_dtype,
+                                       float* lse, float scale, const usp_mask* mask, void* stream)
+{
+    // the workspace this problem's plan needs (0: it runs as the plain call)
+    int kern = USP_KERNEL_NONE;
+    int rc = attn_impl(dtype, B, H, Sq, Sk, D, q, k, v, o, o_dtype, lse, scale, mask, nullptr,
+                       (size_t)USP_STATIC_SCRATCH_BYTES, 0, nullptr, stream, &kern);
+    if (rc != UAA_OK) return rc;
+    const int64_t need = plan_ws_bytes(attn_split_plan(dtype, B, H, Sq, Sk, D, mask), B, H, Sq);
+    if (need > (int64_t)USP_STATIC_SCRATCH_BYTES)
+        return fail(UAA_ERR_UNSUPPORTED, "static attn: the key split needs %lld bytes of scratch, the library holds %lld",
+                    (long long)need, (long long)USP_STATIC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc != UAA_OK) return rc;
+    return attn_impl(dtype, B, H, Sq, Sk, D, q, k, v, o, o_dtype, lse, scale, mask, need > 0 ? ws : nullptr,
+                     (size_t)USP_STATIC_SCRATCH_BYTES, 0, nullptr, stream, nullptr, true);
 }
