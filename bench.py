@@ -111,9 +111,13 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-backward", action="store_true", help="skip the backward variant")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    p.add_argument("--pmc-probe", action="store_true",
-                   help="only enqueue the dispatches that the HBM traffic counters are read on: a plain "
-                        "device copy of known size, then --steps attention launch pairs")
+    p.add_argument("--pmc-probe", nargs="?", const="attn", choices=["attn", "hbm"],
+                   help="only enqueue the dispatches that the counters are read on: a plain device copy of known "
+                        "size, then --steps attention launch pairs (attn), or --steps rounds of the HBM-bound "
+                        "launches and of plain copies of the same sizes, every one on cold buffers (hbm)")
+    p.add_argument("--hbm-summary", nargs="+", metavar="DIR",
+                   help="print the HBM-bound kernels' counter summary from rocprofv3 runs of --pmc-probe hbm: "
+                        "--pmc runs (FETCH_SIZE, WRITE_SIZE, ...) and one --kernel-trace --stats run")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="print the traffic summary of two rocprofv3 --pmc runs of --pmc-probe")
     p.add_argument("--stats-summary", metavar="DIR", help="print the summary of a rocprofv3 --stats run")
@@ -703,31 +707,31 @@ def _is_attn_fwd(kernel_name):
     return "attn_p32_kernel" in kernel_name or "attn_bf16_kernel" in kernel_name
 
 
-def attn_kernel_name(masked, split, sk):
-    """The forward kernel the library launches for a bf16 D=128 call: the
-    software-pipelined one for unmasked launches without a key split whose
-    key tiles pad to a multiple of six by at most a tenth (unless
-    UAA_ATTN_P32=0), else the general one."""
-    n = (sk + 63) // 64
-    pad = (6 - n % 6) % 6
-    if not masked and not split and n > 0 and pad * 10 <= n and os.environ.get("UAA_ATTN_P32", "1")[:1] != "0":
-        return "attn_p32_kernel<true>"
-    return "attn_bf16_kernel<128,%s,true,%s>" % ("true" if masked else "false", "true" if split else "false")
+# forward kernels by the library's USP_KERNEL_* code (usp_attn_kernel), as
+# the kernel traces name them
+KERNEL_NAMES = {
+    2: "attn_bf16_kernel<128, false, true, false>",
+    3: "attn_bf16_kernel<128, true, true, false>",
+    4: "attn_bf16_kernel<128, false, true, true>",
+    5: "attn_p32_kernel<true, false>",
+    6: "attn_p32_kernel<true, true>",
+}
 
 
 def attn_kernel_label(share, ring):
-    """The forward kernel(s) the timed attention launches run.  A zigzag
-    K chunk other than the rank's own Q chunks lies wholly in the past or
-    the future of every 256-row unit (the chunk length is a multiple of
-    256), which the pipelined kernel handles; the label then counts the
-    launches of each kernel."""
-    if not ring:
-        return attn_kernel_name(False, False, share.ring[0][1] - share.ring[0][0])
+    """The forward kernel(s) the timed attention launches run, from the
+    library's own choice (usp_attn_kernel); with several, each with its
+    launch count."""
+    uaa = share.uaa
     names = []
-    for c, (a, b) in enumerate(share.kv):
-        masked = share.masks[c] is not None and not (share.chunk is not None and share.chunk % 256 == 0
-                                                     and c not in share.qc)
-        names.append(attn_kernel_name(masked, share.ws[0] is not None and not masked, b - a))
+    if ring:
+        q = share.sets[0]["q"]
+        for (a, b), m in zip(share.kv, share.masks):
+            ws = share.ws[0].numel() if share.ws[0] is not None else 0
+            names.append(KERNEL_NAMES.get(uaa.usp_attn_kernel(q.shape, b - a, mask=m, workspace_bytes=ws), "?"))
+    else:
+        for a, b in share.ring:
+            names.append(KERNEL_NAMES.get(uaa.usp_attn_kernel(share.qh["q"].shape, b - a), "?"))
     if len(set(names)) == 1:
         return names[0]
     return " + ".join("%s x%d" % (n, names.count(n)) for n in sorted(set(names), key=names.index))
@@ -736,28 +740,162 @@ def attn_kernel_label(share, ring):
 def pmc_probe(args):
     import torch
     torch.cuda.set_device(0)
+    cfg_id, _ = WORKLOADS[args.workload]
     src = torch.ones(PMC_COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    if args.pmc_probe == "hbm":
+        hbm_probe(args, cfg_id, src, dst)
+        return
     for _ in range(3):
         dst.copy_(src)
-    cfg_id, _ = WORKLOADS[args.workload]
     share = Share(cfg_id, 4)
     for i in range(args.steps):
         share.launch_one("attn", i % 4)
     torch.cuda.synchronize()
 
 
-def _pmc_values(d, counter):
-    """{kernel name: [per-dispatch values]} of one counter from a rocprofv3 --pmc csv run."""
+# The HBM-bound launches of the FLUX-type step whose counters --pmc-probe hbm
+# collects, in the order each round enqueues them, then the plain device
+# copies of the same byte counts measured beside them.
+HBM_PROBE_ORDER = ("permute", "permute_qkv", "head2seq_o_lse", "merge", "copy_1x", "copy_3x", "copy_merge")
+
+
+def hbm_probe(args, cfg_id, big_src, big_dst):
+    """Everything allocated and initialised first; then the calibration
+    copies (3 x 1 GiB); then --steps rounds of HBM_PROBE_ORDER: each
+    HBM-bound launch of the step on its rotating set's own buffers, and
+    plain device copies that read and write the byte counts of one tensor,
+    of Q/K/V and of the merge, also rotating -- every dispatch on buffers
+    that rotate over more than 1 GiB, so nothing is served from the
+    Infinity Cache."""
+    import torch
+    n_sets = 11
+    share = Share(cfg_id, n_sets)
+    for s_ in range(n_sets):
+        share.timing_bufs(s_)
+    sizes = {"copy_1x": share.permute_bytes() / 2, "copy_3x": 3 * share.permute_bytes() / 2,
+             "copy_merge": share.merge_bytes() / 2}
+    copies = {k: [(torch.ones(int(v) // 4, device="cuda"), torch.empty(int(v) // 4, device="cuda"))
+                  for _ in range(n_sets)] for k, v in sizes.items()}
+    torch.cuda.synchronize()
+    for _ in range(3):
+        big_dst.copy_(big_src)
+    for i in range(args.steps):
+        s_ = i % n_sets
+        for name in HBM_PROBE_ORDER:
+            if name.startswith("copy"):
+                a, b = copies[name][s_]
+                b.copy_(a)
+            else:
+                share.launch_one(name, s_, timing=True)
+    torch.cuda.synchronize()
+
+
+def _hbm_dispatches(d):
+    """[(label, {counter: value}, duration_ns)] of the probe rounds in one
+    rocprofv3 output directory (counter collection or kernel trace): the
+    dispatches after the last calibration copy, labelled by their place in
+    the round."""
     import csv
     import glob
-    out = {}
-    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-        with open(f) as fh:
-            for r in csv.DictReader(fh):
-                if r["Counter_Name"] == counter:
-                    out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    recs = {}
+    for pat in ("*counter_collection.csv", "*kernel_trace.csv"):
+        for f in glob.glob(os.path.join(d, "**", pat), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    did = int(r["Dispatch_Id"])
+                    e = recs.setdefault(did, {"name": r["Kernel_Name"], "c": {},
+                                              "ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
+                    if "Counter_Name" in r:
+                        e["c"][r["Counter_Name"]] = float(r["Counter_Value"])
+    order = sorted(recs)
+    # the last of the three big copies: the copy dispatch followed by the first round's permute
+    last_cal = None
+    for i, did in enumerate(order):
+        if "copy" in recs[did]["name"].lower() and i + 1 < len(order) and \
+                "permute_kernel<0>" in recs[order[i + 1]]["name"]:
+            last_cal = i
+            break
+    if last_cal is None:
+        return []
+    out = []
+    for j, did in enumerate(order[last_cal + 1:]):
+        e = recs[did]
+        out.append((HBM_PROBE_ORDER[j % len(HBM_PROBE_ORDER)], e["c"], e["ns"], e["name"]))
     return out
+
+
+def hbm_summary(dirs, workload):
+    """Per HBM-bound kernel of --pmc-probe hbm and per plain copy of the same
+    size: HBM bytes from FETCH_SIZE and WRITE_SIZE, each scaled by what the
+    counter reads for the 1 GiB calibration copy, against the algorithmic
+    bytes; the kernel-trace duration and rate; and the means of every other
+    counter the runs hold."""
+    import numpy as np
+    import synth
+    cfg_id, _ = WORKLOADS[workload]
+    c = synth.CONFIGS[cfg_id]
+    B, S, H, D = c["B"], c["S"], c["H"], c["D"]
+    Hr, S0 = (H + 1) // 2, c["shards"][0]
+    perm = 2.0 * 2 * B * S * Hr * D
+    rows = B * S * Hr
+    merge = 3.0 * (rows * D * 2 + rows * 4)
+    algo = {"permute": perm, "permute_qkv": 3 * perm,
+            "head2seq_o_lse": 2.0 * 2 * B * S0 * H * D + 2.0 * 4 * B * S0 * H, "merge": merge,
+            "copy_1x": perm, "copy_3x": 3 * perm, "copy_merge": merge}
+    per = {}       # label -> counter -> [values]
+    scale = {}
+    for d in dirs:
+        # calibration: the 1 GiB copies' FETCH_SIZE / WRITE_SIZE (KiB)
+        for counter, vs in _pmc_values(d, "FETCH_SIZE").items():
+            pass
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            big = [v for k, vv in _pmc_values(d, counter).items() if "copy" in k.lower() for v in vv
+                   if v * 1024 > PMC_COPY_BYTES / 4]
+            if big:
+                scale[counter] = PMC_COPY_BYTES / (1024 * float(np.mean(big)))
+        for label, cs, ns, name in _hbm_dispatches(d):
+            for k, v in cs.items():
+                per.setdefault(label, {}).setdefault(k, []).append(v)
+            if not cs:
+                per.setdefault(label, {}).setdefault("duration_ns", []).append(ns)
+    cmd = "python3 bench.py --pmc-probe hbm --steps 40"
+    lines = [
+        "rocprofv3 counter summary: the HBM-bound kernels of the %s step (the single-tensor and Q/K/V" % workload,
+        "SEQ2HEAD permutes, the O+LSE HEAD2SEQ, the N=2 LSE merge) and plain device copies of the same byte",
+        "counts (hipMemcpy device to device), every dispatch on buffers that rotate over more than 1 GiB",
+        "",
+        "commands (run from the repository root on one MI355X; one counter group per run):",
+        "  rocprofv3 --kernel-trace --stats -d gpurun_out/hbm_trace -o hbm --output-format csv -- " + cmd,
+        "  rocprofv3 --pmc FETCH_SIZE -d gpurun_out/hbm_fetch -o pmc --output-format csv -- " + cmd,
+        "  rocprofv3 --pmc WRITE_SIZE GRBM_GUI_ACTIVE -d gpurun_out/hbm_write -o pmc --output-format csv -- " + cmd,
+        "  (further --pmc groups as listed below)",
+        "  python3 bench.py --hbm-summary " + " ".join(dirs),
+        "",
+        "calibration (1 GiB copy): FETCH_SIZE scale %s, WRITE_SIZE scale %s" % (
+            "%.4f" % scale["FETCH_SIZE"] if "FETCH_SIZE" in scale else "n/a",
+            "%.4f" % scale["WRITE_SIZE"] if "WRITE_SIZE" in scale else "n/a"),
+        "",
+        "%-16s %9s %9s %9s %10s %8s %8s %6s" % ("dispatch", "algo_MB", "fetch_MB", "write_MB", "traffic/x",
+                                               "avg_us", "GB/s", "n"),
+    ]
+    for label in HBM_PROBE_ORDER:
+        g = per.get(label, {})
+        f = float(np.mean(g["FETCH_SIZE"])) * 1024 * scale["FETCH_SIZE"] if "FETCH_SIZE" in g and \
+            "FETCH_SIZE" in scale else float("nan")
+        w = float(np.mean(g["WRITE_SIZE"])) * 1024 * scale["WRITE_SIZE"] if "WRITE_SIZE" in g and \
+            "WRITE_SIZE" in scale else float("nan")
+        us = float(np.mean(g["duration_ns"])) / 1e3 if "duration_ns" in g else float("nan")
+        n = len(g.get("duration_ns", g.get("FETCH_SIZE", [])))
+        lines.append("%-16s %9.2f %9.2f %9.2f %10.3f %8.2f %8.1f %6d" % (
+            label, algo[label] / 1e6, f / 1e6, w / 1e6, (f + w) / algo[label], us, algo[label] / (us * 1e3), n))
+    others = sorted({k for g in per.values() for k in g} - {"FETCH_SIZE", "WRITE_SIZE", "duration_ns"})
+    if others:
+        lines += ["", "other counters, mean per dispatch (columns in the order above):"]
+        for k in others:
+            lines.append("  %-40s %s" % (k, " ".join("%10.4g" % float(np.mean(per.get(lb, {}).get(k, [float("nan")])))
+                                                     for lb in HBM_PROBE_ORDER)))
+    print("\n".join(lines))
 
 
 def pmc_summary(fetch_dir, write_dir, workload):
@@ -868,6 +1006,9 @@ def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
+        return
+    if args.hbm_summary:
+        hbm_summary(args.hbm_summary, args.workload)
         return
     if args.stats_summary:
         stats_summary(args.stats_summary)

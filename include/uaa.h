@@ -349,6 +349,8 @@ int usp_attn_fwd_lse_gather(int dtype, int world, int rank, const int64_t* seq_o
 #define USP_KERNEL_GENERAL_MASKED 3  /* bf16, a mask with units on its diagonal: the general kernel */
 #define USP_KERNEL_GENERAL_SPLIT 4   /* bf16, keys of the last round's units split: the general kernel */
 #define USP_KERNEL_PIPELINED 5       /* bf16, D = 128: the software-pipelined kernel */
+#define USP_KERNEL_PIPELINED_DIAG 6  /* bf16, D = 128, a mask whose keys form one increasing piece:
+                                        the pipelined kernel, diagonal units masked row by row */
 int usp_attn_kernel(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, int o_dtype,
                     const usp_mask* mask, size_t workspace_bytes);
 

@@ -874,16 +874,22 @@ static bool general_args(const AttnArgs& a0, AttnArgs& a)
     return true;
 }
 
-static bool use_p32(int D, const AttnArgs& a)
+// 0: the general kernel; 1: the pipelined kernel; 2: its DIAG form (units
+// on a mask diagonal)
+static int use_p32(int D, const AttnArgs& a)
 {
-    return D == 128 && a.split_p <= 1 && attn_p32_fits(a.Sk, a.row_heads) && p32_on() && attn_p32_mask_ok(a);
+    if (!(D == 128 && a.split_p <= 1 && attn_p32_fits(a.Sk, a.row_heads) && p32_on())) return 0;
+    if (attn_p32_mask_ok(a)) return 1;
+    return attn_p32_diag_ok(a) ? 2 : 0;
 }
 
 int attn_bf16_kernel_choice(int D, const AttnArgs& a0)
 {
     AttnArgs a;
     if (!general_args(a0, a)) return USP_KERNEL_NONE;
-    if (use_p32(D, a)) return USP_KERNEL_PIPELINED;
+    const int p = use_p32(D, a);
+    if (p == 1) return USP_KERNEL_PIPELINED;
+    if (p == 2) return USP_KERNEL_PIPELINED_DIAG;
     if (a.masked) return USP_KERNEL_GENERAL_MASKED;
     return a.split_p > 1 ? USP_KERNEL_GENERAL_SPLIT : USP_KERNEL_GENERAL;
 }
@@ -895,7 +901,7 @@ hipError_t launch_attn_bf16(int D, int o_dtype, const AttnArgs& a0, hipStream_t 
     const int64_t units = (int64_t)a.n_qtiles * a.H * a.B;
     const int64_t blocks = a.split_p > 1 ? a.n_whole + (units - a.n_whole) * a.split_p : units;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    if (use_p32(D, a)) return launch_attn_p32(o_dtype, a0, s);
+    if (const int p = use_p32(D, a)) return launch_attn_p32(o_dtype, p == 2, a0, s);
     const dim3 grid((unsigned)blocks);
     const bool ob = o_dtype == UAA_BF16;
     if (D == 128) return ob ? launch_d<128, true>(a, grid, s) : launch_d<128, false>(a, grid, s);

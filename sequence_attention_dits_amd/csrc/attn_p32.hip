@@ -165,7 +165,15 @@ __device__ __forceinline__ void p_pin_p(p_u32x4 (&p)[4])
 }
 __device__ __forceinline__ void p_pin_f(float& x) { asm volatile("" : "+v"(x)); }
 
-template <bool OUT_BF16>
+// DIAG: a masked call whose key map is one increasing piece, so that the
+// keys each query row may see are a prefix of the block (causal by
+// position: basic and stripe layouts, a zigzag block of one chunk).  Each
+// unit then runs only its live key tiles -- those before the last allowed
+// key of its last row -- and the rows of a tile on a unit's diagonal are
+// masked one by one (each lane's row has its own allowed-key count); units
+// run longest first.  Without DIAG every unit runs every key tile (a masked
+// call only when each unit sees every key of the block or none).
+template <bool OUT_BF16, bool DIAG>
 __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArgs a)
 {
     // V stages, K stages, Q staging: every operand read is a per-lane
@@ -176,7 +184,18 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
     p_lds_u8* const L = (p_lds_u8*)smem;
 
     int64_t qt, hh, b;
-    decode_tile(a, qt, hh, b);
+    if (DIAG && gridDim.x % 8u == 0u && (gridDim.x / 8u) % (uint32_t)a.n_qtiles == 0u) {
+        // every XCD holds whole heads: each XCD's workgroups (blockIdx =
+        // 8 j + x on XCD x) take its heads' q tiles last-first with the heads
+        // interleaved -- later rows see at least as many keys under every
+        // mask kind, so the longest units are dispatched first
+        const uint32_t nq = (uint32_t)a.n_qtiles, per = gridDim.x / 8u, hpx = per / nq;
+        const uint32_t x = blockIdx.x % 8u, j = blockIdx.x / 8u;
+        unit_coords(a, x * per + (j % hpx) * nq + (nq - 1u - j / hpx), qt, hh, b);
+    } else {
+        decode_tile(a, qt, hh, b);
+        if (DIAG) qt = a.n_qtiles - 1 - qt;
+    }
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hg = lane >> 5;
@@ -187,7 +206,18 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
     const int64_t i = r0 + l32;                    // this lane's row
     const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + ((b * Sk) * RH + h_in) * kPD * 2;
     const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + ((b * Sk) * RH + h_in) * kPD * 2;
-    const int n = (int)((Sk + kPBN - 1) / kPBN);
+    // key tiles this unit runs, and with DIAG this lane's row's allowed keys
+    // (a prefix of the block; rows past Sq are never stored and see all)
+    int n = (int)((Sk + kPBN - 1) / kPBN);
+    int32_t kcnt = (int32_t)Sk;
+    if constexpr (DIAG) {
+        const int64_t t0 = qt * kPBM, t1 = t0 + kPBM < Sq ? t0 + kPBM : Sq;
+        int64_t qlo, qhi;
+        pos_range(a.qmap, t0, t1, qlo, qhi);
+        const int64_t live = allowed_prefix(a.kmap.base0, a.kmap.stride, qhi, Sk);
+        n = (int)((live + kPBN - 1) / kPBN);
+        if (i < Sq) kcnt = (int32_t)allowed_prefix(a.kmap.base0, a.kmap.stride, pos_of(a.qmap, i), Sk);
+    }
 
     // One descriptor per tensor over this head's keys (rows from Sk on read
     // as zero; the launcher checks that the range fits 32 bits) and this
@@ -217,7 +247,7 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
         int64_t qlo, qhi, klo, khi;
         pos_range(a.qmap, t0, t1, qlo, qhi);
         pos_range(a.kmap, 0, Sk, klo, khi);
-        if (klo > qhi) {
+        if (klo > qhi || (DIAG && n == 0)) {
             if (!a.acc) {
                 constexpr int C = (OUT_BF16 ? 2 : 4) * kPD / 16;   // 16-byte pieces per output row
                 for (int j = lane; j < 32 * C; j += 64) {
@@ -351,9 +381,16 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
             for (int v = 0; v < 16; ++v)
                 if (32 * jb + 8 * (v >> 2) + (v & 3) >= ll) s[jb][v] = -INFINITY;
     };
+    // keys of tile t this lane's row may see (a prefix of the tile): the
+    // ragged end of the block, and with DIAG the row's own allowed count
     auto key_lim = [&](int t) {
-        const int64_t r = Sk - (int64_t)t * kPBN;
+        const int64_t r = (DIAG ? (int64_t)kcnt : Sk) - (int64_t)t * kPBN;
         return r <= 0 ? 0 : (r >= kPBN ? kPBN : (int)r);
+    };
+    // some lane of the wave has a masked key in tile t (uniform)
+    auto tile_masked = [&](int lim) {
+        if constexpr (DIAG) return __builtin_amdgcn_ballot_w64(lim < kPBN) != 0;
+        return lim < kPBN;
     };
     // Row maximum as 16 single instructions: ten three-way maxima of the
     // lane's 32 scores, one two-way, then the tree.
@@ -432,7 +469,7 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
         for (int r = 0; r < KPF; ++r) kop[r] = kread(0, r >> 1, r & 1);
 #pragma unroll
         for (int r = 0; r < 16; ++r) score_mma(sacc[0], kop, 0, r);
-        if (key_lim(0) < kPBN) mask_keys(sacc[0], key_lim(0));
+        if (tile_masked(key_lim(0))) mask_keys(sacc[0], key_lim(0));
         p_fence_s(sacc[0]);
 #pragma unroll
         for (int j = 0; j < 16; ++j) max_op(sacc[0], j);
@@ -493,7 +530,7 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
         __builtin_amdgcn_s_setprio(0);
         p_pin_p(pw);
         const int lim = key_lim(t + 1);
-        if (lim < kPBN) mask_keys(sacc[P ^ 1], lim);
+        if (tile_masked(lim)) mask_keys(sacc[P ^ 1], lim);
         // [B] O += V_t^T P_t beside the row maximum of tile t+1 (its scores
         // were written at least two matrix instructions, > 60 cycles,
         // before), with this step's copies among them
@@ -663,6 +700,13 @@ bool attn_p32_fits(int64_t Sk, int64_t row_heads)
     return n > 0 && Sk * row_heads * kPD * 2 < (int64_t)0xF0000000 && pad * 10 <= n;
 }
 
+bool attn_p32_diag_ok(const AttnArgs& a)
+{
+    // one increasing piece of keys covers the block (the allowed keys of a
+    // row are a prefix), positions fit the kernel's 32-bit counts
+    return a.masked && a.Sq > 0 && a.Sk > 0 && a.kmap.seg_len >= a.Sk && a.kmap.stride >= 1;
+}
+
 bool attn_p32_mask_ok(const AttnArgs& a)
 {
     if (!a.masked) return true;
@@ -677,7 +721,7 @@ bool attn_p32_mask_ok(const AttnArgs& a)
     return true;
 }
 
-hipError_t launch_attn_p32(int o_dtype, const AttnArgs& a0, hipStream_t s)
+hipError_t launch_attn_p32(int o_dtype, bool diag, const AttnArgs& a0, hipStream_t s)
 {
     AttnArgs a = a0;
     a.n_qtiles = (int32_t)((a.Sq + kPBM - 1) / kPBM);
@@ -685,8 +729,12 @@ hipError_t launch_attn_p32(int o_dtype, const AttnArgs& a0, hipStream_t s)
     if (units <= 0) return hipSuccess;
     if (units > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)units), block(64 * kPWaves);
-    if (o_dtype == UAA_BF16) return launch_kernel(attn_p32_kernel<true>, grid, block, 0, s, a);
-    return launch_kernel(attn_p32_kernel<false>, grid, block, 0, s, a);
+    if (diag) {
+        if (o_dtype == UAA_BF16) return launch_kernel(attn_p32_kernel<true, true>, grid, block, 0, s, a);
+        return launch_kernel(attn_p32_kernel<false, true>, grid, block, 0, s, a);
+    }
+    if (o_dtype == UAA_BF16) return launch_kernel(attn_p32_kernel<true, false>, grid, block, 0, s, a);
+    return launch_kernel(attn_p32_kernel<false, false>, grid, block, 0, s, a);
 }
 
 }  // namespace uaa

@@ -137,7 +137,10 @@ int attn_bf16_kernel_choice(int D, const AttnArgs& a);
 bool attn_p32_fits(int64_t Sk, int64_t row_heads);
 // masked calls: the rows of every 256-row unit see every key of the block or none
 bool attn_p32_mask_ok(const AttnArgs& a);
-hipError_t launch_attn_p32(int o_dtype, const AttnArgs& a, hipStream_t s);
+// masked calls whose keys are one increasing piece: units on the diagonal
+// run their live tiles with rows masked one by one (the kernel's DIAG form)
+bool attn_p32_diag_ok(const AttnArgs& a);
+hipError_t launch_attn_p32(int o_dtype, bool diag, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_fp32(int D, const AttnArgs& a, hipStream_t s);
 
 // --------------------------------------------------------------------------

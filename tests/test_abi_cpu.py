@@ -357,6 +357,13 @@ def test_kernel_query_names_the_kernel_of_each_case():
     assert K.usp_attn_kernel(lc, 4096, mask=zz(0)) == K.USP_KERNEL_PIPELINED      # wholly in the past
     assert K.usp_attn_kernel(lc, 4096, mask=zz(3)) == K.USP_KERNEL_PIPELINED      # units see all or none
     assert K.usp_attn_kernel((1, 300, 2, 128), 300, mask=K.mask_causal()) == K.USP_KERNEL_GENERAL_MASKED
+    # units on a diagonal: the pipelined kernel's DIAG form where the keys are one increasing piece
+    assert K.usp_attn_kernel((1, 768, 2, 128), 768, mask=K.mask_causal()) == K.USP_KERNEL_PIPELINED_DIAG
+    assert K.usp_attn_kernel(lc, 4096, mask=zz(1)) == K.USP_KERNEL_PIPELINED_DIAG
+    assert K.usp_attn_kernel(lc, 4096, mask=zz(6)) == K.USP_KERNEL_PIPELINED_DIAG
+    assert K.usp_attn_kernel((1, 768, 2, 128), 768, mask=K.mask_stripe(4, 1, 2)) == K.USP_KERNEL_PIPELINED_DIAG
+    two_key_chunks = K.mask_zigzag(384, [1, 6], [1, 6])   # keys in two pieces: the general kernel
+    assert K.usp_attn_kernel((1, 768, 2, 128), 768, mask=two_key_chunks) == K.USP_KERNEL_GENERAL_MASKED
     with pytest.raises(uaa.UaaError) as e:
         K.usp_attn_kernel(flux, 2304, mask=K.usp_mask(kind=7))
     assert e.value.status == K.UAA_ERR_INVALID_ARG
