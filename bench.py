@@ -809,17 +809,18 @@ def _hbm_dispatches(d):
                     if "Counter_Name" in r:
                         e["c"][r["Counter_Name"]] = float(r["Counter_Value"])
     order = sorted(recs)
-    # the last of the three big copies: the copy dispatch followed by the first round's permute
-    last_cal = None
-    for i, did in enumerate(order):
-        if "copy" in recs[did]["name"].lower() and i + 1 < len(order) and \
-                "permute_kernel<0>" in recs[order[i + 1]]["name"]:
-            last_cal = i
+    # the first round: the first two SEQ2HEAD launches followed by a HEAD2SEQ
+    # and a merge (the set initialisation before it has no such run)
+    sig = ("permute_kernel<0>", "permute_kernel<0>", "permute_kernel<1>", "merge_kernel")
+    first = None
+    for i in range(len(order) - len(sig)):
+        if all(k in recs[order[i + j]]["name"] for j, k in enumerate(sig)):
+            first = i
             break
-    if last_cal is None:
+    if first is None:
         return []
     out = []
-    for j, did in enumerate(order[last_cal + 1:]):
+    for j, did in enumerate(order[first:]):
         e = recs[did]
         out.append((HBM_PROBE_ORDER[j % len(HBM_PROBE_ORDER)], e["c"], e["ns"], e["name"]))
     return out
@@ -847,8 +848,6 @@ def hbm_summary(dirs, workload):
     scale = {}
     for d in dirs:
         # calibration: the 1 GiB copies' FETCH_SIZE / WRITE_SIZE (KiB)
-        for counter, vs in _pmc_values(d, "FETCH_SIZE").items():
-            pass
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
             big = [v for k, vv in _pmc_values(d, counter).items() if "copy" in k.lower() for v in vv
                    if v * 1024 > PMC_COPY_BYTES / 4]
@@ -896,6 +895,20 @@ def hbm_summary(dirs, workload):
             lines.append("  %-40s %s" % (k, " ".join("%10.4g" % float(np.mean(per.get(lb, {}).get(k, [float("nan")])))
                                                      for lb in HBM_PROBE_ORDER)))
     print("\n".join(lines))
+
+
+def _pmc_values(d, counter):
+    """{kernel name: [per-dispatch values]} of one counter from a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
 
 
 def pmc_summary(fetch_dir, write_dir, workload):
