@@ -109,6 +109,11 @@ def parse():
                         "merge launch (auto: per workload)")
     p.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough for 1 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--kernels-only", metavar="NAMES",
+                   help="only time the named launch kinds of the step (comma-separated, e.g. attn,attn_acc), "
+                        "as the per-kernel figures of the line are timed; for kernel traces")
+    p.add_argument("--no-workloads", action="store_true",
+                   help="with the default workload, skip the other three workloads' figures")
     p.add_argument("--no-backward", action="store_true", help="skip the backward variant")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--pmc-probe", nargs="?", const="attn", choices=["attn", "hbm"],
@@ -1015,46 +1020,73 @@ def stats_summary(d):
                                                 float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
 
 
-def main():
-    args = parse()
-    if args.pmc_summary:
-        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
-        return
-    if args.hbm_summary:
-        hbm_summary(args.hbm_summary, args.workload)
-        return
-    if args.stats_summary:
-        stats_summary(args.stats_summary)
-        return
-    if args.counter_summary:
-        counter_summary(args.counter_summary)
-        return
-    if args.gpus != 1:
-        print("bench.py measures one rank's share on one GPU; --gpus %d is not supported "
-              "(the library has no collective or multi-GPU path)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
-    import torch
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        sys.exit(2)
-    torch.cuda.set_device(0)
-    if args.pmc_probe:
-        pmc_probe(args)
-        return
-    cfg_id, desc = WORKLOADS[args.workload]
+def time_launches(share, names, steps: int, n_sets: int) -> dict:
+    """Per-launch microseconds of each named launch kind of the step: `steps`
+    rounds back to back over the rotating sets, every launch on its set's own
+    buffers (timing_bufs: inputs and outputs cold), between two HIP events on
+    the launch stream; a spin kernel first gives the host a head start so
+    that no launch waits on the host."""
+    torch = share.torch
+    for s_ in range(n_sets):   # allocated before the timed region
+        share.timing_bufs(s_)
+    torch.cuda.synchronize()
+    log = {}
+    for name in names:
+        a_ev = torch.cuda.Event(enable_timing=True)
+        b_ev = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2.4e9 * 0.02))
+        a_ev.record()
+        n = 0
+        for i in range(steps):
+            n += share.launch_one(name, i % n_sets, timing=True)
+        b_ev.record()
+        torch.cuda.synchronize()
+        log[name] = 1e3 * a_ev.elapsed_time(b_ev) / n
+    return log
+
+
+def n_sets_for(workload: str) -> int:
+    """Rotating input sets whose inputs exceed 1 GiB (over 4x the 256 MB
+    Infinity Cache), at least 2."""
     import synth
-    c = synth.CONFIGS[cfg_id]
-    ring = args.workload in RING_WORKLOADS
-    # enough rotating input sets to exceed 1 GiB of inputs (> 4x the MALL)
-    if ring:
+    c = synth.CONFIGS[WORKLOADS[workload][0]]
+    if workload in RING_WORKLOADS:
         sq = c["S"] // c["chunks"] * len(c["q_chunks"]) if "chunks" in c else c["shards"][0]
         per_set = (sq + 2 * c["S"]) * c["B"] * c["H"] * c["D"] * 2
     else:
         per_set = 3 * c["B"] * c["S"] * c["H"] * c["D"] * 2 + c["B"] * c["S"] * (c["H"] // 2) * c["D"] * 2
-    n_sets = args.sets or max(2, int(math.ceil((1 << 30) / per_set)))
-    share = make_share(args.workload, n_sets, args.overlap_chunks, args.ring_update)
+    return max(2, int(math.ceil((1 << 30) / per_set)))
 
-    for i in range(max(args.warmup, 1)):
+
+def kernels_only(args):
+    """--kernels-only: only the per-launch timing of the named launch kinds
+    (the same loop that gives the bench line's per-kernel figures), so that a
+    kernel trace of this command averages exactly those launches."""
+    share = make_share(args.workload, args.sets or n_sets_for(args.workload))
+    names = [n for n in args.kernels_only.split(",") if n]
+    for n in names:
+        if n not in share.kernel_names:
+            raise SystemExit("unknown launch kind %r (one of %s)" % (n, ", ".join(share.kernel_names)))
+    share.step(0)
+    log = time_launches(share, names, args.steps, len(share.sets))
+    print(json.dumps({"workload": args.workload, "steps": args.steps, "us_per_launch": log}), flush=True)
+
+
+def measure(args, workload: str, steps: int, warmup: int, full: bool) -> dict:
+    """Build one workload's step, time it (graph replays) and its launches
+    (back to back, cold), run the oracle baseline on a sample and compare
+    its rows with the GPU step; the variants (fused gather, backward) and
+    the command-line overrides of the launch configuration only with full."""
+    import torch
+    cfg_id, desc = WORKLOADS[workload]
+    import synth
+    c = synth.CONFIGS[cfg_id]
+    ring = workload in RING_WORKLOADS
+    n_sets = (args.sets if full else 0) or n_sets_for(workload)
+    share = make_share(workload, n_sets, args.overlap_chunks if full else "auto", args.ring_update if full else "auto")
+
+    for i in range(max(warmup, 1)):
         share.step(i % n_sets)
     torch.cuda.synchronize()
 
@@ -1067,7 +1099,7 @@ def main():
             share.step(s_)
         graphs.append(g)
     torch.cuda.synchronize()
-    for i in range(args.warmup):
+    for i in range(warmup):
         graphs[i % n_sets].replay()
     torch.cuda.synchronize()
 
@@ -1089,16 +1121,16 @@ def main():
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
-    for i in range(args.steps):
+    for i in range(steps):
         graphs[i % n_sets].replay()
     t_end.record()
     torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_step = t_start.elapsed_time(t_end) / steps
 
     # the fused-gather variant of the FLUX-type step (SEQ2HEAD inside the
     # attention's loads), checked bit for bit against the step above
     variants = {}
-    if not ring:
+    if full and not ring:
         share.step(0)
         torch.cuda.synchronize()
         ref_o, ref_l = (t.clone() for t in share.result())
@@ -1112,17 +1144,17 @@ def main():
             with torch.cuda.graph(g):
                 share.step_fused(s_)
             fgraphs.append(g)
-        for i in range(args.warmup):
+        for i in range(warmup):
             fgraphs[i % n_sets].replay()
         torch.cuda.synchronize()
         f0 = torch.cuda.Event(enable_timing=True)
         f1 = torch.cuda.Event(enable_timing=True)
         f0.record()
-        for i in range(args.steps):
+        for i in range(steps):
             fgraphs[i % n_sets].replay()
         f1.record()
         torch.cuda.synchronize()
-        ms_fused = f0.elapsed_time(f1) / args.steps
+        ms_fused = f0.elapsed_time(f1) / steps
         variants["fused_gather"] = {
             "ms_per_step": round(ms_fused, 4),
             "value": round(sum(share.attn_flops(c_) for c_ in range(len(share.ring))) / (ms_fused * 1e-3) / 1e12, 2),
@@ -1132,30 +1164,14 @@ def main():
         del fgraphs
 
     # the backward of the step's attention (usp_attn_bwd_delta + usp_attn_bwd)
-    if not args.no_backward:
-        variants["backward"] = backward_variant(share, cfg_id, args.steps, args.warmup)
+    if full and not args.no_backward:
+        variants["backward"] = backward_variant(share, cfg_id, steps, warmup)
 
     # timed region 2: per-kernel durations.  Each launch of the step is
     # repeated back to back over the rotating input sets between two HIP
     # events on the launch stream; a spin kernel first gives the host a head
     # start so no launch waits on the host.
-    log = {}
-    for s_ in range(n_sets):   # allocated before the timed region
-        share.timing_bufs(s_)
-    torch.cuda.synchronize()
-    for name in share.kernel_names:
-        a_ev = torch.cuda.Event(enable_timing=True)
-        b_ev = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        torch.cuda._sleep(int(2.4e9 * 0.02))
-        a_ev.record()
-        n = 0
-        for i in range(args.steps):
-            n += share.launch_one(name, i % n_sets, timing=True)
-        b_ev.record()
-        torch.cuda.synchronize()
-        log[name] = 1e3 * a_ev.elapsed_time(b_ev) / n
-    torch.cuda.synchronize()
+    log = time_launches(share, share.kernel_names, steps, n_sets)
 
     n_attn = len(share.kv) if ring else len(share.ring)
     attn_flops = sum(share.attn_flops(c_) for c_ in range(n_attn))
@@ -1201,8 +1217,8 @@ def main():
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -1213,7 +1229,7 @@ def main():
         "config": config,
         "roofline": {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic() if args.workload == "flux1024" else None,
+                     "traffic": measured_traffic() if workload == "flux1024" else None,
                      "kernel": attn_kernel_label(share, ring),
                      "launch_us": round(attn_us, 2), "flops_per_launch": attn_flops_launch},
         "kernels": kernels,
@@ -1223,7 +1239,54 @@ def main():
     if not ring:
         out["permute_GBps"] = kernels["seq2head_permute"]["GB/s"]
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = (ring_cpu_baseline if ring else cpu_baseline)(share, args.cpu_seconds)
+        out["cpu_baseline"] = (ring_cpu_baseline if ring else cpu_baseline)(
+            share, args.cpu_seconds if full else args.cpu_seconds / 3)
+    del graphs, share
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
+        return
+    if args.hbm_summary:
+        hbm_summary(args.hbm_summary, args.workload)
+        return
+    if args.stats_summary:
+        stats_summary(args.stats_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
+    if args.gpus != 1:
+        print("bench.py measures one rank's share on one GPU; --gpus %d is not supported "
+              "(the library has no collective or multi-GPU path)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    if args.pmc_probe:
+        pmc_probe(args)
+        return
+    if args.kernels_only:
+        kernels_only(args)
+        return
+    out = measure(args, args.workload, args.steps, args.warmup, True)
+    if args.workload == "flux1024" and not args.no_workloads:
+        # the other workloads in their default launch configuration, each
+        # with its own oracle sample (the driver's one line carries all five)
+        out["workloads"] = {}
+        for w in ("flux1008", "qwen1328", "longctx"):
+            r = measure(args, w, min(args.steps, 20), args.warmup, False)
+            out["workloads"][w] = {k: r[k] for k in ("value", "unit", "ms_per_step", "steps", "config", "roofline",
+                                                      "kernels", "cpu_baseline") if k in r}
+        out["workloads_note"] = ("the tiny ragged fp32 share (257 tokens, 129/128) is a correctness case: every "
+                                 "row is checked in the GPU tests, it is not timed")
     print(json.dumps(out), flush=True)
 
 

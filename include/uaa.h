@@ -461,6 +461,12 @@ const char* uaa_last_error(void);
 /* uaa_abi_version -- version of this header's contract (currently 1). */
 int uaa_abi_version(void);
 
+/* uaa_build_id -- sha256 (hex) of the sources, headers and flags this
+ * library was built from, as the build script computes it ("unknown" when
+ * built without it); lets a caller check that a library matches its
+ * sources.  Static storage, never freed. */
+const char* uaa_build_id(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -103,6 +103,9 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError("libuaa.so is not built (%s); run "
                                "`python -m sequence_attention_dits_amd.build`" % LIB_PATH)
         l = ctypes.CDLL(LIB_PATH)
+        l.uaa_build_id.restype = ctypes.c_char_p
+        l.uaa_build_id.argtypes = []
+        _check_build(l.uaa_build_id().decode())
         l.uaa_seq2head_permute.restype = ctypes.c_int
         l.uaa_seq2head_permute.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_p, _c_p,
                                            _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_p, _c_p, _c_p]
@@ -150,6 +153,18 @@ def lib() -> ctypes.CDLL:
         l.uaa_abi_version.argtypes = []
         _lib = l
     return _lib
+
+
+def _check_build(built: str) -> None:
+    """The library must have been built from the sources beside it (when
+    they are there): a stale build is refused, not run."""
+    from . import build
+    if not os.path.isdir(build.CSRC):
+        return
+    want = build.source_id()
+    if built != want:
+        raise RuntimeError("libuaa.so was built from other sources (build id %s, sources %s); rebuild with "
+                           "`python -m sequence_attention_dits_amd.build`" % (built[:12], want[:12]))
 
 
 def _check(status: int) -> None:

@@ -30,9 +30,25 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
+def source_id() -> str:
+    """sha256 over every source and header the library is built from (and
+    the build flags): built into the library, where uaa_build_id() returns
+    it, and compared by the binding at load time, so a library left over
+    from other sources is refused instead of run."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in SOURCES + HEADERS:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(HERE, "..", "include", "uaa.h"), "rb") as f:
+        h.update(b"uaa.h\0" + f.read())
+    h.update(" ".join(CFLAGS).encode())
+    return h.hexdigest()
+
+
+def _compile(src: str, build_id: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, '-DUAA_BUILD_ID="%s"' % build_id, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only feature flag: drop that note
     noise = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
@@ -46,8 +62,9 @@ def _compile(src: str) -> str:
 
 def build_library(jobs: int = 8, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    build_id = source_id()
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, build_id), SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -53,6 +53,11 @@ UAA_EXPORT const char* uaa_last_error(void) { return g_err; }
 
 UAA_EXPORT int uaa_abi_version(void) { return 1; }
 
+#ifndef UAA_BUILD_ID
+#define UAA_BUILD_ID "unknown"
+#endif
+UAA_EXPORT const char* uaa_build_id(void) { return UAA_BUILD_ID; }
+
 UAA_EXPORT int uaa_split_offsets(int64_t total, int parts, int64_t* off)
 {
     if (parts < 1) return fail(UAA_ERR_INVALID_ARG, "split: parts must be >= 1, got %d", parts);
@@ -420,7 +425,9 @@ static int attn_impl(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, in
         if (plan.p > 1 && workspace_bytes >= (size_t)plan_ws_bytes(plan, B, H, Sq)) {
             a.split_p = plan.p;
             a.n_whole = plan.n_whole;
-            a.ws = workspace;
+            // a query has no workspace pointer: any non-null value stands in
+            // for it, since the plan only checks that there is one
+            a.ws = query ? reinterpret_cast<void*>(uintptr_t(256)) : workspace;
         }
     }
     if (query) {

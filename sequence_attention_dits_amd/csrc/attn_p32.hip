@@ -32,12 +32,11 @@
 //    not see them as matrix instructions, so vector code touching their
 //    results sits behind explicit wait states (fences below) or, inside a
 //    step, at least two matrix instructions later;
-//  * the loop body is one straight block of six steps (two score-register
-//    parities x three LDS stages) with no exit in the middle: exits make the
-//    register allocator move the AGPR accumulators behind the matrix
-//    instructions still writing them.  Steps past the last tile run on fully
-//    masked tiles (nothing added), so the launcher uses this kernel only
-//    where that padding is small;
+//  * the loop body is six steps (two score-register parities x three LDS
+//    stages) with a uniform exit after each step, so a unit runs exactly its
+//    tile count; the inline-assembly accumulators stay where the matrix
+//    instructions write them across those exits (checked in the ISA: the
+//    steps' matrix blocks have no accumulator copies);
 //  * the softmax results are pinned with an empty asm before the branch
 //    that follows them; otherwise IR-level sinking moves the softmax below
 //    the branch, away from the matrix instructions it is meant to run beside;
@@ -568,13 +567,21 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    for (int t = 0; t < n; t += 6) {
+    // six steps per iteration (two score parities x three stages), left
+    // after whichever step reaches the unit's tile count
+    for (int t = 0; n > 0; t += 6) {
         step(I0{}, I0{}, t);
+        if (t + 1 >= n) break;
         step(I1{}, I1{}, t + 1);
+        if (t + 2 >= n) break;
         step(I0{}, I2{}, t + 2);
+        if (t + 3 >= n) break;
         step(I1{}, I0{}, t + 3);
+        if (t + 4 >= n) break;
         step(I0{}, I1{}, t + 4);
+        if (t + 5 >= n) break;
         step(I1{}, I2{}, t + 5);
+        if (t + 6 >= n) break;
     }
     // the last copies (into stages nothing reads) have landed and every wave
     // is done with the stages before the LDS is reused; O is final
@@ -692,12 +699,9 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
 
 bool attn_p32_fits(int64_t Sk, int64_t row_heads)
 {
-    // the key range of one head must fit the 32-bit buffer range, and the
-    // fully masked steps that pad the tile count to a multiple of six must
-    // be at most a tenth of the work
+    // the key range of one head must fit the 32-bit buffer range
     const int64_t n = (Sk + kPBN - 1) / kPBN;
-    const int64_t pad = (6 - n % 6) % 6;
-    return n > 0 && Sk * row_heads * kPD * 2 < (int64_t)0xF0000000 && pad * 10 <= n;
+    return n > 0 && Sk * row_heads * kPD * 2 < (int64_t)0xF0000000;
 }
 
 bool attn_p32_diag_ok(const AttnArgs& a)

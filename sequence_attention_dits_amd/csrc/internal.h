@@ -133,7 +133,7 @@ int64_t attn_bf16_units(int64_t B, int64_t H, int64_t Sq);
 hipError_t launch_attn_bf16(int D, int o_dtype, const AttnArgs& a, hipStream_t s);
 // the USP_KERNEL_* code of the kernel launch_attn_bf16 runs for these arguments
 int attn_bf16_kernel_choice(int D, const AttnArgs& a);
-// D = 128, no key split, no unit on a mask diagonal: the software-pipelined kernel, where its padding to a multiple of six key tiles is small
+// D = 128, no key split: the software-pipelined kernel, where one head's keys fit its 32-bit buffer range
 bool attn_p32_fits(int64_t Sk, int64_t row_heads);
 // masked calls: the rows of every 256-row unit see every key of the block or none
 bool attn_p32_mask_ok(const AttnArgs& a);

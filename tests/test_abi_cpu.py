@@ -339,9 +339,10 @@ def test_split_offsets_validation(total, parts, text):
 
 def test_kernel_query_names_the_kernel_of_each_case():
     """usp_attn_kernel: the workloads' launches and the selection rules
-    (pipelined for unmasked D = 128 bf16 whose key tiles pad to a multiple
-    of six by at most a tenth, and for masks whose 256-row units see every
-    key of the block or none; the general kernel otherwise).  Host only."""
+    (pipelined for bf16 D = 128 without a key split: unmasked, masks whose
+    256-row units see every key of the block or none, and in its DIAG form
+    masks whose keys are one increasing piece; the general kernel
+    otherwise).  Host only."""
     K = uaa
     bf, f32 = __import__("torch").bfloat16, __import__("torch").float32
     flux = (1, 4608, 12, 128)
@@ -350,13 +351,15 @@ def test_kernel_query_names_the_kernel_of_each_case():
     assert K.usp_attn_kernel(flux, 2304, f32) == K.USP_KERNEL_FP32
     assert K.usp_attn_kernel(flux, 2304, bf, f32) == K.USP_KERNEL_PIPELINED
     assert K.usp_attn_kernel((1, 4608, 12, 64), 2304) == K.USP_KERNEL_GENERAL
-    assert K.usp_attn_kernel((1, 300, 2, 128), 64 * 7) == K.USP_KERNEL_GENERAL   # 7 tiles pad by 5 > 0.7
+    assert K.usp_attn_kernel((1, 300, 2, 128), 64 * 7) == K.USP_KERNEL_PIPELINED   # any tile count
+    assert K.usp_attn_kernel((1, 300, 2, 128), 1) == K.USP_KERNEL_PIPELINED
     assert K.usp_attn_kernel((0, 300, 2, 128), 64) == K.USP_KERNEL_NONE
     lc = (1, 8192, 32, 128)
     zz = lambda c: K.mask_zigzag(4096, [1, 6], [c])
     assert K.usp_attn_kernel(lc, 4096, mask=zz(0)) == K.USP_KERNEL_PIPELINED      # wholly in the past
     assert K.usp_attn_kernel(lc, 4096, mask=zz(3)) == K.USP_KERNEL_PIPELINED      # units see all or none
-    assert K.usp_attn_kernel((1, 300, 2, 128), 300, mask=K.mask_causal()) == K.USP_KERNEL_GENERAL_MASKED
+    assert K.usp_attn_kernel((1, 300, 2, 128), 300, mask=K.mask_causal()) == K.USP_KERNEL_PIPELINED_DIAG
+    assert K.usp_attn_kernel((1, 300, 2, 64), 300, mask=K.mask_causal()) == K.USP_KERNEL_GENERAL_MASKED
     # units on a diagonal: the pipelined kernel's DIAG form where the keys are one increasing piece
     assert K.usp_attn_kernel((1, 768, 2, 128), 768, mask=K.mask_causal()) == K.USP_KERNEL_PIPELINED_DIAG
     assert K.usp_attn_kernel(lc, 4096, mask=zz(1)) == K.USP_KERNEL_PIPELINED_DIAG

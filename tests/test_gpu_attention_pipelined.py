@@ -1,13 +1,14 @@
 """GPU parity of the software-pipelined attention kernel (unmasked, D = 128,
 bf16 inputs, no key split) against the fp64 oracle, every row.
 
-The library launches that kernel when the key tiles of a call (64 keys
-each) pad to a multiple of six by at most a tenth, so these shapes are
-chosen to reach it: 6, 11 and 12 key tiles, with and without a ragged last
-tile, ragged query rows (a partial last 256-row workgroup and waves past the
-end), several heads and batches, bf16 and fp32 output, a two-block Ring pass
-accumulated in place, and scores large enough to make the running maximum
-rise mid-row (the rescale path).
+The kernel's loop body is six tile steps (two score parities x three LDS
+stages) with an exit after each, so the key-tile counts here (64 keys a
+tile) end the loop at every one of the six positions and after one and
+two whole bodies: 1, 2, 3, 4, 5, 6, 7, 11, 12 and 13 tiles, with and without
+a ragged last tile, ragged query rows (a partial last 256-row workgroup and
+waves past the end), several heads and batches, bf16 and fp32 output, a
+two-block Ring pass accumulated in place, and scores large enough to make
+the running maximum rise mid-row (the rescale path).
 """
 
 import math
@@ -25,10 +26,17 @@ pytestmark = pytest.mark.gpu
 
 CASES = [
     # name, B, Sq, Sk, H
+    ("tiles1_tail", 1, 200, 50, 2),
+    ("tiles2", 1, 300, 128, 1),
+    ("tiles3_tail", 2, 260, 150, 2),
+    ("tiles4", 1, 256, 256, 1),
+    ("tiles5_tail", 1, 513, 300, 1),
     ("tiles6_exact", 1, 256, 384, 2),
     ("tiles6_ragged_keys_rows", 2, 300, 367, 3),
-    ("tiles11_pad1", 1, 513, 700, 1),
+    ("tiles7_tail", 1, 300, 420, 1),
+    ("tiles11", 1, 513, 700, 1),
     ("tiles12_tail63", 1, 100, 767, 2),
+    ("tiles13", 1, 256, 832, 1),
 ]
 
 
