@@ -718,8 +718,9 @@ KERNEL_NAMES = {
     2: "attn_bf16_kernel<128, false, true, false>",
     3: "attn_bf16_kernel<128, true, true, false>",
     4: "attn_bf16_kernel<128, false, true, true>",
-    5: "attn_p32_kernel<true, false>",
-    6: "attn_p32_kernel<true, true>",
+    5: "attn_p32_kernel<true, false, false>",
+    6: "attn_p32_kernel<true, true, false>",
+    7: "attn_p32_kernel<true, false, true>",
 }
 
 
@@ -735,8 +736,9 @@ def attn_kernel_label(share, ring):
             ws = share.ws[0].numel() if share.ws[0] is not None else 0
             names.append(KERNEL_NAMES.get(uaa.usp_attn_kernel(q.shape, b - a, mask=m, workspace_bytes=ws), "?"))
     else:
+        ws = share.ws[0].numel() if share.ws[0] is not None else 0
         for a, b in share.ring:
-            names.append(KERNEL_NAMES.get(uaa.usp_attn_kernel(share.qh["q"].shape, b - a), "?"))
+            names.append(KERNEL_NAMES.get(uaa.usp_attn_kernel(share.qh["q"].shape, b - a, workspace_bytes=ws), "?"))
     if len(set(names)) == 1:
         return names[0]
     return " + ".join("%s x%d" % (n, names.count(n)) for n in sorted(set(names), key=names.index))

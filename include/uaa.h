@@ -232,12 +232,15 @@ int usp_attn_fwd_lse(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, in
  * e.g. 336 units on 256 compute units take two full rounds.  With a
  * workspace, bf16 input and USP_MASK_FULL, the kernel instead keeps
  * floor(units / CUs) rounds' worth of units whole and cuts the keys of each
- * remaining unit into p <= 8 pieces of about equal length, each run by its
- * own workgroup ahead of the whole units; the last piece of a unit to finish
- * merges the pieces' partial states in fp32 -- the Ring merge of key blocks
- * ([USP]) done inside the kernel -- in piece order, so the result does not
- * depend on timing.  It equals the plain call's up to rounding (the bf16
- * probabilities of a piece are taken relative to that piece's maximum).
+ * remaining unit (of every unit, when they fill at most half the compute
+ * units) into p <= 8 pieces of about equal length, each run by its own
+ * workgroup ahead of the whole units, where a cost model of the launch says
+ * this pays.  The last piece of a unit to finish merges the pieces' results
+ * -- the Ring merge of key blocks ([USP]) done inside the kernel -- in piece
+ * order, so the result does not depend on timing.  It equals the plain
+ * call's up to rounding (a piece's probabilities are taken relative to that
+ * piece's maximum; with D = 128 a piece's O is kept in bf16 between the
+ * piece and the merge).
  *
  *   workspace  device, 256-byte aligned, at least
  *              usp_attn_workspace_bytes(...) bytes, zero-filled before its
@@ -351,6 +354,9 @@ int usp_attn_fwd_lse_gather(int dtype, int world, int rank, const int64_t* seq_o
 #define USP_KERNEL_PIPELINED 5       /* bf16, D = 128: the software-pipelined kernel */
 #define USP_KERNEL_PIPELINED_DIAG 6  /* bf16, D = 128, a mask whose keys form one increasing piece:
                                         the pipelined kernel, diagonal units masked row by row */
+#define USP_KERNEL_PIPELINED_SPLIT 7 /* bf16, D = 128, every key allowed, with a workspace: the
+                                        pipelined kernel with the keys of some units split into
+                                        pieces run on otherwise idle CUs */
 int usp_attn_kernel(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, int o_dtype,
                     const usp_mask* mask, size_t workspace_bytes);
 

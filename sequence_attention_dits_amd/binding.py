@@ -42,6 +42,7 @@ USP_KERNEL_GENERAL_MASKED = 3
 USP_KERNEL_GENERAL_SPLIT = 4
 USP_KERNEL_PIPELINED = 5
 USP_KERNEL_PIPELINED_DIAG = 6
+USP_KERNEL_PIPELINED_SPLIT = 7
 
 _c_i64 = ctypes.c_int64
 _c_p = ctypes.c_void_p

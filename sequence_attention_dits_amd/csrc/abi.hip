@@ -271,8 +271,6 @@ static int device_cu_count()
     return n;
 }
 
-// Key split the bf16 kernel would use for this problem on the current
-// device with a workspace (p = 1: unsplit).
 // [lo, hi] of the positions of rows [0, n), n >= 1, of a map whose pieces
 // each increase.
 static void host_pos_range(const uaa::PosMap& m, int64_t n, int64_t& lo, int64_t& hi)
@@ -299,8 +297,20 @@ static bool all_pairs_allowed(const uaa::PosMap& q, int64_t Sq, const uaa::PosMa
     return khi <= qlo;
 }
 
+static bool pipelined_on()
+{
+    static const bool on = [] {
+        const char* e = getenv("UAA_ATTN_P32");
+        return !(e && e[0] == '0');
+    }();
+    return on;
+}
+
+// The pipelined kernel's key split where it applies (bf16, D = 128,
+// unmasked), else the general kernel's.  row_heads: heads per input token
+// (the gathering call reads the shards' rows).
 static uaa::SplitPlan attn_split_plan(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
-                                      const usp_mask* mask)
+                                      const usp_mask* mask, int64_t row_heads = 0)
 {
     uaa::SplitPlan none;
     if (dtype != UAA_BF16 || (D != 64 && D != 128) || B <= 0 || H <= 0 || Sq <= 0 || Sk <= 0) return none;
@@ -308,12 +318,17 @@ static uaa::SplitPlan attn_split_plan(int dtype, int64_t B, int64_t H, int64_t S
     if ((double)B * (Sq > Sk ? Sq : Sk) * H * D > (double)kMaxElems) return none;
     const int64_t units = uaa::attn_bf16_units(B, H, Sq);
     if (units > kMaxIdx32 / 8) return none;
-    return uaa::plan_split(units, (Sk + 63) / 64, device_cu_count());
+    const int cus = device_cu_count();
+    if (D == 128 && pipelined_on() && uaa::attn_p32_fits(Sk, row_heads > 0 ? row_heads : H))
+        return uaa::plan_p32_split(units, (Sk + 63) / 64, cus, Sk,
+                                   row_heads > 0 ? row_heads : H);
+    return uaa::plan_split(units, (Sk + 63) / 64, cus);
 }
 
 static int64_t plan_ws_bytes(const uaa::SplitPlan& plan, int64_t B, int64_t H, int64_t Sq)
 {
     if (plan.p <= 1) return 0;
+    if (plan.p32) return uaa::p32_split_ws_bytes(uaa::attn_bf16_units(B, H, Sq) - plan.n_whole, plan.p);
     return uaa::split_ws_bytes(uaa::attn_bf16_units(B, H, Sq) - plan.n_whole, plan.p);
 }
 
@@ -418,13 +433,15 @@ static int attn_impl(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, in
     if (((Sq + 63) / 64) * H * B >= kMaxIdx32) return fail(UAA_ERR_INVALID_ARG, "attn: grid too large");
     a.split_p = 1;
     a.n_whole = 0;
+    a.split_p32 = 0;
     if (query ? workspace_bytes > 0 : workspace != nullptr) {
         if (!query && !aligned(workspace, 256))
             return fail(UAA_ERR_INVALID_ARG, "attn: workspace must be 256-byte aligned");
-        const uaa::SplitPlan plan = attn_split_plan(dtype, B, H, Sq, Sk, D, mask);
+        const uaa::SplitPlan plan = attn_split_plan(dtype, B, H, Sq, Sk, D, mask, RH);
         if (plan.p > 1 && workspace_bytes >= (size_t)plan_ws_bytes(plan, B, H, Sq)) {
             a.split_p = plan.p;
             a.n_whole = plan.n_whole;
+            a.split_p32 = plan.p32 ? 1 : 0;
             // a query has no workspace pointer: any non-null value stands in
             // for it, since the plan only checks that there is one
             a.ws = query ? reinterpret_cast<void*>(uintptr_t(256)) : workspace;
@@ -688,11 +705,11 @@ int scratch_address(void** out)
 
 static hipError_t clear_split_counters(const uaa::AttnArgs& a, hipStream_t s)
 {
-    const int64_t units = uaa::attn_bf16_units(a.B, a.H, a.Sq);
+    const int64_t units = uaa::attn_bf16_units(a.B, a.H, a.Sq);   // both kernels' units are 256 rows
     const int64_t n_split = units - a.n_whole;
     if (n_split <= 0) return hipSuccess;
     uint32_t* cnt = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(a.ws) +
-                                                n_split * a.split_p * uaa::kSplitSlotBytes);
+                                                uaa::split_counter_offset(n_split, a.split_p, a.split_p32 != 0));
     const unsigned blocks = (unsigned)std::min<int64_t>((n_split + 255) / 256, 64);
     void* params[] = {&cnt, const_cast<int64_t*>(&n_split)};
     return hipLaunchKernel(reinterpret_cast<const void*>(zero_words_kernel), dim3(blocks), dim3(256), params, 0, s);

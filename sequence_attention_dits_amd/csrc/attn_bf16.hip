@@ -731,10 +731,11 @@ __global__ __launch_bounds__(64 * kWaves, D == 64 ? 4 : 2) void attn_bf16_kernel
         // in piece order -- the same loads and arithmetic whichever piece it
         // is, so the result does not depend on timing -- resets the counter
         // and writes the output.  Pieces may run on different XCDs, whose L2
-        // caches are not coherent with each other: the state moves with
-        // device-scope (L2-bypassing) loads and stores, so no cache-wide
-        // write-back or invalidate is needed, only the order of this wave's
-        // stores before its count.
+        // caches are not coherent with each other for ordinary accesses: the
+        // state moves with device-scope loads and stores (cache policy sc1, as
+        // relaxed device-scope atomic loads and stores are), coherent across
+        // XCDs by themselves, so no cache-wide write-back or invalidate is
+        // needed, only the completion of this wave's stores before its count.
         unsigned char* wsb = static_cast<unsigned char*>(a.ws);
         const uint32_t su = unit - (uint32_t)a.n_whole;   // index among the split units
         const int64_t n_split = (int64_t)(gridDim.x - (uint32_t)a.n_whole) / np;
@@ -753,11 +754,11 @@ __global__ __launch_bounds__(64 * kWaves, D == 64 ? 4 : 2) void attn_bf16_kernel
             for (int g = 0; g < 4; ++g) {
                 const u32x4 w{__float_as_uint(oacc[db][4 * g]), __float_as_uint(oacc[db][4 * g + 1]),
                               __float_as_uint(oacc[db][4 * g + 2]), __float_as_uint(oacc[db][4 * g + 3])};
-                __builtin_amdgcn_raw_buffer_store_b128(w, wr, voff, qoff(piece, 4 * db + g), kDev);
+                store_slot_b128(w, wr, voff, qoff(piece, 4 * db + g));
             }
         {
             const u32x4 w{__float_as_uint(m), __float_as_uint(lsum), 0u, 0u};
-            __builtin_amdgcn_raw_buffer_store_b128(w, wr, voff, qoff(piece, 4 * NDB), kDev);
+            store_slot_b128(w, wr, voff, qoff(piece, 4 * NDB));
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the stores above are complete
         __syncthreads();
@@ -859,26 +860,35 @@ static bool p32_on()
     return on;
 }
 
-// The general kernel's arguments with its q-tile count set and a key split
-// kept only where it applies; false when there is no work.
-static bool general_args(const AttnArgs& a0, AttnArgs& a)
+static bool p32_takes(int D, const AttnArgs& a)
+{
+    return D == 128 && attn_p32_fits(a.Sk, a.row_heads) && p32_on();
+}
+
+// The arguments with the general kernel's q-tile count set and a key split
+// kept only where it applies (a plan made for the pipelined kernel runs
+// only there); false when there is no work.
+static bool general_args(int D, const AttnArgs& a0, AttnArgs& a)
 {
     a = a0;
     a.n_qtiles = (int32_t)((a.Sq + kBM - 1) / kBM);
     const int64_t units = (int64_t)a.n_qtiles * a.H * a.B;
     if (units <= 0) return false;
-    if (a.masked || a.ws == nullptr || a.split_p <= 1 || a.n_whole < 0 || a.n_whole >= units) {
+    if (a.masked || a.ws == nullptr || a.split_p <= 1 || a.n_whole < 0 || a.n_whole >= units ||
+        (a.split_p32 != 0 && !p32_takes(D, a))) {
         a.split_p = 1;
         a.n_whole = 0;
+        a.split_p32 = 0;
     }
     return true;
 }
 
 // 0: the general kernel; 1: the pipelined kernel; 2: its DIAG form (units
-// on a mask diagonal)
+// on a mask diagonal); 3: its key split
 static int use_p32(int D, const AttnArgs& a)
 {
-    if (!(D == 128 && a.split_p <= 1 && attn_p32_fits(a.Sk, a.row_heads) && p32_on())) return 0;
+    if (!p32_takes(D, a)) return 0;
+    if (a.split_p > 1) return a.split_p32 ? 3 : 0;
     if (attn_p32_mask_ok(a)) return 1;
     return attn_p32_diag_ok(a) ? 2 : 0;
 }
@@ -886,10 +896,11 @@ static int use_p32(int D, const AttnArgs& a)
 int attn_bf16_kernel_choice(int D, const AttnArgs& a0)
 {
     AttnArgs a;
-    if (!general_args(a0, a)) return USP_KERNEL_NONE;
+    if (!general_args(D, a0, a)) return USP_KERNEL_NONE;
     const int p = use_p32(D, a);
     if (p == 1) return USP_KERNEL_PIPELINED;
     if (p == 2) return USP_KERNEL_PIPELINED_DIAG;
+    if (p == 3) return USP_KERNEL_PIPELINED_SPLIT;
     if (a.masked) return USP_KERNEL_GENERAL_MASKED;
     return a.split_p > 1 ? USP_KERNEL_GENERAL_SPLIT : USP_KERNEL_GENERAL;
 }
@@ -897,11 +908,11 @@ int attn_bf16_kernel_choice(int D, const AttnArgs& a0)
 hipError_t launch_attn_bf16(int D, int o_dtype, const AttnArgs& a0, hipStream_t s)
 {
     AttnArgs a;
-    if (!general_args(a0, a)) return hipSuccess;
+    if (!general_args(D, a0, a)) return hipSuccess;
     const int64_t units = (int64_t)a.n_qtiles * a.H * a.B;
     const int64_t blocks = a.split_p > 1 ? a.n_whole + (units - a.n_whole) * a.split_p : units;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    if (const int p = use_p32(D, a)) return launch_attn_p32(o_dtype, p == 2, a0, s);
+    if (const int p = use_p32(D, a)) return launch_attn_p32(o_dtype, p, a, s);
     const dim3 grid((unsigned)blocks);
     const bool ob = o_dtype == UAA_BF16;
     if (D == 128) return ob ? launch_d<128, true>(a, grid, s) : launch_d<128, false>(a, grid, s);

@@ -41,6 +41,20 @@ __device__ __forceinline__ int64_t allowed_prefix(int64_t base, int64_t stride, 
     return c < n ? c : n;
 }
 
+// 16-byte buffer store at device scope (cache policy sc1) of a piece's
+// slot.  A buffer store of more than 8 bytes with a register offset reads
+// its data registers after it issues; a vector ALU write to them in the next
+// cycle can replace the data of some lanes before the store has read it
+// (seen as dword 0 of lanes 12..15 of each 16 taking the next quad's value).
+// The data stays live, and unwritten, through two wait states after the
+// store.
+template <typename V4>
+__device__ __forceinline__ void store_slot_b128(V4 w, __amdgpu_buffer_rsrc_t rs, int voff, int soff)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(w, rs, voff, soff, 16);
+    asm volatile("s_nop 1" ::"v"(w));
+}
+
 // Workgroup index -> logical work index.  Workgroups are handed to the 8
 // XCDs round-robin, and each XCD has its own L2: renumber so that each XCD
 // gets one contiguous run of logical indices, i.e. the q tiles of the same

@@ -52,6 +52,7 @@
 // LSE at the end.
 #include "attn_common.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace uaa {
@@ -172,7 +173,19 @@ __device__ __forceinline__ void p_pin_f(float& x) { asm volatile("" : "+v"(x)); 
 // masked one by one (each lane's row has its own allowed-key count); units
 // run longest first.  Without DIAG every unit runs every key tile (a masked
 // call only when each unit sees every key of the block or none).
-template <bool OUT_BF16, bool DIAG>
+// Piece form (SPLIT): the keys of some units are cut into pieces, each run
+// by its own workgroup (units [0, n_whole) run whole, one workgroup each;
+// each of the others in split_p pieces of about equal length).  Piece
+// workgroups come first in the grid, piece index major, so they are
+// dispatched first and the whole units fill the compute units as they free
+// up.  A piece stores its normalised O (bf16) and its LSE in a slot of the
+// workspace and counts in; the last piece of a unit to finish combines the
+// unit's slots in piece order and writes the result.  The slot of piece k
+// of split unit su is su * split_p + k; then one int32 arrival counter per
+// split unit.  A slot holds the 256 rows' O as the lanes' registers hold it
+// (16-byte quad j of lane tid at (512 j + tid) * 16) and the rows' LSE
+// (log2 units) at 64 KiB.
+template <bool OUT_BF16, bool DIAG, bool SPLIT>
 __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArgs a)
 {
     // V stages, K stages, Q staging: every operand read is a per-lane
@@ -183,7 +196,25 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
     p_lds_u8* const L = (p_lds_u8*)smem;
 
     int64_t qt, hh, b;
-    if (DIAG && gridDim.x % 8u == 0u && (gridDim.x / 8u) % (uint32_t)a.n_qtiles == 0u) {
+    const int32_t nt = (int32_t)((a.Sk + kPBN - 1) / kPBN);
+    int32_t tb = 0, te = nt;       // this workgroup's key tiles
+    int32_t piece = 0, su = -1;    // SPLIT: piece index and split-unit index (-1: a whole unit)
+    if constexpr (SPLIT) {
+        const uint32_t L = blockIdx.x, nw = (uint32_t)a.n_whole, np = (uint32_t)a.split_p;
+        const uint32_t n_split = (uint32_t)a.n_qtiles * (uint32_t)a.H * (uint32_t)a.B - nw;
+        const uint32_t npw = n_split * np;   // piece workgroups
+        if (L < npw) {
+            // piece-major in dispatch order (every XCD gets its share of
+            // each piece index); within a piece index, each XCD a run of units
+            piece = (int32_t)(L / n_split);
+            su = (int32_t)xcd_logical(L - (uint32_t)piece * n_split, n_split);
+            unit_coords(a, nw + (uint32_t)su, qt, hh, b);
+            tb = (int32_t)((int64_t)piece * nt / np);
+            te = (int32_t)((int64_t)(piece + 1) * nt / np);
+        } else {
+            unit_coords(a, xcd_logical(L - npw, gridDim.x - npw), qt, hh, b);
+        }
+    } else if (DIAG && gridDim.x % 8u == 0u && (gridDim.x / 8u) % (uint32_t)a.n_qtiles == 0u) {
         // every XCD holds whole heads: each XCD's workgroups (blockIdx =
         // 8 j + x on XCD x) take its heads' q tiles last-first with the heads
         // interleaved -- later rows see at least as many keys under every
@@ -207,7 +238,7 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
     const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + ((b * Sk) * RH + h_in) * kPD * 2;
     // key tiles this unit runs, and with DIAG this lane's row's allowed keys
     // (a prefix of the block; rows past Sq are never stored and see all)
-    int n = (int)((Sk + kPBN - 1) / kPBN);
+    int n = te - tb;
     int32_t kcnt = (int32_t)Sk;
     if constexpr (DIAG) {
         const int64_t t0 = qt * kPBM, t1 = t0 + kPBM < Sq ? t0 + kPBM : Sq;
@@ -233,7 +264,7 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
     }
     const uint32_t tile_bytes = (uint32_t)kPBN * ld2;
     auto copy_tile = [&](const p_rsrc& rs, int off, int t, int s, int c) {
-        p_dma(rs, coff[c] + (uint32_t)t * tile_bytes,
+        p_dma(rs, coff[c] + (uint32_t)(tb + t) * tile_bytes,
               (uint32_t)(uintptr_t)(L + off + s * kPTB + (kPWaves * c + wave) * 1024));
     };
 
@@ -299,20 +330,24 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
                 rs = re;
             }
         }
-        // stages past the last tile repeat it: the V a fully masked step
-        // multiplies by zero must be finite
+        // K0, K1, V0, K2, V1 in that order (2 copies each per wave), so that
+        // the first scores wait only for Q and K0 and step 0 only for K1 and
+        // V0 (copy completions count in order); stages past the last tile
+        // repeat it: the V a fully masked step multiplies by zero must be
+        // finite
+        const int t1 = n > 1 ? 1 : 0, t2 = n > 2 ? 2 : n - 1;
 #pragma unroll
-        for (int t = 0; t < 3; ++t) {
-            const int tt = t < n ? t : n - 1;
+        for (int c = 0; c < 2; ++c) copy_tile(krs, OFF_K, 0, 0, c);
 #pragma unroll
-            for (int c = 0; c < 2; ++c) copy_tile(krs, OFF_K, tt, t, c);
-            if (t < 2) {
+        for (int c = 0; c < 2; ++c) copy_tile(krs, OFF_K, t1, 1, c);
 #pragma unroll
-                for (int c = 0; c < 2; ++c) copy_tile(vrs, OFF_V, tt, t, c);
-            }
-        }
+        for (int c = 0; c < 2; ++c) copy_tile(vrs, OFF_V, 0, 0, c);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) copy_tile(krs, OFF_K, t2, 2, c);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) copy_tile(vrs, OFF_V, t1, 1, c);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 8);   // vmcnt(8): Q and K0 have landed (K1, V0, K2, V1 may still run)
     __syncthreads();
 
     // ---- operand addressing ----------------------------------------------
@@ -383,7 +418,8 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
     // keys of tile t this lane's row may see (a prefix of the tile): the
     // ragged end of the block, and with DIAG the row's own allowed count
     auto key_lim = [&](int t) {
-        const int64_t r = (DIAG ? (int64_t)kcnt : Sk) - (int64_t)t * kPBN;
+        if (SPLIT && t >= n) return 0;   // past the piece
+        const int64_t r = (DIAG ? (int64_t)kcnt : Sk) - (int64_t)(tb + t) * kPBN;
         return r <= 0 ? 0 : (r >= kPBN ? kPBN : (int)r);
     };
     // some lane of the wave has a masked key in tile t (uniform)
@@ -474,7 +510,10 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
         for (int j = 0; j < 16; ++j) max_op(sacc[0], j);
         finish_max();
     }
-    // every wave is done with K stage 0 before step 0 copies tile 3 into it
+    // every wave is done with K stage 0 before step 0 copies tile 3 into it,
+    // and K1 and V0 have landed (K2 and V1 may still run: step 0 waits for
+    // them before its barrier)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 4);   // vmcnt(4)
     p_barrier();
     // the first K operands of each step's [A] are read at the end of the
     // step before (after its barrier): step 0's here
@@ -486,7 +525,7 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
     // registers), and its LSE loaded, so that the epilogue's merge does not
     // wait for them.  The copies land before step 0 ends (its vmcnt wait).
     float lse_prev = -INFINITY;
-    if (a.acc) {
+    if (a.acc && su < 0) {
         if (i < Sq) lse_prev = a.lse[(b * Sq + i) * H + hh];
         if constexpr (OUT_BF16) {
             const uint32_t ldo = (uint32_t)(H * kPD * 2);
@@ -599,6 +638,10 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
     }
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lb2 = lt > 0.f ? m + __log2f(lt) : -INFINITY;
+    // The rows' result (o x inv, LSE lb2 in log2 units) written out; with
+    // a.acc merged into the (o, lse) already there (lse_prev, and with bf16
+    // output the previous rows copied into this wave's Q staging region).
+    auto write_out = [&](const p_f32x16 (&o)[4], const float inv, const float lb2) {
     float wp = 0.f, wb = 1.f, lse_out2 = lb2;
     if (a.acc) {
         const float lp2 = lse_prev * kPLog2e;
@@ -626,8 +669,8 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d0 = 32 * db + 8 * g + 4 * hg;
-                const p_u32x2 w{p_pack(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                                p_pack(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+                const p_u32x2 w{p_pack(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                                p_pack(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
                 *(__attribute__((address_space(3))) p_u32x2*)(R + l32 * RS + d0 * 2) = w;
             }
         if (a.acc && hg == 0) *(__attribute__((address_space(3))) p_f32x2*)(R + 32 * RS + l32 * 8) = p_f32x2{wp, wb};
@@ -684,8 +727,8 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
             for (int db = 0; db < 4; ++db)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    p_f32x4 x{oacc[db][4 * g] * sb, oacc[db][4 * g + 1] * sb, oacc[db][4 * g + 2] * sb,
-                              oacc[db][4 * g + 3] * sb};
+                    p_f32x4 x{o[db][4 * g] * sb, o[db][4 * g + 1] * sb, o[db][4 * g + 2] * sb,
+                              o[db][4 * g + 3] * sb};
                     if (use) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) x[e] = fmaf(wp, pvv[db][g][e], x[e]);
@@ -695,6 +738,102 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
         }
     }
     if (hg == 0 && i < Sq) a.lse[(b * Sq + i) * H + hh] = lse_out2 * kPLn2;
+    };
+    if (!SPLIT || su < 0) {
+        write_out(oacc, inv, lb2);
+        return;
+    }
+
+    // ---- a piece: store, count in; the last piece of the unit combines ---
+    // Pieces of a unit run on different XCDs, whose L2 caches are not
+    // coherent with each other for ordinary accesses.  Every slot access is
+    // a device-scope one (cache policy sc1, as the memory model's relaxed
+    // device-scope atomic loads and stores are), which is coherent across
+    // XCDs by itself: each wave's slot stores complete before the workgroup
+    // counts in, and no cache-wide write-back or invalidate is needed.
+    if constexpr (SPLIT) {
+        const int np = a.split_p;
+        const int64_t n_split = (int64_t)a.n_qtiles * a.H * a.B - a.n_whole;
+        unsigned char* const wsb = static_cast<unsigned char*>(a.ws) + (int64_t)su * np * kP32SlotBytes;
+        const __amdgpu_buffer_rsrc_t wr =
+            __builtin_amdgcn_make_buffer_rsrc(wsb, (short)0, (int)(np * kP32SlotBytes), 0x00020000);
+        constexpr int kDev = 16;   // cache policy sc1: device-scope access
+        const int row = 32 * wave + l32;
+        {
+            const int sb = piece * (int)kP32SlotBytes;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int db = j >> 1, v0 = 8 * (j & 1);
+                const p_u32x4 w{p_pack(oacc[db][v0] * inv, oacc[db][v0 + 1] * inv),
+                                p_pack(oacc[db][v0 + 2] * inv, oacc[db][v0 + 3] * inv),
+                                p_pack(oacc[db][v0 + 4] * inv, oacc[db][v0 + 5] * inv),
+                                p_pack(oacc[db][v0 + 6] * inv, oacc[db][v0 + 7] * inv)};
+                store_slot_b128(w, wr, tid * 16, sb + j * (kPWaves * 64 * 16));
+            }
+            if (hg == 0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lb2), wr, row * 4, sb + 65536, kDev);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
+        __syncthreads();
+        int32_t* const cnt = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(a.ws) +
+                                                        n_split * np * kP32SlotBytes) + su;
+        volatile __attribute__((address_space(3))) int* const flag =
+            reinterpret_cast<volatile __attribute__((address_space(3))) int*>(L);
+        if (tid == 0) *flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int arrived = *flag;
+        __syncthreads();   // every wave has read the flag before the LDS is written again
+        if (arrived != np - 1) return;
+        // the last piece: the unit's slots in piece order (the same loads and
+        // arithmetic whichever piece combines them)
+        float mx2 = -INFINITY;
+        for (int k = 0; k < np; ++k)
+            mx2 = __builtin_elementwise_maximum(
+                mx2, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wr, row * 4, k * (int)kP32SlotBytes + 65536,
+                                                                          kDev)));
+        p_f32x16 comb[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) comb[db][v] = 0.f;
+        float wsum = 0.f;
+        for (int k = 0; k < np; ++k) {
+            const int sb = k * (int)kP32SlotBytes;
+            const float lk = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wr, row * 4, sb + 65536, kDev));
+            const float wk = lk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lk - mx2);
+            wsum += wk;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const p_u32x4 q = __builtin_bit_cast(
+                    p_u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, tid * 16, sb + j * (kPWaves * 64 * 16), kDev));
+                const int db = j >> 1, v0 = 8 * (j & 1);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    comb[db][v0 + 2 * e] = fmaf(wk, p_lo(q[e]), comb[db][v0 + 2 * e]);
+                    comb[db][v0 + 2 * e + 1] = fmaf(wk, p_hi(q[e]), comb[db][v0 + 2 * e + 1]);
+                }
+            }
+        }
+        if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // continuing a Ring pass: the running result's LSE, and with bf16
+        // output its rows in this wave's Q staging region
+        if (a.acc) {
+            if (i < Sq) lse_prev = a.lse[(b * Sq + i) * H + hh];
+            if constexpr (OUT_BF16) {
+                const uint32_t ldo = (uint32_t)(H * kPD * 2);
+                const int64_t rows = Sq > r0 ? (Sq - r0 < 32 ? Sq - r0 : 32) : 0;
+                const p_rsrc orr = p_make_rsrc(static_cast<const unsigned char*>(a.o) +
+                                                   ((b * Sq + (rows > 0 ? r0 : 0)) * H + hh) * kPD * 2,
+                                               rows > 0 ? (uint32_t)((rows - 1) * ldo + kPD * 2) : 0u);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    p_dma(orr, (uint32_t)(4 * j + (lane >> 4)) * ldo + (uint32_t)((lane & 15) << 4),
+                          (uint32_t)(uintptr_t)(L + OFF_Q + wave * 32 * kPRowB + j * 1024));
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the rows have landed
+            }
+        }
+        const bool live = mx2 != -INFINITY && wsum > 0.f;
+        write_out(comb, live ? 1.f / wsum : 0.f, live ? mx2 + __log2f(wsum) : -INFINITY);
+    }
 }
 
 bool attn_p32_fits(int64_t Sk, int64_t row_heads)
@@ -725,20 +864,81 @@ bool attn_p32_mask_ok(const AttnArgs& a)
     return true;
 }
 
-hipError_t launch_attn_p32(int o_dtype, bool diag, const AttnArgs& a0, hipStream_t s)
+// Costs of the kernel's fixed parts in tile steps (one tile step: the 256
+// rows of a workgroup against 64 keys), measured on the FLUX.1 share's
+// chunks: the prologue up to the first step, a whole unit's epilogue, a
+// piece's slot store and count, and the combine of a unit's pieces.
+constexpr double kPStartSteps = 2.3, kPEpilogueSteps = 1.1, kPStoreSteps = 1.3, kPCombineSteps = 2.6;
+
+SplitPlan plan_p32_split(int64_t n_units, int64_t n_tiles, int n_cu, int64_t Sk, int64_t row_heads)
+{
+    // Tile-step model of one launch, one workgroup per compute unit (u: a
+    // whole unit's fixed cost, o: a piece's, m: the combine):
+    //  * plain: ceil(U / C) rounds of N + u;
+    //  * U > C: f = floor(U / C) rounds whole and the last partial round's r
+    //    units in p equal pieces, run first: ceil(N / p) + o + m + f (N + u);
+    //  * U <= C / 2: every unit in p = min(8, C / U) equal pieces, one round
+    //    of ceil(N / p) + o + m.
+    // A split is taken when it saves at least 5% of the plain launch.  (A
+    // launch that leaves fewer than half the compute units idle runs plain:
+    // cutting its units so that the idle ones run the short pieces measured
+    // slower than the plain launch.)
+    SplitPlan plan;
+    if (n_cu <= 0 || n_units <= 0 || n_tiles < 8 || !attn_p32_fits(Sk, row_heads)) return plan;
+    const double u = kPStartSteps + kPEpilogueSteps, o = kPStartSteps + kPStoreSteps, m = kPCombineSteps;
+    const double N = (double)n_tiles;
+    const int64_t f = n_units / n_cu, r = n_units - f * n_cu;
+    const double plain = (double)(f + (r > 0)) * (N + u);
+    double best = plain;
+    if (f >= 1) {
+        if (r == 0) return plan;
+        for (int p = 2; p <= 8 && r * p <= n_cu && n_tiles / p >= 4; ++p) {
+            const double T = (double)((n_tiles + p - 1) / p) + o + m + (double)f * (N + u);
+            if (T < best) {
+                best = T;
+                plan.p = p;
+                plan.n_whole = f * n_cu;
+            }
+        }
+    } else {
+        const int64_t pe = std::min<int64_t>(8, n_cu / n_units);
+        if (pe >= 2) {
+            const double T = (double)((n_tiles + pe - 1) / pe) + o + m;
+            if (T < best) {
+                best = T;
+                plan.p = (int)pe;
+            }
+        }
+    }
+    if (best >= 0.95 * plain) return SplitPlan{};
+    plan.p32 = true;
+    return plan;
+}
+
+hipError_t launch_attn_p32(int o_dtype, int form, const AttnArgs& a0, hipStream_t s)
 {
     AttnArgs a = a0;
     a.n_qtiles = (int32_t)((a.Sq + kPBM - 1) / kPBM);
     const int64_t units = (int64_t)a.n_qtiles * a.H * a.B;
     if (units <= 0) return hipSuccess;
     if (units > 0x7fffffff) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)units), block(64 * kPWaves);
-    if (diag) {
-        if (o_dtype == UAA_BF16) return launch_kernel(attn_p32_kernel<true, true>, grid, block, 0, s, a);
-        return launch_kernel(attn_p32_kernel<false, true>, grid, block, 0, s, a);
+    const dim3 block(64 * kPWaves);
+    const bool ob = o_dtype == UAA_BF16;
+    if (form == 3) {
+        if (a.split_p <= 1 || a.ws == nullptr || a.masked || a.n_whole < 0 || a.n_whole >= units)
+            return hipErrorInvalidValue;
+        const int64_t blocks = a.n_whole + (units - a.n_whole) * a.split_p;
+        if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+        const dim3 grid((unsigned)blocks);
+        return ob ? launch_kernel(attn_p32_kernel<true, false, true>, grid, block, 0, s, a)
+                  : launch_kernel(attn_p32_kernel<false, false, true>, grid, block, 0, s, a);
     }
-    if (o_dtype == UAA_BF16) return launch_kernel(attn_p32_kernel<true, false>, grid, block, 0, s, a);
-    return launch_kernel(attn_p32_kernel<false, false>, grid, block, 0, s, a);
+    const dim3 grid((unsigned)units);
+    if (form == 2)
+        return ob ? launch_kernel(attn_p32_kernel<true, true, false>, grid, block, 0, s, a)
+                  : launch_kernel(attn_p32_kernel<false, true, false>, grid, block, 0, s, a);
+    return ob ? launch_kernel(attn_p32_kernel<true, false, false>, grid, block, 0, s, a)
+              : launch_kernel(attn_p32_kernel<false, false, false>, grid, block, 0, s, a);
 }
 
 }  // namespace uaa

@@ -104,11 +104,12 @@ struct AttnArgs {
     int32_t n_qtiles;     // ceil(Sq / rows per workgroup), set by the launcher
     // Key split (bf16, unmasked): units [0, n_whole) run whole, one
     // workgroup each; the keys of every later unit (those of the last,
-    // partial round of workgroups) are cut into split_p pieces of about
-    // equal length, each run by its own workgroup, and the last piece of a
-    // unit to finish combines the pieces.
+    // partial round of workgroups, or every unit when they are few) are cut
+    // into split_p pieces of about equal length, each run by its own
+    // workgroup, and the last piece of a unit to finish combines the pieces.
     int32_t split_p;      // 1: no split
     int32_t n_whole;      // units run whole, set by the caller with split_p
+    int32_t split_p32;    // 1: the pipelined kernel runs the pieces (its slot layout)
     void* ws;             // workspace: piece partials, then arrival counters
 };
 
@@ -122,12 +123,26 @@ constexpr int64_t kSplitSlotBytes = kSplitLanes * kSplitQuads * 16;
 struct SplitPlan {
     int p = 1;            // pieces per split unit; 1: no split
     int64_t n_whole = 0;  // units run whole
+    bool p32 = false;     // the pipelined kernel runs the pieces
 };
 inline int64_t split_ws_bytes(int64_t n_split, int p) { return n_split * p * kSplitSlotBytes + 4 * n_split; }
+
+// Workspace of the pipelined kernel's key split: one slot per piece of a
+// split unit (the piece's normalised O as bf16, 64 KiB, then its 256 rows'
+// LSE), then one int32 arrival counter per split unit.
+constexpr int64_t kP32SlotBytes = 65536 + 1024;
+inline int64_t p32_split_ws_bytes(int64_t n_split, int p) { return n_split * p * kP32SlotBytes + 4 * n_split; }
+inline int64_t split_counter_offset(int64_t n_split, int p, bool p32)
+{
+    return n_split * p * (p32 ? kP32SlotBytes : kSplitSlotBytes);
+}
 
 // Split plan for n_units units of n_tiles key tiles on n_cu compute units,
 // and the unit count of the bf16 kernel.
 SplitPlan plan_split(int64_t n_units, int64_t n_tiles, int n_cu);
+// The pipelined kernel's split plan for this problem (bf16, D = 128,
+// unmasked calls), p = 1 when the plain launch is as fast.
+SplitPlan plan_p32_split(int64_t n_units, int64_t n_tiles, int n_cu, int64_t Sk, int64_t row_heads);
 int64_t attn_bf16_units(int64_t B, int64_t H, int64_t Sq);
 
 hipError_t launch_attn_bf16(int D, int o_dtype, const AttnArgs& a, hipStream_t s);
@@ -140,7 +155,8 @@ bool attn_p32_mask_ok(const AttnArgs& a);
 // masked calls whose keys are one increasing piece: units on the diagonal
 // run their live tiles with rows masked one by one (the kernel's DIAG form)
 bool attn_p32_diag_ok(const AttnArgs& a);
-hipError_t launch_attn_p32(int o_dtype, bool diag, const AttnArgs& a, hipStream_t s);
+// form: 1 plain, 2 DIAG, 3 key split (a.split_p, a.n_whole)
+hipError_t launch_attn_p32(int o_dtype, int form, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_fp32(int D, const AttnArgs& a, hipStream_t s);
 
 // --------------------------------------------------------------------------

@@ -2,13 +2,15 @@
 
 When the (batch, head, 256-row) units of a problem do not fill the last
 round of workgroups, the bf16 kernel cuts the keys of the units of that
-round into pieces and combines the pieces' partial states in fp32 -- the
+round into pieces and combines the pieces' partial results -- the
 online-softmax merge of key blocks that Ring attention performs across
-ranks (USP paper, the Ring attention section), done inside one launch.  The
-result is compared with the fp64 oracle under the bf16 tolerance, with the
-plain call, and with itself on a repeated call (the combine runs in piece
-order, so it is deterministic; the arrival counters are reset by every
-call, which the repeated call also checks)."""
+ranks (USP paper, the Ring attention section), done inside one launch.  With
+D = 64 the general kernel runs the pieces (partial states merged in fp32);
+with D = 128 the pipelined kernel does (each piece's normalised O kept in
+bf16 with its LSE).  The result is compared with the fp64 oracle under the
+bf16 tolerance, with the plain call, and with itself on a repeated call (the
+combine runs in piece order, so it is deterministic; the arrival counters
+are reset by every call, which the repeated call also checks)."""
 
 import math
 
@@ -57,6 +59,8 @@ def test_split_all_rows(case, out):
     assert ws is not None, "this shape is expected to split on a 256-CU device"
     scale = 1.0 / math.sqrt(D)
     odt = torch.bfloat16 if out == "bf16" else torch.float32
+    assert uaa.usp_attn_kernel(q.shape, Sk, o_dtype=odt, workspace_bytes=ws.numel()) == \
+        (uaa.USP_KERNEL_PIPELINED_SPLIT if D == 128 else uaa.USP_KERNEL_GENERAL_SPLIT)
     o, lse = _run(q, k, v, scale, ws, odt)
     o2, lse2 = _run(q, k, v, scale, ws, odt)   # same workspace, not re-zeroed
     o0, lse0 = _run(q, k, v, scale, None, odt)

@@ -26,7 +26,7 @@ SHAPES = [
     # name, B, Sq, Sk, H: the first two split their keys, the third does not
     ("qwen_chunk", 1, 3493, 3493, 24),
     ("smaller_split", 1, 2600, 1024, 24),
-    ("flux_chunk_unsplit", 1, 4608, 2304, 12),
+    ("one_full_round_unsplit", 1, 4096, 2048, 16),   # 256 units: one full round, no split
 ]
 
 
