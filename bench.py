@@ -126,6 +126,9 @@ def parse():
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="print the traffic summary of two rocprofv3 --pmc runs of --pmc-probe")
     p.add_argument("--stats-summary", metavar="DIR", help="print the summary of a rocprofv3 --stats run")
+    p.add_argument("--last", type=int, default=0,
+                   help="with --stats-summary: also average each kernel's last N dispatches (the timed launches "
+                        "a --kernels-only run reports)")
     p.add_argument("--counter-summary", nargs="+", metavar="DIR",
                    help="print the attention kernel's shader counters from rocprofv3 --pmc runs of --pmc-probe "
                         "(MFMA busy cycles against the active cycles, instruction mix, waits)")
@@ -622,7 +625,11 @@ def backward_variant(share, cfg_id: int, steps: int, warmup: int) -> dict:
     for _ in range(max(warmup, 1)):
         run()
     torch.cuda.synchronize()
-    torch.cuda._sleep(int(2.4e9 * 0.02))
+    # untimed steps right before the timed ones: the GPU is at its working
+    # clock when timing starts (an idle GPU lowers it), and the host is
+    # ahead of the GPU by their run time
+    for _ in range(max(warmup, 1)):
+        run()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -1007,8 +1014,11 @@ def counter_summary(dirs):
         print("wave time waiting on a dependency: %.3f" % (mean["SQ_WAIT_INST_ANY"] / mean["SQ_WAVE_CYCLES"]))
 
 
-def stats_summary(d):
-    """Kernel table of a rocprofv3 --kernel-trace --stats run (its *_kernel_stats.csv)."""
+def stats_summary(d, last: int = 0):
+    """Kernel table of a rocprofv3 --kernel-trace --stats run (its
+    *_kernel_stats.csv); with last > 0 also the average of each kernel's
+    last `last` dispatches (its *_kernel_trace.csv): the timed launches of a
+    --kernels-only run of one launch kind."""
     import csv
     import glob
     files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
@@ -1020,31 +1030,67 @@ def stats_summary(d):
         name = r["Name"] if len(r["Name"]) <= 70 else r["Name"][:67] + "..."
         print("%-70s %6d %12.2f %12.2f %12.2f" % (name, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
                                                 float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    traces = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if last > 0 and traces:
+        by = {}
+        for r in csv.DictReader(open(traces[0])):
+            by.setdefault(r["Kernel_Name"], []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+        print("\nlast %d dispatches of each kernel (the timed launches of --kernels-only):" % last)
+        print("%-70s %6s %12s" % ("kernel", "calls", "avg_us"))
+        for name, ts in sorted(by.items(), key=lambda kv: -sum(e - b for b, e in kv[1])):
+            if len(ts) < last:
+                continue
+            ts.sort()
+            tail = ts[-last:]
+            nm = name if len(name) <= 70 else name[:67] + "..."
+            print("%-70s %6d %12.2f" % (nm, len(tail), sum(e - b for b, e in tail) / len(tail) / 1e3))
 
 
-def time_launches(share, names, steps: int, n_sets: int) -> dict:
+TIMED_MS = 20.0   # least GPU time of one launch kind's timed region
+
+
+def time_launches(share, names, steps: int, n_sets: int, counts: dict = None) -> dict:
     """Per-launch microseconds of each named launch kind of the step: `steps`
     rounds back to back over the rotating sets, every launch on its set's own
-    buffers (timing_bufs: inputs and outputs cold), between two HIP events on
-    the launch stream; a spin kernel first gives the host a head start so
-    that no launch waits on the host."""
+    buffers (timing_bufs: inputs and outputs cold).  The rounds of one kind
+    are captured in a HIP graph, replayed once untimed and then, between two
+    HIP events, as many times as fill TIMED_MS: no launch waits on the host
+    (the short HBM-bound kernels take less time than a host-side launch), the
+    GPU is busy at its working clock when timing starts (an idle GPU, or one
+    running a spin kernel, lowers it), and the average spans the swings of
+    its power management (a few milliseconds each).  counts, if given,
+    receives each kind's (untimed, timed) launch counts."""
     torch = share.torch
-    for s_ in range(n_sets):   # allocated before the timed region
+    for s_ in range(n_sets):   # allocated before capture
         share.timing_bufs(s_)
     torch.cuda.synchronize()
     log = {}
     for name in names:
+        g = torch.cuda.CUDAGraph()
+        n = 0
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                n += share.launch_one(name, i % n_sets, timing=True)
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
         a_ev = torch.cuda.Event(enable_timing=True)
         b_ev = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        torch.cuda._sleep(int(2.4e9 * 0.02))
+        w0.record()
+        g.replay()
+        w1.record()
+        torch.cuda.synchronize()
+        reps = max(1, int(math.ceil(TIMED_MS / max(w0.elapsed_time(w1), 1e-3))))
+        g.replay()   # keeps the GPU busy while the timed replays are queued
         a_ev.record()
-        n = 0
-        for i in range(steps):
-            n += share.launch_one(name, i % n_sets, timing=True)
+        for _ in range(reps):
+            g.replay()
         b_ev.record()
         torch.cuda.synchronize()
-        log[name] = 1e3 * a_ev.elapsed_time(b_ev) / n
+        log[name] = 1e3 * a_ev.elapsed_time(b_ev) / (n * reps)
+        if counts is not None:
+            counts[name] = (2 * n, n * reps)
+        del g
     return log
 
 
@@ -1071,8 +1117,10 @@ def kernels_only(args):
         if n not in share.kernel_names:
             raise SystemExit("unknown launch kind %r (one of %s)" % (n, ", ".join(share.kernel_names)))
     share.step(0)
-    log = time_launches(share, names, args.steps, len(share.sets))
-    print(json.dumps({"workload": args.workload, "steps": args.steps, "us_per_launch": log}), flush=True)
+    counts = {}
+    log = time_launches(share, names, args.steps, len(share.sets), counts)
+    print(json.dumps({"workload": args.workload, "steps": args.steps, "us_per_launch": log,
+                      "launches_untimed_timed": counts}), flush=True)
 
 
 def measure(args, workload: str, steps: int, warmup: int, full: bool) -> dict:
@@ -1101,10 +1149,6 @@ def measure(args, workload: str, steps: int, warmup: int, full: bool) -> dict:
             share.step(s_)
         graphs.append(g)
     torch.cuda.synchronize()
-    for i in range(warmup):
-        graphs[i % n_sets].replay()
-    torch.cuda.synchronize()
-
     # replay check: a replay must reproduce the eager step bit for bit
     share.step(0)
     torch.cuda.synchronize()
@@ -1117,6 +1161,13 @@ def measure(args, workload: str, steps: int, warmup: int, full: bool) -> dict:
     if not replay_ok:
         print("graph replay differs from the eager step", file=sys.stderr)
         sys.exit(1)
+
+    # W warm-up replays right before the timed region (only the
+    # synchronisation between them): the GPU is at its working clock when
+    # timing starts
+    for i in range(warmup):
+        graphs[i % n_sets].replay()
+    torch.cuda.synchronize()
 
     # timed region 1: K graph replays (ms_per_step, value)
     t_start = torch.cuda.Event(enable_timing=True)
@@ -1170,9 +1221,8 @@ def measure(args, workload: str, steps: int, warmup: int, full: bool) -> dict:
         variants["backward"] = backward_variant(share, cfg_id, steps, warmup)
 
     # timed region 2: per-kernel durations.  Each launch of the step is
-    # repeated back to back over the rotating input sets between two HIP
-    # events on the launch stream; a spin kernel first gives the host a head
-    # start so no launch waits on the host.
+    # repeated back to back over the rotating input sets, captured in a HIP
+    # graph replayed untimed and then between two HIP events (time_launches).
     log = time_launches(share, share.kernel_names, steps, n_sets)
 
     n_attn = len(share.kv) if ring else len(share.ring)
@@ -1258,7 +1308,7 @@ def main():
         hbm_summary(args.hbm_summary, args.workload)
         return
     if args.stats_summary:
-        stats_summary(args.stats_summary)
+        stats_summary(args.stats_summary, args.last)
         return
     if args.counter_summary:
         counter_summary(args.counter_summary)

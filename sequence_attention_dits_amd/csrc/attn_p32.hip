@@ -9,42 +9,45 @@
 // (out, lse) of the pass.
 //
 // Layout as in attn_bf16.hip: a workgroup owns 256 query rows of one
-// (batch, head), 8 wavefronts of 32 rows, two per SIMD.  What differs is the
-// schedule inside each wavefront.  There, a tile step runs
-//   [A] the scores of tile t+1 (16 matrix instructions), each beside the
-//       softmax numerators of two of tile t's scores (vector work), then
-//   [B] O += V_t^T P_t (16 matrix instructions), each beside one step of the
-//       row maximum of tile t+1,
-// so matrix and vector work of one wavefront are independent of each other
-// and issue back to back, and the other wavefront of the SIMD fills the
-// gaps.  The softmax of the last 16-key chunk moves into [B] (its products
-// come last there), so that [A] carries three quarters of the vector work,
-// and [A] runs at raised wave priority; the first V operands of [B] are read
-// during the end of [A].  The step's barrier sits right after [B]'s last V
-// read, so the first K operands of the next step's [A] are read during the
-// last two slots of [B] instead of after the barrier.  Each of these
-// measured a few per cent, as did copying a Ring pass's previous O rows
-// into the free Q staging region by DMA at the start.  What the
-// pipelining itself takes, learnt the hard way:
-//  * the matrix instructions are inline assembly with their register files
-//    fixed (scores in VGPRs, O and Q in AGPRs): left to itself the compiler
-//    puts the scores in AGPRs and copies them every tile.  The compiler does
-//    not see them as matrix instructions, so vector code touching their
-//    results sits behind explicit wait states (fences below) or, inside a
-//    step, at least two matrix instructions later;
-//  * the loop body is six steps (two score-register parities x three LDS
-//    stages) with a uniform exit after each step, so a unit runs exactly its
-//    tile count; the inline-assembly accumulators stay where the matrix
-//    instructions write them across those exits (checked in the ISA: the
-//    steps' matrix blocks have no accumulator copies);
+// (batch, head), 8 wavefronts of 32 rows, two per SIMD (wavefront w on SIMD
+// w % 4).  What differs is the schedule.  A wavefront's tile step is two
+// phases: M(t), matrix instructions only -- the scores of tile t+1 and
+// O += V_t^T P_t, interleaved, with the step's K/V copies issued among them
+// -- and V(t), vector instructions only: the row maximum and softmax of tile
+// t+1.  Wavefronts 0..3 run M while 4..7 run V and the other way round, a
+// workgroup barrier between half-steps, so on every SIMD one wavefront's
+// matrix instructions run beside the other's vector instructions (the
+// other pairing, both wavefronts of a SIMD in the same phase, measured 22%
+// slower).  Per-phase timers in an instrumented build put the M phase at
+// about 1230 cycles of a tile (32 matrix instructions, 1024 cycles of matrix
+// work) and the V phase at about 1430, the SIMD's one vector issue port
+// being shared by the V phase's ~150 instructions and the M phase's matrix
+// issue; the clock under this load is about 1.5 GHz.  An earlier schedule
+// that interleaved both kinds of work inside each wavefront ran 1% slower.
+// What the pipelining takes, learnt the hard way:
+//  * the matrix instructions are inline assembly with their registers
+//    fixed in VGPRs (scores, O and Q; the vector code reads O in place when
+//    it rescales); the compiler does not see them as matrix instructions,
+//    so vector code touching their results sits behind explicit wait states
+//    (fences below);
+//  * the loop body is three M/V pairs (one per LDS stage), branch-free
+//    inside, with a uniform exit after each pair, so a unit runs exactly its
+//    tile count; a branch inside a phase made the compiler keep a second copy
+//    of the O accumulators;
+//  * the operand addresses pass through an empty asm at the start of each M
+//    phase; otherwise the compiler keeps stage-offset variants of them in
+//    registers across the loop and spills;
 //  * the softmax results are pinned with an empty asm before the branch
 //    that follows them; otherwise IR-level sinking moves the softmax below
-//    the branch, away from the matrix instructions it is meant to run beside;
+//    the branch;
 //  * K and V tiles are copied global -> LDS by buffer loads that write LDS,
 //    issued as inline assembly: as builtins, the compiler would make the next
 //    LDS reads wait for every copy in flight (vmcnt(0)), since it cannot tell
 //    the stage being read from the stage being filled.  Three stages each,
-//    copies two steps ahead, waited for explicitly before the step's barrier.
+//    copies two steps ahead, waited for explicitly before a barrier.
+// Measured and not kept: a deeper operand prefetch (3, 4, 6 matrix
+// instructions ahead: no change) and a row sum over the bf16 P values (the
+// LSE then carries the rounding of the weights, beyond its tolerance).
 // V is stored row-major with the 16-byte units of a row swizzled, and the PV
 // operands are read with ds_read_b64_tr_b16 (two give a lane the 8 keys of
 // one feature in the order the score registers hold them).  Row maximum
@@ -129,18 +132,18 @@ __device__ __forceinline__ void p_barrier()
     asm volatile("" ::: "memory");
 }
 
-// S (VGPRs) = K (VGPRs) x Q (AGPRs) [+ S];  O (AGPRs) += V (VGPRs) x P (VGPRs)
+// S = K x Q [+ S];  O += V x P  (every operand in VGPRs)
 __device__ __forceinline__ void p_mma_s0(p_f32x16& d, const p_bf16x8& k, const p_bf16x8& q)
 {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(k), "a"(q));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(k), "v"(q));
 }
 __device__ __forceinline__ void p_mma_s(p_f32x16& d, const p_bf16x8& k, const p_bf16x8& q)
 {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(k), "a"(q));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(k), "v"(q));
 }
 __device__ __forceinline__ void p_mma_o(p_f32x16& d, const p_bf16x8& v, const p_u32x4& p)
 {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(v), "v"(p));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(v), "v"(p));
 }
 // 32 wait states (more than any matrix result needs) before vector code
 // touches the scores or the O accumulators
@@ -150,13 +153,13 @@ __device__ __forceinline__ void p_fence_s(p_f32x16 (&s)[2])
 }
 __device__ __forceinline__ void p_fence_o(p_f32x16 (&o)[4])
 {
-    asm volatile("s_nop 15\n\ts_nop 15" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
+    asm volatile("s_nop 15\n\ts_nop 15" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
 }
-// the O accumulators are in AGPRs here (both sides of a branch that
+// the O accumulators are complete here (both sides of a branch that
 // rescales them leave them in the same registers)
 __device__ __forceinline__ void p_pin_o(p_f32x16 (&o)[4])
 {
-    asm volatile("" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
+    asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
 }
 // values complete at this point (keeps them from being sunk past a branch)
 __device__ __forceinline__ void p_pin_p(p_u32x4 (&p)[4])
@@ -400,7 +403,7 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
     p_pin_o(oacc);
     float m = -INFINITY;    // reference maximum (exp2 units) of this lane's row
     float lsum = 0.f;       // this lane half's share of the row sum
-    p_f32x16 sacc[2][2];    // [parity][jb]: scores S^T of a tile; register v of
+    p_f32x16 sacc[1][2];    // [0][jb]: scores S^T of a tile; register v of
                             // block jb holds key 32 jb + 8 (v / 4) + 4 hg + v % 4
 
     // Keys at or past lim of a tile -> -inf (the ragged end, read as zeros;
@@ -477,8 +480,7 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
     };
     // score instruction r (0..15): k-chunk r / 2, key block r % 2; its K
     // operand is read two instructions ahead
-    constexpr int KPF = 2, VPF = 2;   // the barrier placement in [B] assumes KPF == VPF
-    static_assert(KPF == VPF, "[B] reads its last V operand in slot 15 - VPF and the next K operands after it");
+    constexpr int KPF = 2, VPF = 2;   // operands read this many matrix instructions ahead
     auto score_mma = [&](p_f32x16 (&s)[2], p_bf16x8 (&kop)[16], int ks, int r) {
         const int kc = r >> 1, jb = r & 1;
         if (r + KPF < 16) kop[r + KPF] = kread(ks, (r + KPF) >> 1, (r + KPF) & 1);
@@ -492,12 +494,31 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
         p_mma_o(oacc[r & 3], vop[r], pw[r >> 2]);
     };
 
-    // ---- main loop ---------------------------------------------------------
-    // K tile j and V tile j in stage j % 3.  Step t reads K stage (t+1) % 3
-    // (tile t+1) and V stage t % 3 (tile t), and copies K tile t+3 into stage
-    // t % 3 and V tile t+2 into stage (t+2) % 3 (both read last in step t-1,
-    // before its closing barrier), among its PV instructions; a copy has a
-    // whole step to land.  Copies past the end repeat the last tile.
+    // ---- main loop: two wave groups in ping-pong -------------------------
+    // A step of one wave is two phases: M(t), its matrix instructions only
+    // -- the scores of tile t+1 (K stage (t+1) % 3) and O += V_t^T P_t (V
+    // stage t % 3) -- and V(t), its vector work only: the row maximum and
+    // softmax of tile t+1, which give P_{t+1}.  Waves 0..3 (one per SIMD)
+    // run M(t) while waves 4..7 (the other wave of each SIMD) run V(t-1),
+    // and the other way round, one workgroup barrier between half-steps: on
+    // every SIMD one wave's matrix instructions run beside the other wave's
+    // vector instructions.  M(t) also copies K tile t+3 into stage t % 3 and
+    // V tile t+2 into stage (t+2) % 3 (both read last in M(t-1), a half-step
+    // or more before) and, before its closing barrier, waits for the copies
+    // of M(t-1), which M(t+1) reads.  Copies past the end repeat the last
+    // tile.  One score buffer serves: V(t) consumes the scores of tile t+1
+    // before M(t+1) writes those of tile t+2.
+    p_u32x4 pw[4];
+    auto softmax = [&]() {
+        const float mu = m == -INFINITY ? 0.f : m;
+        ps0 = 0.f;
+        ps1 = 0.f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) soft_op(sacc[0], pw, mu, k);
+        lsum += ps0 + ps1;
+        p_pin_f(lsum);
+        p_pin_p(pw);
+    };
     if (n > 0) {
         p_bf16x8 kop[16];
 #pragma unroll
@@ -509,21 +530,17 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
 #pragma unroll
         for (int j = 0; j < 16; ++j) max_op(sacc[0], j);
         finish_max();
+        softmax();
     }
-    // every wave is done with K stage 0 before step 0 copies tile 3 into it,
-    // and K1 and V0 have landed (K2 and V1 may still run: step 0 waits for
+    // every wave is done with K stage 0 before M(0) copies tile 3 into it,
+    // and K1 and V0 have landed (K2 and V1 may still run: M(0) waits for
     // them before its barrier)
     __builtin_amdgcn_s_waitcnt(0x0F70 | 4);   // vmcnt(4)
     p_barrier();
-    // the first K operands of each step's [A] are read at the end of the
-    // step before (after its barrier): step 0's here
-    p_bf16x8 knext[KPF];
-#pragma unroll
-    for (int r = 0; r < KPF; ++r) knext[r] = kread(1, r >> 1, r & 1);
     // Continuing a Ring pass with bf16 output: the previous result's rows of
     // this wave are copied now into its Q staging region (free once Q is in
     // registers), and its LSE loaded, so that the epilogue's merge does not
-    // wait for them.  The copies land before step 0 ends (its vmcnt wait).
+    // wait for them.  The copies land before the epilogue (its vmcnt wait).
     float lse_prev = -INFINITY;
     if (a.acc && su < 0) {
         if (i < Sq) lse_prev = a.lse[(b * Sq + i) * H + hh];
@@ -539,89 +556,74 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void attn_p32_kernel(const AttnArg
                       (uint32_t)(uintptr_t)(L + OFF_Q + wave * 32 * kPRowB + j * 1024));
         }
     }
-    auto step = [&](auto parity_tag, auto t3_tag, int t) {
-        constexpr int P = decltype(parity_tag)::value, T3 = decltype(t3_tag)::value;
+    const bool lead = wave < kPWaves / 2;
+    // M(t): the scores of tile t+1 interleaved with the PV instructions of
+    // tile t (past the last tile the scores are computed and masked)
+    auto mphase = [&](auto t3_tag, int t) {
+        constexpr int T3 = decltype(t3_tag)::value;
         constexpr int KS = (T3 + 1) % 3, VS = T3;
         const int tk = t + 3 < n ? t + 3 : n - 1, tv = t + 2 < n ? t + 2 : n - 1;
-        const float mu = m == -INFINITY ? 0.f : m;
-        ps0 = 0.f;
-        ps1 = 0.f;
-        p_u32x4 pw[4];
-        p_bf16x8 vop[16];
-        // [A] scores of tile t+1 beside the softmax of tile t
-        {
-            p_bf16x8 kop[16];
+        p_bf16x8 kop[16], vop[16];
+        // the operand addresses pass through here each phase: nothing
+        // derived from them (stage offsets, which the reads take as
+        // immediates) is kept in registers across the loop
 #pragma unroll
-            for (int r = 0; r < KPF; ++r) kop[r] = knext[r];
-            __builtin_amdgcn_s_setprio(1);
+        for (int kc = 0; kc < 8; ++kc) asm volatile("" : "+v"(kaddr[kc]));
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                score_mma(sacc[P ^ 1], kop, KS, r);
-                if ((r & 3) != 3) {
-                    const int x = r - (r >> 2), c = x >> 2;
-                    soft_op(sacc[P], pw, mu, (c >> 1) * 8 + (c & 1) * 4 + (x & 3));
-                }
-                if (r >= 16 - VPF) vop[r - (16 - VPF)] = vread(VS, (r - (16 - VPF)) >> 2, (r - (16 - VPF)) & 3);
-                __builtin_amdgcn_sched_barrier(0);
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int db = 0; db < 4; ++db) asm volatile("" : "+v"(vaddr[k][db]));
+#pragma unroll
+        for (int r = 0; r < KPF; ++r) kop[r] = kread(KS, r >> 1, r & 1);
+#pragma unroll
+        for (int r = 0; r < VPF; ++r) vop[r] = vread(VS, r >> 2, r & 3);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            score_mma(sacc[0], kop, KS, r);
+            pv_mma(vop, pw, VS, r);
+            if ((r & 3) == 1) {
+                const int c = r >> 2;
+                if (c < 2) copy_tile(krs, OFF_K, tk, T3, c);
+                else copy_tile(vrs, OFF_V, tv, (T3 + 2) % 3, c - 2);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
-        p_pin_p(pw);
+        // the copies of M(t-1) have landed (this phase's 4 may still run)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
+        p_barrier();
+    };
+    // V(t): the row maximum and softmax of tile t+1 (past the last tile:
+    // every key masked, nothing changes)
+    auto vphase = [&](int t) {
+        // the last score instructions of M(t) have written their registers
+        p_fence_s(sacc[0]);
         const int lim = key_lim(t + 1);
-        if (tile_masked(lim)) mask_keys(sacc[P ^ 1], lim);
-        // [B] O += V_t^T P_t beside the row maximum of tile t+1 (its scores
-        // were written at least two matrix instructions, > 60 cycles,
-        // before), with this step's copies among them
-        {
+        if (tile_masked(lim)) mask_keys(sacc[0], lim);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                pv_mma(vop, pw, VS, r);
-                if (r < 8 && (r & 1) == 0) soft_op(sacc[P], pw, mu, 12 + (r >> 1));
-                max_op(sacc[P ^ 1], r);
-                if ((r & 3) == 1) {
-                    const int c = r >> 2;
-                    if (c < 2) copy_tile(krs, OFF_K, tk, T3, c);
-                    else copy_tile(vrs, OFF_V, tv, (T3 + 2) % 3, c - 2);
-                }
-                if (r == 15 - KPF) {
-                    // this wave's last V read of the step is done: the copies
-                    // of step t-1 (K tile t+2, V tile t+1) have landed (this
-                    // step's 4 may still run), and after the barrier every
-                    // wave is done with the stages the next step's copies fill
-                    __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
-                    p_barrier();
-                }
-                if (r > 15 - KPF) {
-                    const int x = r - (16 - KPF);
-                    knext[x] = kread((T3 + 2) % 3, x >> 1, x & 1);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        lsum += ps0 + ps1;
-        p_pin_f(lsum);
+        for (int j = 0; j < 16; ++j) max_op(sacc[0], j);
         p_pin_f(mx);
         finish_max();
+        softmax();
+        p_barrier();
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    // six steps per iteration (two score parities x three stages), left
-    // after whichever step reaches the unit's tile count
-    for (int t = 0; n > 0; t += 6) {
-        step(I0{}, I0{}, t);
+    if (!lead) p_barrier();   // the second group starts a half-step later
+    for (int t = 0; n > 0; t += 3) {
+        mphase(I0{}, t);
+        vphase(t);
         if (t + 1 >= n) break;
-        step(I1{}, I1{}, t + 1);
+        mphase(I1{}, t + 1);
+        vphase(t + 1);
         if (t + 2 >= n) break;
-        step(I0{}, I2{}, t + 2);
+        mphase(I2{}, t + 2);
+        vphase(t + 2);
         if (t + 3 >= n) break;
-        step(I1{}, I0{}, t + 3);
-        if (t + 4 >= n) break;
-        step(I0{}, I1{}, t + 4);
-        if (t + 5 >= n) break;
-        step(I1{}, I2{}, t + 5);
-        if (t + 6 >= n) break;
     }
+    if (lead) p_barrier();    // and ends a half-step later
     // the last copies (into stages nothing reads) have landed and every wave
     // is done with the stages before the LDS is reused; O is final
     __builtin_amdgcn_s_waitcnt(0x0F70);
