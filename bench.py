@@ -214,6 +214,8 @@ class Share:
                 "lse": 8 + torch.randn(B, S, Hr, device="cuda"),
                 "o_tok": torch.empty(B, S0, H, D, device="cuda", dtype=bf),
                 "l_tok": torch.empty(B, S0, H, 1, device="cuda", dtype=torch.float32),
+                "copy": _copy_bufs(torch, {"copy_permute": self.permute_bytes(), "copy_qkv": 3 * self.permute_bytes(),
+                                           "copy_merge": self.merge_bytes()}),
             }
         return self._tbufs[s]
 
@@ -274,6 +276,10 @@ class Share:
             uaa.uaa_seq2head_permute_multi(uaa.UAA_HEAD2SEQ, 0, [[o, d["o_other"]], [lse.unsqueeze(-1), d["l_other"]]],
                                            [o_tok, l_tok], self.seq_off, self.head_off)
             return 1
+        if name.startswith("copy_"):
+            src, dst = t["copy"][name]
+            dst.copy_(src)
+            return 1
         if name == "head2seq_lse":
             uaa.uaa_seq2head_permute(uaa.UAA_HEAD2SEQ, 0, [lse.unsqueeze(-1), d["l_other"]], l_tok, self.seq_off,
                                      self.head_off)
@@ -282,6 +288,9 @@ class Share:
 
     kernel_names = ("permute", "permute_qkv", "attn", "attn_acc", "merge", "head2seq", "head2seq_lse",
                     "head2seq_o_lse")
+    # plain device copies of the HBM-bound launches' byte counts (read + write),
+    # timed the same way: the reference those launches are measured against
+    copy_names = ("copy_permute", "copy_qkv", "copy_merge")
 
     def attn_chunk(self, s, c, ws, acc=False, bufs=None):
         """Chunk c's attention into its partial buffers, or with acc into the
@@ -430,6 +439,7 @@ class RingShare:
                 self.pairs.append(float(np.searchsorted(np.sort(kpos), qpos, side="right").sum()))
 
     kernel_names = ("attn", "attn_acc", "merge")
+    copy_names = ("copy_merge",)
 
     def attn_flops(self, chunk):
         return 4.0 * self.D * self.H * self.B * self.pairs[chunk]
@@ -449,8 +459,10 @@ class RingShare:
             self._tbufs[s] = {
                 "o_part": [torch.randn(*shp, self.D, device="cuda").to(bf) for _ in self.kv],
                 "l_part": [8 + torch.randn(*shp, device="cuda") for _ in self.kv],
-                "o": torch.empty(*shp, self.D, device="cuda", dtype=bf),
-                "lse": torch.empty(*shp, device="cuda", dtype=torch.float32),
+                # the running (O, LSE) the accumulating launches merge into: finite
+                "o": torch.randn(*shp, self.D, device="cuda").to(bf),
+                "lse": 8 + torch.randn(*shp, device="cuda"),
+                "copy": _copy_bufs(torch, {"copy_merge": self.merge_bytes()}),
             }
         return self._tbufs[s]
 
@@ -465,6 +477,10 @@ class RingShare:
             for c in range(1, len(self.kv)):
                 self.attn_chunk(s, c, self.ws[0], acc=True, into=(t["o"], t["lse"]) if timing else None)
             return len(self.kv) - 1
+        if name.startswith("copy_"):
+            src, dst = self.timing_bufs(s)["copy"][name]
+            dst.copy_(src)
+            return 1
         if name == "merge":
             if timing:
                 t = self.timing_bufs(s)
@@ -645,6 +661,13 @@ def backward_variant(share, cfg_id: int, steps: int, warmup: int) -> dict:
             "launches_per_step": 1 + len(chunks), "grad_dtype": "fp32"}
 
 
+def _copy_bufs(torch, sizes):
+    """Source and destination of a plain device copy per entry, each moving
+    `bytes` (half read, half written)."""
+    return {k: (torch.ones(int(n) // 8, device="cuda"), torch.empty(int(n) // 8, device="cuda"))
+            for k, n in sizes.items()}
+
+
 def _contig(t):
     # a K/V chunk of the head-sharded tensor is a slice along S: with B = 1 it
     # is already contiguous, so no copy is made here
@@ -699,7 +722,7 @@ def cpu_baseline(share: "Share", target_s: float):
 
 # ---- HBM traffic of the attention kernel (rocprofv3 counters) ---------------
 PMC_COPY_BYTES = 1 << 30              # calibration copy: a plain device-to-device copy of 1 GiB
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_flux1024_hbm_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_p32_flux1024_hbm_traffic.txt")
 ATTN_SOURCES = ["attn_bf16.hip", "attn_p32.hip", "attn_common.h", "internal.h"]
 
 
@@ -1044,6 +1067,13 @@ def stats_summary(d, last: int = 0):
             tail = ts[-last:]
             nm = name if len(name) <= 70 else name[:67] + "..."
             print("%-70s %6d %12.2f" % (nm, len(tail), sum(e - b for b, e in tail) / len(tail) / 1e3))
+        # a launch kind that runs several attention kernels (the masked Ring
+        # pass: plain and DIAG forms): its last N attention dispatches together
+        att = sorted(t for name, ts in by.items() if _is_attn_fwd(name) for t in ts)
+        if len(att) >= last and len([n for n in by if _is_attn_fwd(n)]) > 1:
+            tail = att[-last:]
+            print("%-70s %6d %12.2f" % ("(every attention-forward kernel together)", len(tail),
+                                        sum(e - b for b, e in tail) / len(tail) / 1e3))
 
 
 TIMED_MS = 20.0   # least GPU time of one launch kind's timed region
@@ -1113,9 +1143,10 @@ def kernels_only(args):
     kernel trace of this command averages exactly those launches."""
     share = make_share(args.workload, args.sets or n_sets_for(args.workload))
     names = [n for n in args.kernels_only.split(",") if n]
+    kinds = share.kernel_names + share.copy_names
     for n in names:
-        if n not in share.kernel_names:
-            raise SystemExit("unknown launch kind %r (one of %s)" % (n, ", ".join(share.kernel_names)))
+        if n not in kinds:
+            raise SystemExit("unknown launch kind %r (one of %s)" % (n, ", ".join(kinds)))
     share.step(0)
     counts = {}
     log = time_launches(share, names, args.steps, len(share.sets), counts)
@@ -1223,7 +1254,7 @@ def measure(args, workload: str, steps: int, warmup: int, full: bool) -> dict:
     # timed region 2: per-kernel durations.  Each launch of the step is
     # repeated back to back over the rotating input sets, captured in a HIP
     # graph replayed untimed and then between two HIP events (time_launches).
-    log = time_launches(share, share.kernel_names, steps, n_sets)
+    log = time_launches(share, share.kernel_names + share.copy_names, steps, n_sets)
 
     n_attn = len(share.kv) if ring else len(share.ring)
     attn_flops = sum(share.attn_flops(c_) for c_ in range(n_attn))
@@ -1233,9 +1264,15 @@ def measure(args, workload: str, steps: int, warmup: int, full: bool) -> dict:
     attn_tf = attn_flops_launch / (attn_us * 1e-6) / 1e12
     merge_us = log["merge"]
     merge_gbps = share.merge_bytes() / (merge_us * 1e-6) / 1e9
+    def vs_copy(us, name):
+        # the same bytes moved by a plain device copy, timed the same way
+        c = log[name]
+        return {"copy_us": round(c, 2), "frac_of_copy": round(c / us, 4)}
+
     kernels = {
         "lse_merge": {"us": round(merge_us, 2), "GB/s": round(merge_gbps, 1),
-                      "hbm_frac": round(merge_gbps / PEAK_HBM_GBPS, 4), "bytes": share.merge_bytes()},
+                      "hbm_frac": round(merge_gbps / PEAK_HBM_GBPS, 4), "bytes": share.merge_bytes(),
+                      **vs_copy(merge_us, "copy_merge")},
         "attention": {"us": round(attn_us, 2), "TFLOP/s": round(attn_tf, 2),
                       "mfma_frac": round(attn_tf / PEAK_BF16_TFLOPS, 4)},
         "attention_acc": {"us": round(log["attn_acc"], 2)},
@@ -1252,12 +1289,14 @@ def measure(args, workload: str, steps: int, warmup: int, full: bool) -> dict:
         h2s_gbps = share.head2seq_bytes() / (h2s_us * 1e-6) / 1e9
         kernels.update({
             "seq2head_permute": {"us": round(perm_us, 2), "GB/s": round(perm_gbps, 1),
-                                 "hbm_frac": round(perm_gbps / PEAK_HBM_GBPS, 4), "bytes": share.permute_bytes()},
+                                 "hbm_frac": round(perm_gbps / PEAK_HBM_GBPS, 4), "bytes": share.permute_bytes(),
+                                 **vs_copy(perm_us, "copy_permute")},
             "seq2head_permute_qkv": {"us": round(qkv_us, 2), "GB/s": round(qkv_gbps, 1),
                                      "hbm_frac": round(qkv_gbps / PEAK_HBM_GBPS, 4),
-                                     "bytes": 3 * share.permute_bytes()},
+                                     "bytes": 3 * share.permute_bytes(), **vs_copy(qkv_us, "copy_qkv")},
             "head2seq_permute": {"us": round(h2s_us, 2), "GB/s": round(h2s_gbps, 1),
-                                 "hbm_frac": round(h2s_gbps / PEAK_HBM_GBPS, 4), "bytes": share.head2seq_bytes()},
+                                 "hbm_frac": round(h2s_gbps / PEAK_HBM_GBPS, 4), "bytes": share.head2seq_bytes(),
+                                 **vs_copy(h2s_us, "copy_permute")},
             "head2seq_permute_o_lse": {"us": round(log["head2seq_o_lse"], 2),
                                        "bytes": share.head2seq_bytes() + share.head2seq_lse_bytes()},
         })
