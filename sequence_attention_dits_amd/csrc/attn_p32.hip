@@ -145,11 +145,12 @@ __device__ __forceinline__ void p_mma_o(p_f32x16& d, const p_bf16x8& v, const p_
 {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(v), "v"(p));
 }
-// 32 wait states (more than any matrix result needs) before vector code
-// touches the scores or the O accumulators
+// wait states before vector code touches matrix results: 16 for the scores
+// (the compiler itself places 12 between a 32x32x16 bf16 matrix instruction
+// and a vector read of its result), 32 for the O accumulators
 __device__ __forceinline__ void p_fence_s(p_f32x16 (&s)[2])
 {
-    asm volatile("s_nop 15\n\ts_nop 15" : "+v"(s[0]), "+v"(s[1]));
+    asm volatile("s_nop 15" : "+v"(s[0]), "+v"(s[1]));
 }
 __device__ __forceinline__ void p_fence_o(p_f32x16 (&o)[4])
 {
