@@ -428,15 +428,19 @@ class RingShare:
         self.lse = torch.empty(self.B, self.Sq, self.H, device="cuda", dtype=torch.float32)
         self.ws = [_workspace(uaa, d0["q"], [d0["k"][:, a:b] for a, b in self.kv], self.masks) for _ in range(2)]
         self.side = torch.cuda.Stream()   # default priority
-        # allowed (query, key) pairs of each launch, from the position maps
-        self.pairs = []
+        # allowed (query, key) pairs of each launch, from the position maps,
+        # and the query rows with at least one allowed key in each chunk (the
+        # others come out of the launch as (0, -inf) and the merge does not
+        # read their O)
+        self.pairs, self.live = [], []
         for (a, b), m in zip(self.kv, self.masks):
             if m is None:
                 self.pairs.append(float(self.Sq) * (b - a))
+                self.live.append(np.ones(self.Sq, dtype=bool))
             else:
-                qpos = q_rows
-                kpos = np.arange(a, b)
-                self.pairs.append(float(np.searchsorted(np.sort(kpos), qpos, side="right").sum()))
+                cnt = np.searchsorted(np.arange(a, b), q_rows, side="right")
+                self.pairs.append(float(cnt.sum()))
+                self.live.append(cnt > 0)
 
     kernel_names = ("attn", "attn_acc", "merge")
     copy_names = ("copy_merge",)
@@ -445,20 +449,27 @@ class RingShare:
         return 4.0 * self.D * self.H * self.B * self.pairs[chunk]
 
     def merge_bytes(self):
+        """The N-way merge's algorithmic bytes: every partial LSE, the O rows
+        of the partials whose chunk has an allowed key for the row (a row
+        without one has LSE -inf and weight 0, so its O is not read), and the
+        merged (O, LSE)."""
         rows = self.B * self.Sq * self.H
-        per = rows * self.D * 2 + rows * 4
-        return len(self.kv) * per + per
+        live_rows = sum(int(l.sum()) for l in self.live) * self.B * self.H
+        return live_rows * self.D * 2 + len(self.kv) * rows * 4 + rows * (self.D * 2 + 4)
 
     def timing_bufs(self, s):
-        """Per-set partials and result for the merge timing (see Share)."""
+        """Per-set partials and result for the merge timing (see Share); the
+        partial LSEs are -inf on the rows a chunk's mask leaves empty, as the
+        attention launches leave them."""
         if not hasattr(self, "_tbufs"):
             self._tbufs = {}
         if s not in self._tbufs:
             torch, bf = self.torch, self.torch.bfloat16
             shp = (self.B, self.Sq, self.H)
+            dead = [torch.from_numpy(~l).cuda().view(1, -1, 1).expand(*shp) for l in self.live]
             self._tbufs[s] = {
                 "o_part": [torch.randn(*shp, self.D, device="cuda").to(bf) for _ in self.kv],
-                "l_part": [8 + torch.randn(*shp, device="cuda") for _ in self.kv],
+                "l_part": [(8 + torch.randn(*shp, device="cuda")).masked_fill(d, float("-inf")) for d in dead],
                 # the running (O, LSE) the accumulating launches merge into: finite
                 "o": torch.randn(*shp, self.D, device="cuda").to(bf),
                 "lse": 8 + torch.randn(*shp, device="cuda"),

@@ -381,7 +381,9 @@ size_t usp_attn_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t Sq, int
  * and (o, lse) = (0, -inf) when every lse_n is -inf.  On finite inputs this
  * is the pages' pairwise sigmoid / log-sigmoid update folded over n; the
  * max-shifted form also accepts -inf partials, which the pairwise form
- * turns into NaN.
+ * turns into NaN.  A partial whose lse_n is -inf for a row (its block had
+ * no allowed key there) has weight 0 and its O row is not read: whatever
+ * it holds, the row's result is that of the other partials.
  *
  *   o_parts   host array of n_parts device pointers, each [B, S, H, D]
  *             part_dtype

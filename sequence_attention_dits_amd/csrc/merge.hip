@@ -12,9 +12,12 @@
 //
 // HBM-bound: each row is D contiguous elements per partial.  A row is split
 // over D / VEC lanes (VEC elements = 16 bytes each), so a wavefront covers
-// several rows with fully coalesced 16-byte accesses; every lane loads all
-// N partial slices before it does any arithmetic, and the few LSE loads per
-// row are shared by the row's lanes through the cache.
+// several rows with fully coalesced 16-byte accesses.  The few LSE loads of
+// a row come first (shared by the row's lanes through the cache); a partial
+// whose LSE is -inf had no allowed key in its block and gets weight 0, so
+// its O slice is not read at all (in a zigzag Ring pass that is half the
+// rows of most key blocks); the other partials' slices are all loaded before
+// any arithmetic.
 #include "internal.h"
 
 namespace uaa {
@@ -35,13 +38,17 @@ __device__ __forceinline__ unsigned short f32_to_bf16(float f)
     return (unsigned short)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// VEC elements of type T at p, widened to fp32.
+// VEC elements of type T: loaded as raw bits (Raw; zero bits are 0.0) and
+// widened to fp32 only where the arithmetic needs them, so the loads of all
+// partials in flight hold half the registers for bf16.
 template <typename T, int VEC> struct Slice;
 
 template <> struct Slice<unsigned short, 8> {     // bf16, 16 bytes
-    static __device__ __forceinline__ void load(const void* p, float* x)
+    typedef u32x4 Raw;
+    static __device__ __forceinline__ Raw load(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+    static __device__ __forceinline__ Raw zero() { return u32x4{0u, 0u, 0u, 0u}; }
+    static __device__ __forceinline__ void widen(const Raw& w, float* x)
     {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(p);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             x[2 * e] = __uint_as_float(w[e] << 16);
@@ -59,9 +66,11 @@ template <> struct Slice<unsigned short, 8> {     // bf16, 16 bytes
 };
 
 template <> struct Slice<float, 4> {              // fp32, 16 bytes
-    static __device__ __forceinline__ void load(const void* p, float* x)
+    typedef u32x4 Raw;
+    static __device__ __forceinline__ Raw load(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+    static __device__ __forceinline__ Raw zero() { return u32x4{0u, 0u, 0u, 0u}; }
+    static __device__ __forceinline__ void widen(const Raw& w, float* x)
     {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(p);
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e]);
     }
@@ -75,10 +84,10 @@ template <> struct Slice<float, 4> {              // fp32, 16 bytes
 };
 
 template <> struct Slice<unsigned short, 1> {     // bf16, any D
-    static __device__ __forceinline__ void load(const void* p, float* x)
-    {
-        x[0] = bf16_to_f32(*reinterpret_cast<const unsigned short*>(p));
-    }
+    typedef unsigned short Raw;
+    static __device__ __forceinline__ Raw load(const void* p) { return *reinterpret_cast<const unsigned short*>(p); }
+    static __device__ __forceinline__ Raw zero() { return 0; }
+    static __device__ __forceinline__ void widen(const Raw& w, float* x) { x[0] = bf16_to_f32(w); }
     static __device__ __forceinline__ void store(void* p, const float* x)
     {
         *reinterpret_cast<unsigned short*>(p) = f32_to_bf16(x[0]);
@@ -86,10 +95,10 @@ template <> struct Slice<unsigned short, 1> {     // bf16, any D
 };
 
 template <> struct Slice<float, 1> {              // fp32, any D
-    static __device__ __forceinline__ void load(const void* p, float* x)
-    {
-        x[0] = *reinterpret_cast<const float*>(p);
-    }
+    typedef float Raw;
+    static __device__ __forceinline__ Raw load(const void* p) { return *reinterpret_cast<const float*>(p); }
+    static __device__ __forceinline__ Raw zero() { return 0.f; }
+    static __device__ __forceinline__ void widen(const Raw& w, float* x) { x[0] = w; }
     static __device__ __forceinline__ void store(void* p, const float* x)
     {
         *reinterpret_cast<float*>(p) = x[0];
@@ -99,9 +108,9 @@ template <> struct Slice<float, 1> {              // fp32, any D
 // A row's D / VEC slices are spread over `lpr` lanes (a power of two, at most
 // 64; lanes loop when a row has more slices), so a wavefront covers 64 / lpr
 // rows side by side and no lane index needs a division.  Each lane group
-// handles RU rows per pass: the O slices of all partials of all RU rows are
-// loaded first (they do not depend on the LSEs), then the LSEs, then the
-// weights and the weighted sums.
+// handles RU rows per pass: the LSEs of all partials of its rows are loaded
+// first, then the O slices of the partials with a finite LSE (the others
+// count as zero: their weight is 0), then the weights and weighted sums.
 template <typename TIn, typename TOut, int VEC, int NMAX, int RU>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a, int lpr_log2)
 {
@@ -113,29 +122,32 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a, int lpr_l
     const int N = a.n_parts;
     const int slices = a.D / VEC;              // host guarantees divisibility
 
+    float lse[RU][NMAX];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+        const int64_t row = row0 + (int64_t)u * groups;
+#pragma unroll
+        for (int n = 0; n < NMAX; ++n) lse[u][n] = (n < N && row < a.rows) ? a.lse_parts[n][row] : -INFINITY;
+    }
     for (int seg = lane & (lpr - 1); seg < slices; seg += lpr) {
-        float x[RU][NMAX][VEC];
+        typedef Slice<TIn, VEC> In;
+        typename In::Raw x[RU][NMAX];
 #pragma unroll
         for (int u = 0; u < RU; ++u) {
             const int64_t row = row0 + (int64_t)u * groups;
-            if (row < a.rows) {
-                const int64_t elem = row * a.D + (int64_t)seg * VEC;
+            const int64_t elem = row * a.D + (int64_t)seg * VEC;
 #pragma unroll
-                for (int n = 0; n < NMAX; ++n)
-                    if (n < N) Slice<TIn, VEC>::load(reinterpret_cast<const TIn*>(a.o_parts[n]) + elem, x[u][n]);
-            }
+            for (int n = 0; n < NMAX; ++n)   // only rows < a.rows and partials n < N have a finite LSE
+                x[u][n] = lse[u][n] != -INFINITY ? In::load(reinterpret_cast<const TIn*>(a.o_parts[n]) + elem)
+                                                 : In::zero();
         }
 #pragma unroll
         for (int u = 0; u < RU; ++u) {
             const int64_t row = row0 + (int64_t)u * groups;
             if (row >= a.rows) continue;
-            float lse[NMAX];
             float M = -INFINITY;
 #pragma unroll
-            for (int n = 0; n < NMAX; ++n) {
-                lse[n] = (n < N) ? a.lse_parts[n][row] : -INFINITY;
-                M = fmaxf(M, lse[n]);
-            }
+            for (int n = 0; n < NMAX; ++n) M = fmaxf(M, lse[u][n]);
             float acc[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
@@ -144,22 +156,23 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a, int lpr_l
                 float sum = 0.f;
 #pragma unroll
                 for (int n = 0; n < NMAX; ++n)
-                    if (n < N) sum += __expf(lse[n] - M);
+                    if (n < N) sum += __expf(lse[u][n] - M);
                 L = M + __logf(sum);
 #pragma unroll
                 for (int n = 0; n < NMAX; ++n)
                     if (n < N) {
-                        const float w = __expf(lse[n] - L);
+                        const float w = __expf(lse[u][n] - L);
+                        float xv[VEC];
+                        In::widen(x[u][n], xv);
 #pragma unroll
-                        for (int e = 0; e < VEC; ++e) acc[e] = fmaf(w, x[u][n][e], acc[e]);
+                        for (int e = 0; e < VEC; ++e) acc[e] = fmaf(w, xv[e], acc[e]);
                     }
             }
             const int64_t elem = row * a.D + (int64_t)seg * VEC;
             Slice<TOut, VEC>::store(reinterpret_cast<TOut*>(a.o_out) + elem, acc);
-            // lse_out may be one of the partials' LSE arrays: it is written
-            // only in the pass after which no lane of the row reads the
-            // partial LSEs again (the lane of slice 0 makes the most passes,
-            // and the row's lanes are one wavefront, in step)
+            // lse_out may be one of the partials' LSE arrays: every lane read
+            // its row's partial LSEs before the first pass, and the row's
+            // lanes are one wavefront, in step
             if ((seg & (lpr - 1)) == 0 && seg + lpr >= slices) a.lse_out[row] = L;
         }
     }

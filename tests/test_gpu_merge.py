@@ -88,6 +88,42 @@ def test_merge_neg_inf_rules():
     assert (host_f64(o_out)[0, 1] == 0).all() and np.isneginf(host_f64(l_out)[0, 1]).all()
 
 
+@pytest.mark.parametrize("din,dout,D", [("bf16", "bf16", 128), ("fp32", "fp32", 64), ("bf16", "bf16", 33),
+                                         ("bf16", "fp32", 128)])
+def test_merge_does_not_read_empty_partials(din, dout, D):
+    """Rows where a partial's LSE is -inf take nothing from its O, which is
+    not read: NaN there gives the same bits as zeros (the zigzag layout's
+    key blocks after half the queries), and both match the oracle with 0."""
+    shape = (2, 300, 3, D)
+    say("merge empty partials not read", din, dout, D)
+    o_bits, o_vals, l_vals = _partials(7, 5, shape, din)
+    # partial 1: the second half of the rows empty; partial 4: every row empty;
+    # partial 2: scattered rows empty
+    l_vals[1][:, 150:] = -np.inf
+    l_vals[4][:] = -np.inf
+    l_vals[2][synth.rng(7, 400).random(shape[:3]) < 0.3] = -np.inf
+    nan_bits, zero_vals = [], []
+    for b, v, l in zip(o_bits, o_vals, l_vals):
+        empty = np.isneginf(l)
+        nb = b.copy()
+        nb[empty] = 0x7FC0 if din == "bf16" else np.nan   # a quiet NaN in the storage dtype
+        zv = v.copy()
+        zv[empty] = 0.0
+        nan_bits.append(nb)
+        zero_vals.append(zv)
+    zero_bits = [b.copy() for b in o_bits]
+    for zb, l in zip(zero_bits, l_vals):
+        zb[np.isneginf(l)] = 0
+    o_nan, l_nan = _gpu_merge(nan_bits, l_vals, din, dout)
+    o_zero, l_zero = _gpu_merge(zero_bits, l_vals, din, dout)
+    assert torch.equal(l_nan, l_zero)
+    assert torch.equal(o_nan.view(torch.int16) if dout == "bf16" else o_nan.view(torch.int32),
+                       o_zero.view(torch.int16) if dout == "bf16" else o_zero.view(torch.int32))
+    o_ref, l_ref = oracle.lse_merge(zero_vals, [l.astype(np.float64) for l in l_vals])
+    check_pair(host_f64(o_nan), host_f64(l_nan), o_ref, l_ref, "fp32" if din == "fp32" else "bf16",
+               "empty partials")
+
+
 def test_merge_single_partial_copies():
     o = [np.random.default_rng(1).standard_normal((1, 40, 3, 64)).astype(np.float32)]
     l = [np.random.default_rng(2).standard_normal((1, 40, 3)).astype(np.float32)]
