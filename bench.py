@@ -1389,7 +1389,19 @@ def main():
                                                       "kernels", "cpu_baseline") if k in r}
         out["workloads_note"] = ("the tiny ragged fp32 share (257 tokens, 129/128) is a correctness case: every "
                                  "row is checked in the GPU tests, it is not timed")
+    out["library"] = library_record()
     print(json.dumps(out), flush=True)
+
+
+def library_record() -> dict:
+    """Which native library this run called: its file and the build id
+    compiled into it (sha256 of the csrc sources and build flags; the binding
+    refuses a library whose id differs from the sources beside it)."""
+    from sequence_attention_dits_amd import binding, build
+    lib = binding.lib()
+    return {"file": os.path.relpath(lib._name, os.path.dirname(os.path.abspath(__file__))),
+            "build_id": lib.uaa_build_id().decode(), "sources_id": build.source_id(),
+            "kernel_arch": build.ARCH}
 
 
 if __name__ == "__main__":
