@@ -18,12 +18,15 @@
 // workgroup barrier between half-steps, so on every SIMD one wavefront's
 // matrix instructions run beside the other's vector instructions (the
 // other pairing, both wavefronts of a SIMD in the same phase, measured 22%
-// slower).  Per-phase timers in an instrumented build put the M phase at
-// about 1230 cycles of a tile (32 matrix instructions, 1024 cycles of matrix
-// work) and the V phase at about 1430, the SIMD's one vector issue port
-// being shared by the V phase's ~150 instructions and the M phase's matrix
-// issue; the clock under this load is about 1.5 GHz.  An earlier schedule
-// that interleaved both kinds of work inside each wavefront ran 1% slower.
+// slower).  What bounds it, measured by timing copies of the kernel with one
+// part removed: the M phase.  Each of its matrix instructions consumes a
+// 1 KB LDS operand read (a 16 KB K tile and a 16 KB V tile per wavefront
+// and tile), and a SIMD with one wavefront issuing such instructions keeps
+// its matrix core only ~75-84% busy; without the LDS reads the softmax-free
+// kernel takes a quarter less time, without the softmax only an eighth
+// less.  An earlier schedule that interleaved both kinds of work inside
+// each wavefront ran 1% slower; 64-row wavefronts, a role split of the two
+// wavefronts of a SIMD and early operand reads all ran 5-11% slower.
 // What the pipelining takes, learnt the hard way:
 //  * the matrix instructions are inline assembly with their registers
 //    fixed in VGPRs (scores, O and Q; the vector code reads O in place when
