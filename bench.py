@@ -280,6 +280,22 @@ class Share:
             src, dst = t["copy"][name]
             dst.copy_(src)
             return 1
+        if name == "copy2d_permute":
+            # the runtime's own 2-D copy with the SEQ2HEAD geometry: per source
+            # shard, rows of this rank's heads (strided reads) to contiguous rows
+            a, b = self.head_off[0], self.head_off[1]
+            for p, src in enumerate(d["q"]):
+                r0, r1 = self.seq_off[p], self.seq_off[p + 1]
+                _memcpy2d(qh["q"][:, r0:r1], src[:, :, a:b], r1 - r0)
+            return 1   # one transfer of the permute's bytes
+        if name == "copy2d_head2seq":
+            # and with the HEAD2SEQ geometry: each rank's head rows (contiguous
+            # reads) into their columns of this shard's token rows
+            S0 = self.seq_off[1]
+            for r, src in enumerate((o, d["o_other"])):
+                a, b = self.head_off[r], self.head_off[r + 1]
+                _memcpy2d(o_tok[:, :, a:b], src[:, :S0], S0)
+            return 1   # one transfer of the inverse gather's bytes
         if name == "head2seq_lse":
             uaa.uaa_seq2head_permute(uaa.UAA_HEAD2SEQ, 0, [lse.unsqueeze(-1), d["l_other"]], l_tok, self.seq_off,
                                      self.head_off)
@@ -290,7 +306,7 @@ class Share:
                     "head2seq_o_lse")
     # plain device copies of the HBM-bound launches' byte counts (read + write),
     # timed the same way: the reference those launches are measured against
-    copy_names = ("copy_permute", "copy_qkv", "copy_merge")
+    copy_names = ("copy_permute", "copy_qkv", "copy_merge", "copy2d_permute", "copy2d_head2seq")
 
     def attn_chunk(self, s, c, ws, acc=False, bufs=None):
         """Chunk c's attention into its partial buffers, or with acc into the
@@ -670,6 +686,32 @@ def backward_variant(share, cfg_id: int, steps: int, warmup: int) -> dict:
     return {"ms_per_step": round(ms, 4), "value": round(tf, 2), "unit": "TFLOP/s",
             "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_step": flops,
             "launches_per_step": 1 + len(chunks), "grad_dtype": "fp32"}
+
+
+_HIP = None
+
+
+def _memcpy2d(dst, src, rows):
+    """hipMemcpy2DAsync of `rows` rows (B = 1) from the strided view src to
+    the strided view dst on the current stream: each row is src.shape[2] x
+    src.shape[3] contiguous elements, the pitches are the views' row strides."""
+    global _HIP
+    import ctypes
+
+    import torch
+    if _HIP is None:
+        _HIP = ctypes.CDLL("libamdhip64.so")
+        _HIP.hipMemcpy2DAsync.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                          ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    assert src.shape[0] == 1 and dst.shape[0] == 1 and src.shape[2:] == dst.shape[2:]
+    es = src.element_size()
+    width = src.shape[2] * src.shape[3] * es
+    assert src.stride(3) == 1 and src.stride(2) == src.shape[3] and dst.stride(3) == 1 and dst.stride(2) == dst.shape[3]
+    r = _HIP.hipMemcpy2DAsync(ctypes.c_void_p(dst.data_ptr()), dst.stride(1) * es, ctypes.c_void_p(src.data_ptr()),
+                              src.stride(1) * es, width, rows, 3,   # hipMemcpyDeviceToDevice
+                              ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if r != 0:
+        raise RuntimeError("hipMemcpy2DAsync failed: %d" % r)
 
 
 def _copy_bufs(torch, sizes):
@@ -1280,6 +1322,11 @@ def measure(args, workload: str, steps: int, warmup: int, full: bool) -> dict:
         c = log[name]
         return {"copy_us": round(c, 2), "frac_of_copy": round(c / us, 4)}
 
+    def vs_copy2d(us, name):
+        # the same transfer, same geometry, by the runtime's 2-D copy
+        c = log[name]
+        return {"copy2d_us": round(c, 2), "frac_of_copy2d": round(c / us, 4)}
+
     kernels = {
         "lse_merge": {"us": round(merge_us, 2), "GB/s": round(merge_gbps, 1),
                       "hbm_frac": round(merge_gbps / PEAK_HBM_GBPS, 4), "bytes": share.merge_bytes(),
@@ -1301,13 +1348,13 @@ def measure(args, workload: str, steps: int, warmup: int, full: bool) -> dict:
         kernels.update({
             "seq2head_permute": {"us": round(perm_us, 2), "GB/s": round(perm_gbps, 1),
                                  "hbm_frac": round(perm_gbps / PEAK_HBM_GBPS, 4), "bytes": share.permute_bytes(),
-                                 **vs_copy(perm_us, "copy_permute")},
+                                 **vs_copy(perm_us, "copy_permute"), **vs_copy2d(perm_us, "copy2d_permute")},
             "seq2head_permute_qkv": {"us": round(qkv_us, 2), "GB/s": round(qkv_gbps, 1),
                                      "hbm_frac": round(qkv_gbps / PEAK_HBM_GBPS, 4),
                                      "bytes": 3 * share.permute_bytes(), **vs_copy(qkv_us, "copy_qkv")},
             "head2seq_permute": {"us": round(h2s_us, 2), "GB/s": round(h2s_gbps, 1),
                                  "hbm_frac": round(h2s_gbps / PEAK_HBM_GBPS, 4), "bytes": share.head2seq_bytes(),
-                                 **vs_copy(h2s_us, "copy_permute")},
+                                 **vs_copy(h2s_us, "copy_permute"), **vs_copy2d(h2s_us, "copy2d_head2seq")},
             "head2seq_permute_o_lse": {"us": round(log["head2seq_o_lse"], 2),
                                        "bytes": share.head2seq_bytes() + share.head2seq_lse_bytes()},
         })
