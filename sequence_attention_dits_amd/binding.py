@@ -384,7 +384,9 @@ def usp_attn_fwd_lse_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o
 
 def usp_lse_merge(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor],
                   o_out: torch.Tensor, lse_out: torch.Tensor) -> None:
-    """N-way LSE merge of partial (O, LSE) pairs into o_out, lse_out."""
+    """N-way LSE merge of partial (O, LSE) pairs into o_out, lse_out (see
+    usp_lse_merge in include/uaa.h): a part whose LSE is -inf for a row has
+    weight 0 there, and its O row is not read."""
     n = len(o_parts)
     if n != len(lse_parts) or n < 1:
         raise ValueError("need matching, non-empty part lists")
