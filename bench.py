@@ -69,7 +69,8 @@ WORKLOADS = {
     "qwen1328": (4, "Qwen-Image 1328x1328 Ring rank share: Q = 3493 of 6986 tokens, 24 heads, D=128, bf16, "
                     "K/V as 2 Ring chunks of 3493, LSE merge"),
     "longctx": (5, "long-context causal zigzag Ring share: S=32768 in 8 chunks of 4096, Q = chunks {1,6}, "
-                   "32 heads, D=128, bf16, K/V over all 8 chunks masked by global position, 8-way LSE merge"),
+                   "32 heads, D=128, bf16, K/V over all 8 chunks masked by global position, LSE merge of the "
+                   "chunks' results (Ring-step update on two streams, 2-way merge of the two running results)"),
 }
 RING_WORKLOADS = ("qwen1328", "longctx")
 # Workloads whose chunk launches run on two streams by default.  Measured:
@@ -79,11 +80,14 @@ RING_WORKLOADS = ("qwen1328", "longctx")
 OVERLAP_WORKLOADS = ("longctx",)
 # Workloads whose chunk partials are merged by the Ring-step update inside
 # the attention launches (usp_attn_fwd_lse_acc) rather than by one N-way
-# merge launch: the FLUX shares, where it saves the merge pass.  The Qwen
-# and long-context workloads are defined with a usp_lse_merge of their
-# partials (N = 2 and N = 8) and keep it (their steps measured within ~3 %
-# and ~1 % of the accumulating form).
-ACC_WORKLOADS = ("flux1024", "flux1008")
+# merge launch: the FLUX shares, where it saves the merge pass, and the
+# long-context share (two running results on two streams, merged at the end:
+# 1.5-2 % faster than its 8 partials and an 8-way merge on the same box,
+# since a partial is written for every query row while the update leaves a
+# chunk's rows without an allowed key untouched).  The Qwen share is defined
+# with a usp_lse_merge of its 2 partials and keeps it (within ~3 % of the
+# accumulating form).
+ACC_WORKLOADS = ("flux1024", "flux1008", "longctx")
 
 
 def make_share(workload: str, n_sets: int, overlap_chunks: str = "auto", ring_update: str = "auto"):

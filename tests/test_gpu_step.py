@@ -22,9 +22,11 @@ and compared with the oracle's composition of the same pass:
   against both K/V chunks, merged by one usp_lse_merge launch; every row.
 * long-context zigzag share (USP / yunchang summary, "How It Works": the
   zigzag layout): queries = chunks {1, 6} of 8, against all 8 K/V chunks
-  masked by global position on two streams, then the 8-way merge; 1024 rows
-  sampled across both query chunks (the first and last rows of every 256-row
-  unit boundary region included), since the oracle takes ~45 s for all 8192.
+  masked by global position on two streams, merged by the Ring-step update
+  (one running result per stream, then their 2-way merge) as the bench times
+  it, and as 8 partials with one 8-way merge; 1024 rows sampled across both
+  query chunks (the first and last rows of every 256-row unit included),
+  since the oracle takes ~45 s for all 8192.
 
 Tolerances: bf16 outputs, max-abs 2e-2 on O and 1e-3 on the LSE; rows the
 oracle leaves without a key must come back exactly (0, -inf).
@@ -123,10 +125,11 @@ def test_qwen_ring_step_every_row():
     say("step qwen1328 every row: O err %.3e, LSE err %.3e" % (err["o_err"], err["lse_err"]))
 
 
-def test_longctx_zigzag_step_sampled_rows():
-    say("step longctx build")
-    share = bench.make_share("longctx", 1)
-    assert share.overlap_chunks
+@pytest.mark.parametrize("ring_update", ["auto", "merge"])
+def test_longctx_zigzag_step_sampled_rows(ring_update):
+    say("step longctx build", ring_update)
+    share = bench.make_share("longctx", 1, ring_update=ring_update)
+    assert share.overlap_chunks and share.ring_acc == (ring_update == "auto")
     say("step longctx run")
     o, lse = _run_eager_and_graph(share)
     # the first and last row of every 256-row unit, the rest drawn at random
