@@ -641,8 +641,10 @@ def backward_variant(share, cfg_id: int, steps: int, warmup: int) -> dict:
     dO of the step's (O, LSE), delta = rowsum(dO * O) once, then
     usp_attn_bwd per Ring chunk against the final LSE -- the first chunk
     writes dQ, later chunks add into it, each chunk's dK, dV written fresh
-    (fp32 gradients).  Algorithmic FLOPs: 2.5x the forward's (the five
-    products S, dP, dV, dK, dQ over the allowed pairs)."""
+    (fp32 gradients) -- with the dS workspace where it applies (dQ formed
+    from the dS the dK/dV kernel stores), and for comparison without it
+    (dQ recomputing the scores).  Algorithmic FLOPs: 2.5x the forward's
+    (the five products S, dP, dV, dK, dQ over the allowed pairs)."""
     import numpy as np
 
     import synth
@@ -663,33 +665,44 @@ def backward_variant(share, cfg_id: int, steps: int, warmup: int) -> dict:
     dkv = [(torch.empty(k.shape, device="cuda", dtype=torch.float32),
             torch.empty(k.shape, device="cuda", dtype=torch.float32)) for k, _, _ in chunks]
 
-    def run():
+    # one dS workspace for the chunks (their calls run in stream order), the
+    # largest any of them uses
+    sizes = [uaa.attn_bwd_workspace_bytes(q, k, m) for k, _, m in chunks]
+    ws = torch.empty(max(sizes), dtype=torch.uint8, device="cuda") if max(sizes) > 0 else None
+
+    def run(use_ws):
         uaa.usp_attn_bwd_delta(share.o, dout, delta)
         for c, ((k, v, m), (dk, dv)) in enumerate(zip(chunks, dkv)):
             uaa.usp_attn_bwd(q, k, v, dout, share.lse, delta, dq, dk, dv, share.scale, m,
-                             accumulate="dq" if c else False)
+                             accumulate="dq" if c else False, workspace=ws if use_ws and sizes[c] else None)
 
-    for _ in range(max(warmup, 1)):
-        run()
-    torch.cuda.synchronize()
-    # untimed steps right before the timed ones: the GPU is at its working
-    # clock when timing starts (an idle GPU lowers it), and the host is
-    # ahead of the GPU by their run time
-    for _ in range(max(warmup, 1)):
-        run()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    def timed(use_ws):
+        for _ in range(max(warmup, 1)):
+            run(use_ws)
+        torch.cuda.synchronize()
+        # untimed steps right before the timed ones: the GPU is at its working
+        # clock when timing starts (an idle GPU lowers it), and the host is
+        # ahead of the GPU by their run time
+        for _ in range(max(warmup, 1)):
+            run(use_ws)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            run(use_ws)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_re = timed(False)
+    ms = timed(True) if ws is not None else ms_re
     flops = 2.5 * sum(share.attn_flops(c) for c in range(len(chunks)))
     tf = flops / (ms * 1e-3) / 1e12
     return {"ms_per_step": round(ms, 4), "value": round(tf, 2), "unit": "TFLOP/s",
             "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_step": flops,
-            "launches_per_step": 1 + len(chunks), "grad_dtype": "fp32"}
+            "launches_per_step": 1 + 2 * len(chunks), "grad_dtype": "fp32",
+            "dq_from_ds_chunks": sum(1 for n in sizes if n > 0), "ds_workspace_bytes": max(sizes),
+            "recompute_ms_per_step": round(ms_re, 4)}
 
 
 _HIP = None

@@ -460,6 +460,42 @@ int usp_attn_bwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_
                  float scale, const usp_mask* mask, int accumulate, void* stream);
 
 /*
+ * usp_attn_bwd_ws -- usp_attn_bwd with a caller-owned device workspace that
+ * holds dS for the dq kernel.  Without it, the dq kernel recomputes the
+ * scores and dP of every pair (the dk/dv kernel forms them too, so S and dP
+ * are computed twice: 14 D FLOP per pair against the 10 D of the five
+ * products above).  With it, for bf16 input, D = 128 and every pair
+ * allowed, the dk/dv kernel also writes dS_ij in bf16 (the value its dk
+ * product uses) to the workspace and the dq kernel forms dq_i = scale
+ * sum_j dS_ij k_j from it: 2 bytes of traffic each way per pair instead of
+ * 4 D FLOP.  The result equals usp_attn_bwd's up to rounding (dS is formed
+ * from P rounded to bf16, as in dk).
+ *
+ *   workspace  device, 16-byte aligned, at least
+ *              usp_attn_bwd_workspace_bytes(...) bytes, contents ignored
+ *              (both kernels of the call use it; calls that share a
+ *              workspace must not overlap).  NULL, fewer bytes than needed,
+ *              or a call the path does not cover: the plain call.
+ * Every other argument is that of usp_attn_bwd.
+ * Returns UAA_OK, UAA_ERR_INVALID_ARG, UAA_ERR_UNSUPPORTED or UAA_ERR_HIP.
+ */
+int usp_attn_bwd_ws(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                    const void* q, const void* k, const void* v, const void* dout,
+                    const float* lse, const float* delta, void* dq, void* dk, void* dv, int grad_dtype,
+                    float scale, const usp_mask* mask, int accumulate, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * usp_attn_bwd_workspace_bytes -- bytes of the workspace usp_attn_bwd_ws
+ * uses for these sizes and mask: B * H * ceil(Sq / 32) * ceil(Sk / 16) *
+ * 1024 (dS in bf16, in blocks of 32 queries x 16 keys), or 0 where the path does not
+ * apply (fp32 input, D != 128, a mask that excludes some pair, an empty
+ * call, or an invalid mask).  Host only; no device work.
+ */
+size_t usp_attn_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                    const usp_mask* mask);
+
+/*
  * uaa_last_error -- text describing the last non-zero status returned on
  * the calling thread ("" if none).  The pointer stays valid until the next
  * call on that thread.

@@ -143,6 +143,10 @@ def lib() -> ctypes.CDLL:
         l.usp_attn_bwd.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p,
                                    _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_int, ctypes.c_float,
                                    ctypes.POINTER(usp_mask), ctypes.c_int, _c_p]
+        l.usp_attn_bwd_ws.restype = ctypes.c_int
+        l.usp_attn_bwd_ws.argtypes = l.usp_attn_bwd.argtypes[:-1] + [_c_p, ctypes.c_size_t, _c_p]
+        l.usp_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        l.usp_attn_bwd_workspace_bytes.argtypes = l.usp_attn_workspace_bytes.argtypes
         l.usp_attn_kernel.restype = ctypes.c_int
         l.usp_attn_kernel.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int,
                                       ctypes.POINTER(usp_mask), ctypes.c_size_t]
@@ -473,13 +477,35 @@ def usp_attn_bwd_delta(o: torch.Tensor, dout: torch.Tensor, delta: torch.Tensor,
                                     delta.data_ptr(), _stream(o)))
 
 
+def attn_bwd_workspace_bytes(q: torch.Tensor, k: torch.Tensor, mask: Optional[usp_mask] = None) -> int:
+    """Bytes of the dS workspace usp_attn_bwd(..., workspace=) uses for this
+    problem (usp_attn_bwd_workspace_bytes; 0: the call does not use one)."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k are [B, S, H, D]")
+    B, Sq, H, D = q.shape
+    m = mask if mask is not None else mask_full()
+    return int(lib().usp_attn_bwd_workspace_bytes(_code(q.dtype, "q"), B, H, Sq, k.shape[1], D, ctypes.byref(m)))
+
+
+def attn_bwd_workspace(q: torch.Tensor, k: torch.Tensor, mask: Optional[usp_mask] = None) -> Optional[torch.Tensor]:
+    """A device workspace for usp_attn_bwd(..., workspace=) for this problem
+    on q's device (dS of every pair), or None when the call would not use
+    one."""
+    n = attn_bwd_workspace_bytes(q, k, mask)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
 def usp_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
                  delta: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, scale: float,
-                 mask: Optional[usp_mask] = None, accumulate=False) -> None:
+                 mask: Optional[usp_mask] = None, accumulate=False, workspace: Optional[torch.Tensor] = None) -> None:
     """Gradients of one attention call (one Ring key block) into caller-owned
     dq [B,Sq,H,D], dk, dv [B,Sk,H,D] (bf16 or float32), from the rows' final
     lse and delta (usp_attn_bwd_delta).  accumulate: False (write all), True
-    (add into all three), "dq" (add into dq only) or "dkdv" (into dk, dv)."""
+    (add into all three), "dq" (add into dq only) or "dkdv" (into dk, dv).
+    With a workspace from attn_bwd_workspace() the call is usp_attn_bwd_ws:
+    dq formed from the dS the dK/dV kernel stores there."""
     acc_code = {False: 0, True: 3, "dq": 1, "dkdv": 2}.get(accumulate)
     if acc_code is None:
         raise ValueError("accumulate must be False, True, 'dq' or 'dkdv'")
@@ -502,7 +528,12 @@ def usp_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.
     if dk.dtype != dq.dtype or dv.dtype != dq.dtype:
         raise ValueError("dq, dk, dv must share a dtype")
     m = mask if mask is not None else mask_full()
-    _check(lib().usp_attn_bwd(_code(q.dtype, "q"), B, H, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                              dout.data_ptr(), lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                              dv.data_ptr(), _code(dq.dtype, "dq"), float(scale), ctypes.byref(m),
-                              acc_code, _stream(q)))
+    args = (_code(q.dtype, "q"), B, H, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _code(dq.dtype, "dq"),
+            float(scale), ctypes.byref(m), acc_code)
+    if workspace is None:
+        _check(lib().usp_attn_bwd(*args, _stream(q)))
+        return
+    _dev(workspace, "workspace")
+    _check(lib().usp_attn_bwd_ws(*args, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                 _stream(q)))

@@ -597,10 +597,21 @@ UAA_EXPORT int usp_attn_bwd_delta(int dtype, int64_t B, int64_t S, int64_t H, in
     return hip_status(uaa::launch_bwd_delta(dtype, (int)D, a, static_cast<hipStream_t>(stream)), "bwd delta launch");
 }
 
-UAA_EXPORT int usp_attn_bwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, const void* q,
-                            const void* k, const void* v, const void* dout, const float* lse, const float* delta,
-                            void* dq, void* dk, void* dv, int grad_dtype, float scale, const usp_mask* mask,
-                            int accumulate, void* stream)
+// Bytes of the dS workspace of the backward for these sizes: dS^T in bf16,
+// 1 KB per 32 queries x 16 keys (0 where the path does not apply: fp32
+// inputs, D != 128, a mask that excludes some pair, or no pair at all).
+static size_t bwd_ds_bytes(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, bool masked)
+{
+    if (dtype != UAA_BF16 || D != 128 || masked || B <= 0 || H <= 0 || Sq <= 0 || Sk <= 0) return 0;
+    const double n = (double)B * H * ((Sq + 31) / 32) * ((Sk + 15) / 16) * 1024.0;
+    if (n >= 9.0e18) return 0;
+    return (size_t)B * (size_t)H * (size_t)((Sq + 31) / 32) * (size_t)((Sk + 15) / 16) * 1024u;
+}
+
+static int attn_bwd_impl(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, const void* q,
+                         const void* k, const void* v, const void* dout, const float* lse, const float* delta,
+                         void* dq, void* dk, void* dv, int grad_dtype, float scale, const usp_mask* mask,
+                         int accumulate, void* workspace, size_t workspace_bytes, void* stream)
 {
     if (dtype != UAA_BF16 && dtype != UAA_FP32)
         return fail(UAA_ERR_INVALID_ARG, "bwd: dtype must be UAA_BF16 or UAA_FP32, got %d", dtype);
@@ -655,9 +666,46 @@ UAA_EXPORT int usp_attn_bwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t
         if (rc != UAA_OK) return rc;
         if (all_pairs_allowed(a.qmap, Sq, a.kmap, Sk)) a.masked = 0;
     }
+    const size_t need = bwd_ds_bytes(dtype, B, H, Sq, Sk, D, a.masked != 0);
+    if (workspace != nullptr && need > 0 && workspace_bytes >= need) {
+        if (!aligned(workspace, 16)) return fail(UAA_ERR_INVALID_ARG, "bwd: workspace must be 16-byte aligned");
+        a.ds = workspace;
+        a.ds_nq = (Sq + 31) / 32;
+        a.ds_nk = (Sk + 15) / 16;
+    }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == UAA_BF16) return hip_status(uaa::launch_attn_bwd_bf16((int)D, a, s), "bwd launch");
     return hip_status(uaa::launch_attn_bwd_fp32((int)D, a, s), "bwd launch");
+}
+
+UAA_EXPORT int usp_attn_bwd(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, const void* q,
+                            const void* k, const void* v, const void* dout, const float* lse, const float* delta,
+                            void* dq, void* dk, void* dv, int grad_dtype, float scale, const usp_mask* mask,
+                            int accumulate, void* stream)
+{
+    return attn_bwd_impl(dtype, B, H, Sq, Sk, D, q, k, v, dout, lse, delta, dq, dk, dv, grad_dtype, scale, mask,
+                         accumulate, nullptr, 0, stream);
+}
+
+UAA_EXPORT size_t usp_attn_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                               const usp_mask* mask)
+{
+    bool masked = false;
+    if (mask != nullptr && mask->kind != USP_MASK_FULL) {
+        uaa::PosMap qm{}, km{};
+        if (side_map(*mask, true, Sq, qm) != UAA_OK || side_map(*mask, false, Sk, km) != UAA_OK) return 0;
+        masked = !all_pairs_allowed(qm, Sq, km, Sk);
+    }
+    return bwd_ds_bytes(dtype, B, H, Sq, Sk, D, masked);
+}
+
+UAA_EXPORT int usp_attn_bwd_ws(int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, const void* q,
+                               const void* k, const void* v, const void* dout, const float* lse, const float* delta,
+                               void* dq, void* dk, void* dv, int grad_dtype, float scale, const usp_mask* mask,
+                               int accumulate, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return attn_bwd_impl(dtype, B, H, Sq, Sk, D, q, k, v, dout, lse, delta, dq, dk, dv, grad_dtype, scale, mask,
+                         accumulate, workspace, workspace_bytes, stream);
 }
 
 // --------------------------------------------------------------------------

@@ -28,6 +28,10 @@
 //      S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
 //    S is recomputed here rather than exchanged: the two kernels share no
 //    memory but their inputs, and each writes its gradients once.
+//  * With a dS workspace (bf16 inputs, D = 128, every pair allowed) the
+//    dK/dV kernel also stores dS, as the dQ products' B operands, and the
+//    dQ kernel is replaced by one that streams them: dQ^T += K^T dS^T with
+//    no scores computed a second time (attn_bwd_dqs_kernel).
 //  * The transposed operands come from ds_read_b64_tr_b16 on the row-major
 //    tiles: within each group of 16 lanes, lane 16g + 4a + c receives the
 //    c-th 16-bit element at the addresses of lanes 16g + a + 4e, e = 0..3,
@@ -40,6 +44,8 @@
 //  * Masked keys are removed by global position exactly as in the forward:
 //    the allowed set of a row (keys) or of a key (queries) is a union of two
 //    index intervals, classified once per workgroup and wave.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace uaa {
@@ -53,6 +59,7 @@ typedef unsigned int bwd_u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int bwd_u32x2 __attribute__((ext_vector_type(2)));
 typedef short bwd_i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char bwd_lds_u8;
+typedef __attribute__((address_space(3))) bwd_u32x2 bwd_lds_u32x2;
 typedef __attribute__((address_space(3))) bwd_u32x4 bwd_lds_u32x4;
 typedef __attribute__((address_space(3))) bwd_i16x4 bwd_lds_i16x4;
 typedef __attribute__((address_space(3))) bwd_f32x4 bwd_lds_f32x4;
@@ -107,6 +114,35 @@ __device__ __forceinline__ void bwd_copy(const unsigned char* src, uint32_t nrec
     const int row = n * RPD + lane / UPR;
     const uint32_t off = (uint32_t)row * ld2 + (uint32_t)((((lane % UPR) ^ bwd_swz<D>(row))) << 4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + n * 1024, 16, off, 0, 0, 0);
+}
+
+// The same copy issued from inline assembly, for a kernel that runs one
+// workgroup per compute unit: the compiler does not count a load it cannot
+// see, so it places no vmcnt(0) in front of the LDS reads that follow (it
+// does for the builtin, and with no second workgroup to run meanwhile that
+// wait would expose each copy's latency); the kernel waits with explicit
+// vmcnt counts before the barrier that publishes a tile.  The descriptor
+// fields are uniform; readfirstlane keeps them in scalar registers.
+typedef unsigned int bwd_rsrc __attribute__((ext_vector_type(4)));
+template <int D>
+__device__ __forceinline__ void bwd_copy_asm(const unsigned char* src, uint32_t nrec, uint32_t ld2, bwd_lds_u8* dst,
+                                             int wave, int lane, int i)
+{
+    constexpr int UPR = D / 8, RPD = 1024 / (2 * D);
+    const int n = kBwdWaves * i + wave;
+    const int row = n * RPD + lane / UPR;
+    const uint32_t off = (uint32_t)row * ld2 + (uint32_t)((((lane % UPR) ^ bwd_swz<D>(row))) << 4);
+    const uint64_t p = (uint64_t)src;
+    const bwd_rsrc r{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xffffu)),
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)nrec), 0x00020000u};
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass has no SGPR operand constraint
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(off), "s"(r),
+                   "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(dst + n * 1024)))
+                 : "memory", "m0");
+#endif
 }
 
 // Transposed matrix operand from a row-major swizzled tile: this lane, as
@@ -439,6 +475,41 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void attn_bwd_dkdv_kernel(const 
                                          bwd_hi(x[c][e]) * r2[qb][8 * h + 2 * e + 1]);
                     *(bwd_lds_u32x4*)(L + OFF_S + dsb * XB + xslot(c)) = sw;
                 }
+                if constexpr (!MASKED) {
+                    if (a.ds != nullptr) {
+                        // dS^T into the workspace as B-operand blocks (16
+                        // keys x 32 queries, 1 KB each), read back from this
+                        // wave's slots with transposing reads: block (kk, qq)
+                        // holds keys 16 kk .. +15 of the group and queries
+                        // 32 qq .. +31 of the tile.  Slot (chunk c, lane
+                        // 32 hg + key) holds at byte 8 ep + 2 x the pair of
+                        // that key with tile row 32 qb + 16 h + 8 ep + 4 hg + x
+                        // (c = 2 qb + h); source lane (g, e, a) = (lane / 16,
+                        // lane / 4 % 4, lane % 4) addresses key 16 kk +
+                        // 4 (g / 2) + e at rows 32 qq + 16 (g % 2) + 8 (a / 2)
+                        // + 4 (a % 2) + {0..3}, so result lane 32 e' + n gets
+                        // keys 16 kk + 4 e' + {0..3} of query 32 qq + n, and
+                        // the same 8 keys on: keys + {8..11}.
+                        const int g = lane >> 4, se = (lane >> 2) & 3, sa = lane & 3;
+#pragma unroll
+                        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+                            for (int kk = 0; kk < 2; ++kk) {
+                                const int64_t qc = (i0 >> 5) + qq, kc = (kw0 >> 4) + kk;
+                                if (qc >= a.ds_nq || kc >= a.ds_nk) continue;
+                                const bwd_lds_u8* src = L + OFF_S + dsb * XB +
+                                                        ((kg * 4 + 2 * qq + (g & 1)) * 64 + (sa & 1) * 32 + 16 * kk +
+                                                         4 * (g >> 1) + se) * 16 + (sa >> 1) * 8;
+                                const bwd_i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bwd_lds_i16x4*)src);
+                                const bwd_i16x4 y =
+                                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((bwd_lds_i16x4*)(src + 8 * 16));
+                                *reinterpret_cast<bwd_u32x4*>(static_cast<unsigned char*>(a.ds) +
+                                                              (((b * H + hh) * a.ds_nq + qc) * a.ds_nk + kc) * 1024 +
+                                                              lane * 16) =
+                                    __builtin_bit_cast(bwd_u32x4, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+                            }
+                    }
+                }
             }
         }
 
@@ -740,6 +811,155 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void attn_bwd_dq_kernel(const Bw
 }
 
 // ==========================================================================
+// dQ from the dS workspace (D = 128, every key allowed)
+// ==========================================================================
+// dQ^T += K^T dS^T per 64-key tile with dS^T read back from the workspace
+// the dK/dV kernel filled, instead of recomputed: a workgroup owns 256 query
+// rows of one (batch, head), 32 per wave.  The workspace holds dS^T as the
+// matrix instructions' B operands, so each wave loads its own operands
+// straight into registers (one 1 KB load per 16 keys), kDqsPF tiles ahead;
+// the K tiles stream through kDqsStages LDS stages (one copy per wave per
+// 1 KB, kDqsStages - 1 tiles ahead) and are read transposed as the A
+// operands, three instructions ahead.  The work is the dS stream (2 bytes per pair)
+// and 2 D FLOP per pair.
+constexpr int kDqsStages = 6;
+constexpr int kDqsPF = 4;
+// s_waitcnt immediate waiting for vmcnt <= n only (vmcnt is split over
+// bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima)
+constexpr int bwd_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+__global__ __launch_bounds__(64 * kBwdWaves, 1) void attn_bwd_dqs_kernel(const BwdArgs a)
+{
+    constexpr int D = 128, ROWB = 2 * D, NDB = D / 32, TB = kBwdT * ROWB;
+    constexpr int CPT = TB / 1024 / kBwdWaves;       // K copy instructions per wave per tile
+    constexpr int NST = kDqsStages, PF = kDqsPF;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * TB];
+
+    const uint32_t unit = xcd_logical(blockIdx.x, gridDim.x);
+    const int64_t qt = unit % (uint32_t)a.n_tiles;
+    const int64_t rest = unit / (uint32_t)a.n_tiles;
+    const int64_t hh = rest % a.H, b = rest / a.H;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, hg = lane >> 5;
+    const int64_t H = a.H, Sq = a.Sq, Sk = a.Sk;
+    const uint32_t ld2 = (uint32_t)(H * D * 2);
+    const int64_t qc = qt * (kBwdRows / 32) + wave;               // this wave's 32-query block
+    const int64_t i = 32 * qc + (lane & 31);                      // this lane's query row
+    const int n_kt = (int)((Sk + kBwdT - 1) / kBwdT);
+
+    // K tile t into stage st (zeros past the last tile, so that every wave
+    // issues the same number of copies each step)
+    const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + ((b * Sk) * H + hh) * D * 2;
+    bwd_lds_u8* const L = (bwd_lds_u8*)smem;
+    auto issue_k = [&](int t, int st) {
+        const int64_t r0 = (int64_t)t * kBwdT;
+        const int64_t nv = t < n_kt ? (Sk - r0 < kBwdT ? Sk - r0 : kBwdT) : 0;
+        const unsigned char* src = t < n_kt ? kbase + r0 * ld2 : kbase;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c)
+            bwd_copy_asm<D>(src, nv > 0 ? (uint32_t)((nv - 1) * ld2 + ROWB) : 0u, ld2, L + st * TB, wave, lane, c);
+    };
+    // this wave's dS^T blocks (key groups 0 .. ds_nk - 1, 1 KB each, in
+    // order; reads from the end on, and for a wave past the last query
+    // block, return zero)
+    const bool live = qc < a.ds_nq;
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<unsigned char*>(a.ds) + (live ? (((b * H + hh) * a.ds_nq + qc) * a.ds_nk) * 1024 : 0), (short)0,
+        live ? (uint32_t)(a.ds_nk * 1024) : 0u, 0x00020000);
+    auto load_s = [&](int t, bwd_bf16x8 (&sd)[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            sd[q] = __builtin_bit_cast(bwd_bf16x8,
+                                       __builtin_amdgcn_raw_buffer_load_b128(sr, (uint32_t)((4 * t + q) * 1024 + lane * 16),
+                                                                             0, 0));
+    };
+    const BwdTr trs = bwd_tr_setup<D>(lane);
+
+    bwd_f32x16 acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
+
+    // prologue: K tiles 0 .. NST - 2, then the dS of tiles 0 .. PF - 1
+    for (int t = 0; t < NST - 1; ++t) issue_k(t, t);
+    bwd_bf16x8 sd[PF][4];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) load_s(p, sd[p]);
+    asm volatile("" ::: "memory");   // the loads above stay above the wait
+    __builtin_amdgcn_s_waitcnt(bwd_vmcnt(CPT * (NST - 2) + 4 * PF));   // K tile 0 has landed
+    __syncthreads();
+
+    // Step t: the products of tile t, the dS of tile t + PF into the
+    // registers tile t used, the copies of K tile t + NST - 1 into the stage
+    // tile t - 1 used.  Before the barrier that ends step t, K tile t + 1
+    // must have landed: it was issued last in step t + 2 - NST (or in the
+    // prologue), and every step issues 4 loads and CPT copies, so at most
+    // (4 + CPT) (NST - 2) loads after it may still run.  The steps run in
+    // groups of PF with no exit in between (past the last tile, K and dS
+    // read as zero and add nothing), so the compiler's own waits for the dS
+    // registers see the PF - 1 steps of loads issued since; it does not see
+    // the copies, which only makes those waits stricter.
+    auto step = [&](auto slot_tag, int t) {
+        constexpr int s = decltype(slot_tag)::value;
+        const bwd_lds_u8* Kl = L + (t % NST) * TB;
+        auto tr = [&](int r) { return bwd_tr<D>(Kl, 16 * (r / NDB) * ROWB, trs, r % NDB); };
+        bwd_bf16x8 ka[4];
+        ka[0] = tr(0);
+        ka[1] = tr(1);
+        ka[2] = tr(2);
+#pragma unroll
+        for (int r = 0; r < 4 * NDB; ++r) {
+            if (r + 3 < 4 * NDB) ka[(r + 3) & 3] = tr(r + 3);
+            acc[r % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[r & 3], sd[s][r / NDB], acc[r % NDB], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        load_s(t + PF, sd[s]);
+        issue_k(t + NST - 1, (t + NST - 1) % NST);
+        asm volatile("" ::: "memory");   // the count below includes these loads
+        __builtin_amdgcn_s_waitcnt(bwd_vmcnt((4 + CPT) * (NST - 2)));
+        bwd_barrier();
+    };
+    static_assert(PF == 4, "the step groups below are written out for PF = 4");
+    for (int t0 = 0; t0 < n_kt; t0 += PF) {
+        step(std::integral_constant<int, 0>{}, t0);
+        step(std::integral_constant<int, 1>{}, t0 + 1);
+        step(std::integral_constant<int, 2>{}, t0 + 2);
+        step(std::integral_constant<int, 3>{}, t0 + 3);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+
+    if (i >= Sq) return;
+    const int64_t orow = ((b * Sq + i) * H + hh) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int f = 32 * db + 8 * g4 + 4 * hg;
+            float r[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = acc[db][4 * g4 + e] * a.scale;
+            if (a.grad_bf16) {
+                bwd_u32x2* p = reinterpret_cast<bwd_u32x2*>(static_cast<unsigned short*>(a.dq) + orow + f);
+                if (a.accumulate & 1) {
+                    const bwd_u32x2 old = *p;
+                    r[0] += bwd_lo(old[0]);
+                    r[1] += bwd_hi(old[0]);
+                    r[2] += bwd_lo(old[1]);
+                    r[3] += bwd_hi(old[1]);
+                }
+                *p = bwd_u32x2{bwd_pack(r[0], r[1]), bwd_pack(r[2], r[3])};
+            } else {
+                bwd_f32x4* p = reinterpret_cast<bwd_f32x4*>(static_cast<float*>(a.dq) + orow + f);
+                bwd_f32x4 w{r[0], r[1], r[2], r[3]};
+                if (a.accumulate & 1) w += *p;
+                *p = w;
+            }
+        }
+}
+
+// ==========================================================================
 // delta = rowsum(dout * o) - dlse
 // ==========================================================================
 // LPR lanes per row, each with 16 bytes of o and dout; rows strided over the grid.
@@ -787,6 +1007,11 @@ static hipError_t launch_bwd_d(const BwdArgs& a0, hipStream_t s)
     if (a0.Sq == 0) return hipSuccess;
     BwdArgs a = a0;
     a.n_tiles = (int32_t)((a.Sq + kBwdRows - 1) / kBwdRows);
+    if constexpr (D == 128 && !M) {
+        if (a.ds != nullptr)
+            return launch_kernel(attn_bwd_dqs_kernel, dim3((uint32_t)(a.B * a.H * a.n_tiles)), dim3(64 * kBwdWaves), 0,
+                                 s, a);
+    }
     return launch_kernel(attn_bwd_dq_kernel<D, M>, dim3((uint32_t)(a.B * a.H * a.n_tiles)), dim3(64 * kBwdWaves), 0,
                          s, a);
 }

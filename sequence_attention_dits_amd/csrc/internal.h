@@ -181,6 +181,16 @@ struct BwdArgs {
     int32_t grad_bf16;    // gradients stored as bf16 (else fp32)
     int32_t n_tiles;      // work tiles per (batch, head) of the launched kernel, set by the launcher
     PosMap qmap, kmap;
+    // dS workspace (null: none): dS^T of every (key, query) pair in bf16 as
+    // matrix-core B operands.  Block (b, h, query block qc of 32, key group
+    // kc of 16) is 1 KB at (((b * H + h) * ds_nq + qc) * ds_nk + kc) * 1024;
+    // its lane L = 32 e + n holds, as 8 bf16, the pairs of query 32 qc + n
+    // with keys 16 kc + 4 e + {0, 1, 2, 3, 8, 9, 10, 11}.  The dK/dV kernel
+    // writes it; the dQ kernel then forms dQ = scale dS K from it instead of
+    // recomputing the scores.
+    void* ds;
+    int64_t ds_nq;        // ceil(Sq / 32)
+    int64_t ds_nk;        // ceil(Sk / 16)
 };
 
 struct DeltaArgs {

@@ -15,7 +15,10 @@ from the bf16 forward.  Cases:
   backward per block (dq accumulated, dk / dv per block) equals the
   gradient of attention over all keys;
 * edge cases: no keys (dq = 0), no queries (dk = dv = 0), accumulation;
-* the FLUX Ring-block shape at full size on sampled heads.
+* the FLUX Ring-block shape at full size on sampled heads;
+* usp_attn_bwd_ws (dq from the dS the dK/dV kernel stores): the cases it
+  covers against the oracle with the workspace pre-filled with NaN bits,
+  dK / dV unchanged by it, the calls it does not cover, accumulation.
 """
 
 import math
@@ -97,8 +100,18 @@ def _masks(kind, Sq, Sk, **kw):
     raise ValueError(kind)
 
 
-def _run_hip(bits, shapes, scale, mask, grad_dtype, dlse=None):
-    """HIP forward (o bf16, lse), delta, backward; returns host float64 grads."""
+def _nan_workspace(q, k, mask):
+    """The dS workspace of this problem filled with NaN bits (every value the
+    dq kernel reads must have been written by the dK/dV kernel), or None."""
+    ws = uaa.attn_bwd_workspace(q, k, mask)
+    if ws is not None:
+        ws.fill_(255)
+    return ws
+
+
+def _run_hip(bits, shapes, scale, mask, grad_dtype, dlse=None, ws=False):
+    """HIP forward (o bf16, lse), delta, backward; returns host float64 grads.
+    ws: through usp_attn_bwd_ws (the workspace must apply)."""
     qb, kb, vb, ob = bits
     B, Sq, Sk, H, D = shapes
     q, k, v, do = dev(qb, "bf16"), dev(kb, "bf16"), dev(vb, "bf16"), dev(ob, "bf16")
@@ -111,7 +124,11 @@ def _run_hip(bits, shapes, scale, mask, grad_dtype, dlse=None):
     dq = torch.full((B, Sq, H, D), float("nan"), device="cuda", dtype=grad_dtype)
     dk = torch.full((B, Sk, H, D), float("nan"), device="cuda", dtype=grad_dtype)
     dv = torch.full((B, Sk, H, D), float("nan"), device="cuda", dtype=grad_dtype)
-    uaa.usp_attn_bwd(q, k, v, do, lse, delta, dq, dk, dv, scale, mask)
+    workspace = None
+    if ws:
+        workspace = _nan_workspace(q, k, mask)
+        assert workspace is not None, "the dS workspace should apply to this call"
+    uaa.usp_attn_bwd(q, k, v, do, lse, delta, dq, dk, dv, scale, mask, workspace=workspace)
     torch.cuda.synchronize()
     return host_f64(dq), host_f64(dk), host_f64(dv)
 
@@ -153,6 +170,76 @@ def test_small_against_oracle(case, grad):
         dead = ~(kpos[None, :] <= qpos[:, None]).any(axis=1)
         if dead.any():
             assert (got[0][:, dead] == 0).all(), "rows without keys must get dq = 0"
+
+
+WS = [
+    # (name, B, Sq, Sk, H, D, mask kind, mask kwargs): calls the dS workspace
+    # covers (bf16, D = 128, every pair allowed)
+    ("ragged", 1, 257, 129, 2, 128, "full", {}),
+    ("three_panels_two_batches", 2, 300, 200, 2, 128, "full", {}),
+    ("one_query", 1, 1, 200, 1, 128, "full", {}),
+    ("one_key", 1, 70, 1, 2, 128, "full", {}),
+    ("long_keys", 1, 65, 700, 1, 128, "full", {}),
+    ("whole_tiles", 1, 512, 256, 3, 128, "full", {}),
+    ("causal_all_allowed", 1, 160, 90, 2, 128, "causal", dict(q_off=100, k_off=0)),
+]
+
+
+@pytest.mark.parametrize("case", WS, ids=[c[0] for c in WS])
+@pytest.mark.parametrize("grad", ["fp32", "bf16"])
+def test_ds_workspace_against_oracle(case, grad):
+    """usp_attn_bwd_ws: dQ formed from the dS the dK/dV kernel stores (the
+    workspace starts as NaN bits, so a value read but never written shows),
+    against the oracle at the same bound."""
+    name, B, Sq, Sk, H, D, kind, kw = case
+    say("backward dS workspace %s grads=%s B=%d Sq=%d Sk=%d H=%d" % (name, grad, B, Sq, Sk, H))
+    bits, vals, _ = _inputs(780 + WS.index(case), B, Sq, Sk, H, D)
+    q, k, v, do = vals
+    scale = 1.0 / math.sqrt(D)
+    mask, qpos, kpos = _masks(kind, Sq, Sk, **kw)
+    gdt = torch.float32 if grad == "fp32" else torch.bfloat16
+    got = _run_hip(bits, (B, Sq, Sk, H, D), scale, mask, gdt, ws=True)
+    ref = oracle.attention_bwd(q, k, v, do, scale, qpos, kpos)
+    bnd = _bounds(q, k, v, do, scale, qpos, kpos, None)
+    extra = 2.0 ** -8 if grad == "bf16" else 0.0
+    for nm, g, r, bd in zip(("dq", "dk", "dv"), got, ref, bnd):
+        _check(nm, g, r, bd + extra / REL * np.abs(r))
+
+
+def test_ds_workspace_scope_and_accumulate():
+    """The workspace changes only dq (dK, dV bit for bit as without it); it
+    is not used where it does not apply (D = 64, a mask that excludes a pair:
+    size 0) or when too small (the plain call, bit for bit); dq accumulation
+    through it adds exactly."""
+    B, Sq, Sk, H, D = 1, 200, 150, 2, 128
+    say("backward dS workspace scope / accumulate")
+    bits, _, _ = _inputs(790, B, Sq, Sk, H, D)
+    qb, kb, vb, ob = bits
+    q, k, v, do = dev(qb, "bf16"), dev(kb, "bf16"), dev(vb, "bf16"), dev(ob, "bf16")
+    scale = 1.0 / math.sqrt(D)
+    o = torch.empty((B, Sq, H, D), device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty((B, Sq, H), device="cuda", dtype=torch.float32)
+    uaa.usp_attn_fwd_lse(q, k, v, o, lse, scale)
+    delta = torch.empty_like(lse)
+    uaa.usp_attn_bwd_delta(o, do, delta)
+    grads = lambda: [torch.empty((B, S, H, D), device="cuda", dtype=torch.float32) for S in (Sq, Sk, Sk)]
+    g0, g1, g2, g3 = grads(), grads(), grads(), grads()
+    ws = _nan_workspace(q, k, None)
+    assert ws is not None and ws.numel() == B * H * ((Sq + 31) // 32) * ((Sk + 15) // 16) * 1024
+    uaa.usp_attn_bwd(q, k, v, do, lse, delta, *g0, scale)
+    uaa.usp_attn_bwd(q, k, v, do, lse, delta, *g1, scale, workspace=ws)
+    uaa.usp_attn_bwd(q, k, v, do, lse, delta, *g2, scale, workspace=ws[:-1])   # too small: plain call
+    g3 = [torch.full_like(x, 0.5) for x in g1]
+    uaa.usp_attn_bwd(q, k, v, do, lse, delta, *g3, scale, accumulate="dq", workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(g0[1], g1[1]) and torch.equal(g0[2], g1[2])
+    assert not torch.equal(g0[0], g1[0])   # dq from the stored dS (P rounded to bf16 first)
+    assert all(torch.equal(a, b) for a, b in zip(g0, g2))
+    assert torch.equal(g1[0] + 0.5, g3[0]) and torch.equal(g1[1], g3[1]) and torch.equal(g1[2], g3[2])
+    q64 = torch.zeros((B, Sq, H, 64), device="cuda", dtype=torch.bfloat16)
+    assert uaa.attn_bwd_workspace(q64, q64[:, :Sk]) is None
+    assert uaa.attn_bwd_workspace(q, k, uaa.mask_causal(0, 0)) is None
+    assert uaa.attn_bwd_workspace(q.float(), k.float()) is None
 
 
 def test_lse_gradient():
@@ -284,16 +371,18 @@ def test_delta_matches_definition():
     assert (np.abs(host_f64(delta) - ref) <= bound + 1e-6).all()
 
 
-def test_flux_block_full_size_sampled_heads():
+@pytest.mark.parametrize("ws", [False, True], ids=["recompute", "ds_workspace"])
+def test_flux_block_full_size_sampled_heads(ws):
     """The FLUX Ring-block shape (Sq = 4608 queries of 12 heads against a
-    2304-key block, D = 128), in the launch the bench times; heads 0 and 11
+    2304-key block, D = 128), in both launches the bench may time (dq
+    recomputing the scores, or from the dS workspace); heads 0 and 11
     checked against the oracle element by element."""
     B, Sq, Sk, H, D = 1, 4608, 2304, 12, 128
-    say("backward FLUX block full size")
+    say("backward FLUX block full size", "ds workspace" if ws else "recompute")
     bits, vals, _ = _inputs(770, B, Sq, Sk, H, D, rms=True)
     q, k, v, do = vals
     scale = 1.0 / math.sqrt(D)
-    got = _run_hip(bits, (B, Sq, Sk, H, D), scale, uaa.mask_full(), torch.float32)
+    got = _run_hip(bits, (B, Sq, Sk, H, D), scale, uaa.mask_full(), torch.float32, ws=ws)
     for h in (0, 11):
         sl = slice(h, h + 1)
         ref = oracle.attention_bwd(q[:, :, sl], k[:, :, sl], v[:, :, sl], do[:, :, sl], scale)
