@@ -18,7 +18,8 @@ from the bf16 forward.  Cases:
 * the FLUX Ring-block shape at full size on sampled heads;
 * usp_attn_bwd_ws (dq from the dS the dK/dV kernel stores): the cases it
   covers against the oracle with the workspace pre-filled with NaN bits,
-  dK / dV unchanged by it, the calls it does not cover, accumulation.
+  dK / dV unchanged by it, the calls it does not cover, accumulation, and
+  graph replays against the eager call.
 """
 
 import math
@@ -240,6 +241,50 @@ def test_ds_workspace_scope_and_accumulate():
     assert uaa.attn_bwd_workspace(q64, q64[:, :Sk]) is None
     assert uaa.attn_bwd_workspace(q, k, uaa.mask_causal(0, 0)) is None
     assert uaa.attn_bwd_workspace(q.float(), k.float()) is None
+
+
+def test_ds_workspace_graph_replays():
+    """usp_attn_bwd_ws captured in a HIP graph (delta, then the dK/dV and dQ
+    kernels sharing the workspace): every replay, with eager work and
+    synchronisation between replays, equals the eager call bit for bit."""
+    B, Sq, Sk, H, D = 1, 300, 260, 2, 128
+    say("backward dS workspace graph replays")
+    bits, _, _ = _inputs(795, B, Sq, Sk, H, D)
+    qb, kb, vb, ob = bits
+    q, k, v, do = dev(qb, "bf16"), dev(kb, "bf16"), dev(vb, "bf16"), dev(ob, "bf16")
+    scale = 1.0 / math.sqrt(D)
+    o = torch.empty((B, Sq, H, D), device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty((B, Sq, H), device="cuda", dtype=torch.float32)
+    uaa.usp_attn_fwd_lse(q, k, v, o, lse, scale)
+    delta = torch.empty_like(lse)
+    ws = _nan_workspace(q, k, None)
+    grads = [torch.empty((B, S, H, D), device="cuda", dtype=torch.bfloat16) for S in (Sq, Sk, Sk)]
+
+    def run():
+        uaa.usp_attn_bwd_delta(o, do, delta)
+        uaa.usp_attn_bwd(q, k, v, do, lse, delta, *grads, scale, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    ref = [g.clone() for g in grads]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()   # warm the side stream before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        for g in grads:
+            g.fill_(float("nan"))
+        ws.fill_(255)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for g, r in zip(grads, ref):
+            assert torch.equal(g.view(torch.int16), r.view(torch.int16)), "replay %d differs" % rep
 
 
 def test_lse_gradient():
