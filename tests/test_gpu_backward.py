@@ -15,7 +15,8 @@ from the bf16 forward.  Cases:
   backward per block (dq accumulated, dk / dv per block) equals the
   gradient of attention over all keys;
 * edge cases: no keys (dq = 0), no queries (dk = dv = 0), accumulation;
-* the FLUX Ring-block shape at full size on sampled heads;
+* the FLUX Ring-block shape at full size on sampled heads, and a
+  long-context zigzag block on a diagonal at full size;
 * usp_attn_bwd_ws (dq from the dS the dK/dV kernel stores): the cases it
   covers against the oracle with the workspace pre-filled with NaN bits,
   dK / dV unchanged by it, the calls it does not cover, accumulation, and
@@ -434,6 +435,26 @@ def test_flux_block_full_size_sampled_heads(ws):
         bnd = _bounds(q[:, :, sl], k[:, :, sl], v[:, :, sl], do[:, :, sl], scale, None, None, None)
         for nm, g, r, bd in zip(("dq", "dk", "dv"), got, ref, bnd):
             _check("%s head %d" % (nm, h), g[:, :, sl], r, bd)
+
+
+def test_longctx_diagonal_block_full_size_sampled_head():
+    """A long-context zigzag Ring block at full size: queries = chunks {1, 6}
+    of 4096 tokens, keys = chunk 1 (the first query chunk's rows see a causal
+    diagonal, the second's every key), 4 heads, D = 128; head 2 checked
+    against the oracle element by element."""
+    chunk = 4096
+    B, Sq, Sk, H, D = 1, 2 * chunk, chunk, 4, 128
+    say("backward long-context diagonal block full size")
+    bits, vals, _ = _inputs(775, B, Sq, Sk, H, D)
+    q, k, v, do = vals
+    scale = 1.0 / math.sqrt(D)
+    mask, qpos, kpos = _masks("zigzag", Sq, Sk, chunk=chunk, q_chunks=[1, 6], k_chunks=[1])
+    got = _run_hip(bits, (B, Sq, Sk, H, D), scale, mask, torch.float32)
+    sl = slice(2, 3)
+    ref = oracle.attention_bwd(q[:, :, sl], k[:, :, sl], v[:, :, sl], do[:, :, sl], scale, qpos, kpos)
+    bnd = _bounds(q[:, :, sl], k[:, :, sl], v[:, :, sl], do[:, :, sl], scale, qpos, kpos, None)
+    for nm, g, r, bd in zip(("dq", "dk", "dv"), got, ref, bnd):
+        _check("%s head 2" % nm, g[:, :, sl], r, bd)
 
 
 FP32 = [
