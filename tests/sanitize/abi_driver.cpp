@@ -158,6 +158,24 @@ static void merges_and_backward()
     rejected(usp_attn_bwd(UAA_BF16, 1, 2, 300, 250, 128, dptr(1), dptr(2), dptr(3), dptr(4),
                           static_cast<const float*>(dptr(5)), static_cast<const float*>(dptr(6)), dptr(7), dptr(8),
                           dptr(9), UAA_FP32, 0.1f, m, 4, nullptr), UAA_ERR_INVALID_ARG, "bwd accumulate");
+    // the dS workspace: sizes where it applies and 0 where it does not; a
+    // workspace call (the plain one without it), and a misaligned one
+    {
+        const size_t n = usp_attn_bwd_workspace_bytes(UAA_BF16, 1, 2, 300, 250, 128, nullptr);
+        expect(n == (size_t)2 * 10 * 16 * 1024, "bwd ws bytes", (int)(n / 1024));
+        expect(usp_attn_bwd_workspace_bytes(UAA_BF16, 1, 2, 300, 250, 128, m) == 0, "bwd ws masked", 0);
+        expect(usp_attn_bwd_workspace_bytes(UAA_FP32, 1, 2, 300, 250, 128, nullptr) == 0, "bwd ws fp32", 0);
+        expect(usp_attn_bwd_workspace_bytes(UAA_BF16, 1, 2, 300, 250, 64, nullptr) == 0, "bwd ws d64", 0);
+        accepted(usp_attn_bwd_ws(UAA_BF16, 1, 2, 300, 250, 128, dptr(1), dptr(2), dptr(3), dptr(4),
+                                 static_cast<const float*>(dptr(5)), static_cast<const float*>(dptr(6)), dptr(7),
+                                 dptr(8), dptr(9), UAA_FP32, 0.1f, nullptr, 1, dptr(10), n, nullptr),
+                 "bwd ws");
+        rejected(usp_attn_bwd_ws(UAA_BF16, 1, 2, 300, 250, 128, dptr(1), dptr(2), dptr(3), dptr(4),
+                                 static_cast<const float*>(dptr(5)), static_cast<const float*>(dptr(6)), dptr(7),
+                                 dptr(8), dptr(9), UAA_FP32, 0.1f, nullptr, 1,
+                                 static_cast<unsigned char*>(dptr(10)) + 4, n, nullptr),
+                 UAA_ERR_INVALID_ARG, "bwd ws misaligned");
+    }
     free(m);
     int64_t* off = static_cast<int64_t*>(malloc(sizeof(int64_t) * 8));
     accepted(uaa_split_offsets(4481, 7, off), "split");
