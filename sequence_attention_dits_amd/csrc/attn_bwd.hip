@@ -820,8 +820,8 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void attn_bwd_dq_kernel(const Bw
 // straight into registers (one 1 KB load per 16 keys), kDqsPF tiles ahead;
 // the K tiles stream through kDqsStages LDS stages (one copy per wave per
 // 1 KB, kDqsStages - 1 tiles ahead) and are read transposed as the A
-// operands, three instructions ahead.  The work is the dS stream (2 bytes per pair)
-// and 2 D FLOP per pair.
+// operands, three instructions ahead.  The work is the dS stream (2 bytes
+// per pair) and 2 D FLOP per pair.
 constexpr int kDqsStages = 6;
 constexpr int kDqsPF = 4;
 // s_waitcnt immediate waiting for vmcnt <= n only (vmcnt is split over
@@ -832,6 +832,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void attn_bwd_dqs_kernel(const B
     constexpr int D = 128, ROWB = 2 * D, NDB = D / 32, TB = kBwdT * ROWB;
     constexpr int CPT = TB / 1024 / kBwdWaves;       // K copy instructions per wave per tile
     constexpr int NST = kDqsStages, PF = kDqsPF;
+    static_assert(CPT * (NST - 2) + 4 * PF <= 63 && (4 + CPT) * (NST - 2) <= 63, "vmcnt counts up to 63");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * TB];
 
     const uint32_t unit = xcd_logical(blockIdx.x, gridDim.x);
