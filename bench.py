@@ -120,10 +120,11 @@ def parse():
                    help="with the default workload, skip the other three workloads' figures")
     p.add_argument("--no-backward", action="store_true", help="skip the backward variant")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    p.add_argument("--pmc-probe", nargs="?", const="attn", choices=["attn", "hbm"],
+    p.add_argument("--pmc-probe", nargs="?", const="attn", choices=["attn", "hbm", "bwd"],
                    help="only enqueue the dispatches that the counters are read on: a plain device copy of known "
                         "size, then --steps attention launch pairs (attn), or --steps rounds of the HBM-bound "
-                        "launches and of plain copies of the same sizes, every one on cold buffers (hbm)")
+                        "launches and of plain copies of the same sizes, every one on cold buffers (hbm), or "
+                        "--steps backward passes of the step's attention with the dS workspace (bwd)")
     p.add_argument("--hbm-summary", nargs="+", metavar="DIR",
                    help="print the HBM-bound kernels' counter summary from rocprofv3 runs of --pmc-probe hbm: "
                         "--pmc runs (FETCH_SIZE, WRITE_SIZE, ...) and one --kernel-trace --stats run")
@@ -136,6 +137,8 @@ def parse():
     p.add_argument("--counter-summary", nargs="+", metavar="DIR",
                    help="print the attention kernel's shader counters from rocprofv3 --pmc runs of --pmc-probe "
                         "(MFMA busy cycles against the active cycles, instruction mix, waits)")
+    p.add_argument("--counter-kernels", choices=["attn", "bwd"], default="attn",
+                   help="with --counter-summary: the forward attention kernel (attn) or each backward kernel (bwd)")
     return p.parse_args()
 
 
@@ -636,15 +639,14 @@ def _parity(o_gpu, l_gpu, o_ref, l_ref, n_rows):
             "parity_ok": bool(same_empty and o_err <= 2e-2 and l_err <= 1e-3)}
 
 
-def backward_variant(share, cfg_id: int, steps: int, warmup: int) -> dict:
-    """The backward of one step's attention: for a seeded output gradient
-    dO of the step's (O, LSE), delta = rowsum(dO * O) once, then
-    usp_attn_bwd per Ring chunk against the final LSE -- the first chunk
-    writes dQ, later chunks add into it, each chunk's dK, dV written fresh
-    (fp32 gradients) -- with the dS workspace where it applies (dQ formed
-    from the dS the dK/dV kernel stores), and for comparison without it
-    (dQ recomputing the scores).  Algorithmic FLOPs: 2.5x the forward's
-    (the five products S, dP, dV, dK, dQ over the allowed pairs)."""
+def _backward_setup(share, cfg_id: int):
+    """The backward of one step's attention, ready to enqueue: a seeded output
+    gradient dO of the step's (O, LSE), delta, dQ and per-chunk dK, dV
+    buffers (fp32), one dS workspace for the chunks (their calls run in
+    stream order), the largest any of them uses; returns (run, sizes, chunks)
+    with run(use_ws) enqueueing delta and usp_attn_bwd per Ring chunk -- the
+    first chunk writes dQ, later chunks add into it -- with the workspace
+    where use_ws and it applies."""
     import numpy as np
 
     import synth
@@ -664,9 +666,6 @@ def backward_variant(share, cfg_id: int, steps: int, warmup: int) -> dict:
     dq = torch.empty(B, Sq, H, D, device="cuda", dtype=torch.float32)
     dkv = [(torch.empty(k.shape, device="cuda", dtype=torch.float32),
             torch.empty(k.shape, device="cuda", dtype=torch.float32)) for k, _, _ in chunks]
-
-    # one dS workspace for the chunks (their calls run in stream order), the
-    # largest any of them uses
     sizes = [uaa.attn_bwd_workspace_bytes(q, k, m) for k, _, m in chunks]
     ws = torch.empty(max(sizes), dtype=torch.uint8, device="cuda") if max(sizes) > 0 else None
 
@@ -675,6 +674,19 @@ def backward_variant(share, cfg_id: int, steps: int, warmup: int) -> dict:
         for c, ((k, v, m), (dk, dv)) in enumerate(zip(chunks, dkv)):
             uaa.usp_attn_bwd(q, k, v, dout, share.lse, delta, dq, dk, dv, share.scale, m,
                              accumulate="dq" if c else False, workspace=ws if use_ws and sizes[c] else None)
+
+    return run, sizes, chunks
+
+
+def backward_variant(share, cfg_id: int, steps: int, warmup: int) -> dict:
+    """The backward of one step's attention (_backward_setup), with the dS
+    workspace where it applies (dQ formed from the dS the dK/dV kernel
+    stores), and for comparison without it (dQ recomputing the scores).
+    Algorithmic FLOPs: 2.5x the forward's (the five products S, dP, dV, dK,
+    dQ over the allowed pairs)."""
+    torch = share.torch
+    run, sizes, chunks = _backward_setup(share, cfg_id)
+    ws = max(sizes) > 0
 
     def timed(use_ws):
         for _ in range(max(warmup, 1)):
@@ -695,7 +707,7 @@ def backward_variant(share, cfg_id: int, steps: int, warmup: int) -> dict:
         return e0.elapsed_time(e1) / steps
 
     ms_re = timed(False)
-    ms = timed(True) if ws is not None else ms_re
+    ms = timed(True) if ws else ms_re
     flops = 2.5 * sum(share.attn_flops(c) for c in range(len(chunks)))
     tf = flops / (ms * 1e-3) / 1e12
     return {"ms_per_step": round(ms, 4), "value": round(tf, 2), "unit": "TFLOP/s",
@@ -852,6 +864,12 @@ def pmc_probe(args):
     dst = torch.empty_like(src)
     if args.pmc_probe == "hbm":
         hbm_probe(args, cfg_id, src, dst)
+        return
+    if args.pmc_probe == "bwd":
+        run, _, _ = _backward_setup(Share(cfg_id, 1), cfg_id)
+        for _ in range(args.steps):
+            run(True)
+        torch.cuda.synchronize()
         return
     for _ in range(3):
         dst.copy_(src)
@@ -1077,34 +1095,43 @@ def measured_traffic():
 SIMDS = 256 * 4   # MI355X: 256 compute units of 4 SIMDs, in 8 XCDs
 
 
-def counter_summary(dirs):
-    """Means per attention-forward dispatch of every counter in the given rocprofv3
-    --pmc runs, and the matrix-core utilisation they imply: busy cycles of
-    the matrix units over (active cycles of one XCD x all SIMDs), where
-    GRBM_GUI_ACTIVE is summed over the 8 XCDs."""
+def counter_summary(dirs, which: str = "attn"):
+    """Means per dispatch of every counter in the given rocprofv3 --pmc runs,
+    for the bf16 attention forward kernel (which="attn") or for each
+    backward kernel (which="bwd"), and the matrix-core utilisation they
+    imply: busy cycles of the matrix units over (active cycles of one XCD x
+    all SIMDs), where GRBM_GUI_ACTIVE is summed over the 8 XCDs."""
     import collections
-    vals = collections.defaultdict(list)
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
     for d in dirs:
         for counter in ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
                         "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES",
                         "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT"):
             for k, vs in _pmc_values(d, counter).items():
-                if _is_attn_fwd(k):
-                    vals[counter].extend(vs)
+                if which == "attn" and _is_attn_fwd(k):
+                    vals["attention forward"][counter].extend(vs)
+                elif which == "bwd" and "attn_bwd_" in k and "delta" not in k:
+                    vals[k.replace("void ", "").split("(")[0]][counter].extend(vs)
     if not vals:
-        raise SystemExit("no attention dispatch in " + " ".join(dirs))
-    mean = {k: sum(v) / len(v) for k, v in vals.items()}
-    print("%-28s %10s %16s" % ("counter", "dispatches", "mean per dispatch"))
-    for k in sorted(mean):
-        print("%-28s %10d %16.4g" % (k, len(vals[k]), mean[k]))
-    if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and "GRBM_GUI_ACTIVE" in mean:
-        cyc = mean["GRBM_GUI_ACTIVE"] / 8
-        print("active cycles per XCD: %.4g" % cyc)
-        print("matrix-core busy / (active cycles x %d SIMDs): %.3f" % (SIMDS, mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * SIMDS)))
-        if "SQ_INSTS_MFMA" in mean:
-            print("busy cycles per matrix instruction: %.2f" % (mean["SQ_VALU_MFMA_BUSY_CYCLES"] / mean["SQ_INSTS_MFMA"]))
-    if "SQ_WAIT_INST_ANY" in mean and "SQ_WAVE_CYCLES" in mean:
-        print("wave time waiting on a dependency: %.3f" % (mean["SQ_WAIT_INST_ANY"] / mean["SQ_WAVE_CYCLES"]))
+        raise SystemExit("no %s dispatch in %s" % (which, " ".join(dirs)))
+    for name in sorted(vals):
+        mean = {k: sum(v) / len(v) for k, v in vals[name].items()}
+        if which == "bwd":
+            print("\n%s" % name)
+        print("%-28s %10s %16s" % ("counter", "dispatches", "mean per dispatch"))
+        for k in sorted(mean):
+            print("%-28s %10d %16.4g" % (k, len(vals[name][k]), mean[k]))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and "GRBM_GUI_ACTIVE" in mean:
+            cyc = mean["GRBM_GUI_ACTIVE"] / 8
+            print("active cycles per XCD: %.4g" % cyc)
+            print("matrix-core busy / (active cycles x %d SIMDs): %.3f" %
+                  (SIMDS, mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * SIMDS)))
+            if "SQ_INSTS_MFMA" in mean:
+                print("busy cycles per matrix instruction: %.2f" % (mean["SQ_VALU_MFMA_BUSY_CYCLES"] / mean["SQ_INSTS_MFMA"]))
+        if "SQ_WAIT_INST_ANY" in mean and "SQ_WAVE_CYCLES" in mean:
+            print("wave time waiting on a dependency: %.3f" % (mean["SQ_WAIT_INST_ANY"] / mean["SQ_WAVE_CYCLES"]))
+        if "SQ_INSTS_LDS" in mean and "SQ_INSTS_MFMA" in mean:
+            print("LDS instructions per matrix instruction: %.2f" % (mean["SQ_INSTS_LDS"] / mean["SQ_INSTS_MFMA"]))
 
 
 def stats_summary(d, last: int = 0):
@@ -1425,7 +1452,7 @@ def main():
         stats_summary(args.stats_summary, args.last)
         return
     if args.counter_summary:
-        counter_summary(args.counter_summary)
+        counter_summary(args.counter_summary, args.counter_kernels)
         return
     if args.gpus != 1:
         print("bench.py measures one rank's share on one GPU; --gpus %d is not supported "
