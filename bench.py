@@ -866,7 +866,7 @@ def pmc_probe(args):
         hbm_probe(args, cfg_id, src, dst)
         return
     if args.pmc_probe == "bwd":
-        run, _, _ = _backward_setup(Share(cfg_id, 1), cfg_id)
+        run, _, _ = _backward_setup(make_share(args.workload, 1), cfg_id)
         for _ in range(args.steps):
             run(True)
         torch.cuda.synchronize()
