@@ -217,7 +217,13 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void attn_bwd_dkdv_kernel(const 
 {
     constexpr int ROWB = 2 * D, NKC = D / 16, NDB = D / 32, TB = kBwdT * ROWB;
     constexpr int CPT = TB / 1024 / kBwdWaves;        // copy instructions per wave per tensor per tile
-    constexpr int XB = 4 * 4 * 64 * 16;               // an exchange buffer: key group x chunk x lane x 16 bytes
+    // An exchange buffer: key group x chunk x lane x 16 bytes, the two lane
+    // halves of a chunk XH bytes apart and chunks XC apart (64 and 128 bytes
+    // past a multiple of the 256-byte bank period), so that the transposing
+    // reads of the dS workspace blocks, whose source lanes span two chunks and
+    // both halves, hit distinct banks; every 16 lanes of a slot access stay
+    // contiguous.
+    constexpr int XH = 32 * 16 + 64, XC = 2 * XH, XB = 4 * 4 * XC;
     // LDS: Q[3] | dO[2] | lse[2] (log2 units) | delta[2] | P | dS[2]
     constexpr int OFF_Q = 0, OFF_O = 3 * TB, OFF_L = 5 * TB, OFF_D = OFF_L + 512, OFF_P = OFF_D + 512;
     constexpr int OFF_S = OFF_P + XB, SMEM = OFF_S + 2 * XB;
@@ -337,7 +343,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void attn_bwd_dkdv_kernel(const 
     const int rrow = l32 * ROWB, rx = (hg ^ bwd_swz<D>(l32)) << 4;
     const BwdTr trs = bwd_tr_setup<D>(lane);
     // exchange slot of chunk c of this key group
-    auto xslot = [&](int c) { return ((kg * 4 + c) * 64 + lane) * 16; };
+    auto xslot = [&](int c) { return (kg * 4 + c) * XC + (lane >> 5) * XH + (lane & 31) * 16; };
 
     bwd_f32x16 acc[NDB];
 #pragma unroll
@@ -497,9 +503,9 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void attn_bwd_dkdv_kernel(const 
                             for (int kk = 0; kk < 2; ++kk) {
                                 const int64_t qc = (i0 >> 5) + qq, kc = (kw0 >> 4) + kk;
                                 if (qc >= a.ds_nq || kc >= a.ds_nk) continue;
-                                const bwd_lds_u8* src = L + OFF_S + dsb * XB +
-                                                        ((kg * 4 + 2 * qq + (g & 1)) * 64 + (sa & 1) * 32 + 16 * kk +
-                                                         4 * (g >> 1) + se) * 16 + (sa >> 1) * 8;
+                                const bwd_lds_u8* src = L + OFF_S + dsb * XB + (kg * 4 + 2 * qq + (g & 1)) * XC +
+                                                        (sa & 1) * XH + (16 * kk + 4 * (g >> 1) + se) * 16 +
+                                                        (sa >> 1) * 8;
                                 const bwd_i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bwd_lds_i16x4*)src);
                                 const bwd_i16x4 y =
                                     __builtin_amdgcn_ds_read_tr16_b64_v4i16((bwd_lds_i16x4*)(src + 8 * 16));
